@@ -1,0 +1,234 @@
+"""Benchmark of one SwitchSD copy-speculation step on one MI355X.
+
+A step is the whole hot path over one batch, all on one HIP stream with no host
+synchronisation inside: probe_score -> kgram_retrieve -> blocktri_verify
+(block-triangular attention, LM head, argmax) -> accept_longest.  Inputs are
+synthetic (seeded) and resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
+                    [--no-cpu-baseline]
+
+Prints one JSON line: copy-steps/s (whole job), verified candidate tokens/s,
+the LM-head kernel's roofline position (HIP events around that kernel in the
+timed region) and the CPU oracle timed on the host on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0     # dense bf16
+FP32_PEAK_TFS = 157.3
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama8b_b1")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return p.parse_args()
+
+
+def lm_algorithmic(s, R_tot):
+    """LM-head work the method itself needs: the weights once, the real rows in,
+    one int per row out; 2 flops per weight per real row."""
+    elt = 2 if s.dtype == "bf16" else 4
+    byts = s.V * s.hid * elt + R_tot * s.hid * elt + 4 * R_tot
+    flops = 2.0 * R_tot * s.hid * s.V
+    return byts, flops
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the oracle (as it stands) on the host for one step of this workload.
+
+    Integer stages and the probe run on every sequence.  Attention and the LM head
+    run on a seeded sample of real rows sized to the budget, and their time is
+    scaled to all real rows of the step."""
+    import oracle
+    from oracle.attention import real_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    s = wl.spec
+    t0 = time.perf_counter()
+    pr = oracle.probe_score(wl.h, wl.w, s.tau)
+    kg = oracle.kgram_retrieve(wl.ids, wl.cu_len, s.kappa, s.W, s.D, pr["fire"])
+    t_int = time.perf_counter() - t0
+    real = [(b, r) for b in range(s.B) for r in real_rows(kg["cand_len"][b], kg["copy_gate"][b], s.W, s.D)]
+    if not real:
+        return None
+    rng = np.random.default_rng(0)
+    # attention: grow the sample until about a third of the budget is spent
+    k_att = min(len(real), 8)
+    while True:
+        idx = rng.choice(len(real), k_att, replace=False)
+        rows = [real[i] for i in idx]
+        t0 = time.perf_counter()
+        out, ev = oracle.blocktri_attention(wl.q, wl.k_pre, wl.v_pre, wl.cu_len, wl.k_cand, wl.v_cand,
+                                            kg["cand_len"], kg["copy_gate"], s.Hq, s.Hkv, s.d, s.W,
+                                            s.D, wl.scale, rows=rows)
+        t_att = time.perf_counter() - t0
+        if t_att > budget_s / 3 or k_att == len(real):
+            break
+        k_att = min(len(real), k_att * 4)
+    # LM head: every real row in one call when the step has at most 1024 of them
+    # (the weight widening is part of the oracle's call); otherwise a 256-row sample
+    # whose whole-call time is scaled by rows (this overstates the CPU time)
+    k_lm = n_real = len(real)
+    if n_real > 1024:
+        k_lm = 256
+    rows_lm = real if k_lm == n_real else [real[i] for i in rng.choice(n_real, k_lm, replace=False)]
+    if k_att < n_real or rows_lm is not real:
+        out, _ = oracle.blocktri_attention(wl.q, wl.k_pre, wl.v_pre, wl.cu_len, wl.k_cand, wl.v_cand,
+                                           kg["cand_len"], kg["copy_gate"], s.Hq, s.Hkv, s.d, s.W,
+                                           s.D, wl.scale, rows=rows_lm)
+    O = out[[b for b, _ in rows_lm], [r for _, r in rows_lm]]
+    t0 = time.perf_counter()
+    lm = oracle.lmhead_argmax(O, wl.lm_head)
+    t_lm = time.perf_counter() - t0
+    am = np.full((s.B, wl.R), -1, dtype=np.int64)
+    for (b, r), p in zip(rows_lm, lm["pred"]):
+        am[b, r] = p
+    t0 = time.perf_counter()
+    oracle.accept_longest(kg["cand"], kg["cand_len"], kg["copy_gate"], am, s.W, s.D)
+    t_acc = time.perf_counter() - t0
+    t_step = t_int + t_att * n_real / k_att + t_lm * n_real / k_lm + t_acc
+    return {"value": s.B / t_step, "unit": "copy-steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{s.name}: probe+kgram+accept on all {s.B} sequences; attention on {k_att} "
+                       f"of {n_real} real rows ({t_att:.2f}s), LM head+argmax on {k_lm} rows "
+                       f"({t_lm:.2f}s, includes widening the {s.V}x{s.hid} weights to float64); "
+                       f"scaled to all rows: {t_step:.2f}s per step"),
+            "measured_s": round(t_int + t_att + t_lm + t_acc, 2)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported in this build "
+              f"(the path shards over sequences with no exchange; see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import copy_draft_verification_amd as cdv
+    from workloads import generate, to_torch
+
+    wl = generate(a.workload)
+    s = wl.spec
+    dev = "cuda:0"
+    up = lambda x: to_torch(x, dev)  # noqa: E731
+    ids, cu, h, w = up(wl.ids), up(wl.cu_len), up(wl.h), up(wl.w)
+    q, kp, vp, kc, vc, lm = (up(wl.q), up(wl.k_pre), up(wl.v_pre), up(wl.k_cand), up(wl.v_cand),
+                             up(wl.lm_head))
+    B, R = s.B, wl.R
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    # every output and the workspace are allocated once, outside the timed region
+    z = torch.empty(B, dtype=torch.float32, device=dev)
+    fire = torch.empty(B, dtype=torch.uint8, device=dev)
+    kout = {"match_end": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "n_match": torch.empty(B, dtype=torch.int32, device=dev),
+            "cand": torch.empty(B, s.W, s.D, dtype=torch.int32, device=dev),
+            "cand_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev)}
+    attn = torch.empty(B, R, s.Hq * s.d, dtype=tdt, device=dev)
+    am = torch.empty(B, R, dtype=torch.int32, device=dev)
+    ws = torch.empty(cdv.verify_workspace_bytes(B, wl.max_n, s.W, s.D, s.Hq, s.Hkv, s.d, s.V, tdt),
+                     dtype=torch.uint8, device=dev)
+    aout = {"accept_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "best_w": torch.empty(B, dtype=torch.int32, device=dev),
+            "best_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "next_token": torch.empty(B, dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def step(lm_events=None):
+        cdv.probe_score(h, w, s.tau, z_out=z, fire_out=fire, stream=stream)
+        cdv.kgram_retrieve(ids, cu, s.kappa, s.W, s.D, fire, out=kout, stream=stream)
+        cdv.blocktri_verify(q, kp, vp, cu, wl.max_n, kc, vc, kout["cand_len"], kout["copy_gate"], lm,
+                            s.W, s.D, wl.scale, attn_out=attn, argmax_out=am, workspace=ws,
+                            events=lm_events, stream=stream)
+        cdv.accept_longest(kout["cand"], kout["cand_len"], kout["copy_gate"], am, s.W, s.D,
+                           out=aout, stream=stream)
+
+    print(f"[bench] workload={s.name} B={B} n={np.diff(wl.cu_len).tolist()[:4]} V={s.V} "
+          f"warmup={a.warmup} steps={a.steps}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    lm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(a.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(a.steps):
+        step(lm_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_begin.elapsed_time(t_end) / a.steps
+    lm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in lm_ev]))
+    gate = kout["copy_gate"].cpu().numpy().astype(bool)
+    cl = kout["cand_len"].cpu().numpy()
+    sum_L = int(cl[gate].sum())
+    R_tot = int(gate.sum()) + sum_L
+    print(f"[bench] {ms:.4f} ms/step, lm-head kernel {lm_ms:.4f} ms, gates={int(gate.sum())} "
+          f"sumL={sum_L}", file=sys.stderr, flush=True)
+
+    lm_bytes, lm_flops = lm_algorithmic(s, R_tot)
+    # the contraction runs over every row of the batch (B*R), padded rows included;
+    # the algorithmic figures count real rows only
+    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
+    tflops = lm_flops / (lm_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFS if s.dtype == "bf16" else FP32_PEAK_TFS
+    hbm_time = lm_bytes / (HBM_PEAK_GBS * 1e9)
+    mfma_time = lm_flops / (mfma_peak * 1e12)
+    if hbm_time >= mfma_time:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tflops / mfma_peak, 4)}
+    roof.update({"traffic": None, "kernel": "lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel",
+                 "kernel_ms": round(lm_ms, 4), "algorithmic_bytes": int(lm_bytes),
+                 "algorithmic_flops": lm_flops, "mfma_tflops": round(tflops, 1)})
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, a.cpu_budget_s)
+
+    line = {
+        "metric": "copy-steps/sec & verified cand tokens/sec @8B shape; % HBM/MFMA peak",
+        "value": round(B / (ms * 1e-3), 2),
+        "unit": "copy-steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": s.name, "B": B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
+                   "hid": s.hid, "Hq": s.Hq, "Hkv": s.Hkv, "d": s.d, "V": s.V, "kappa": s.kappa,
+                   "W": s.W, "D": s.D, "tau": s.tau, "parallelism": "single-gpu"},
+        "verified_cand_tokens_per_s": round(sum_L / (ms * 1e-3), 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Python binding of libswitchsd.so (argument marshalling only).
+
+Every function here forwards device pointers and sizes to the C ABI declared
+in include/switchsd.h; every step of the copy path runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to the same HIP runtime as torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libswitchsd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+_lib = None
+
+_c_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_SIGS = {
+    "ssd_abi_version": (ctypes.c_int, []),
+    "ssd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ssd_probe_score": (ctypes.c_int, [_c_p, ctypes.c_int, _c_p, _i32, _i32, ctypes.c_float, _c_p,
+                                       _c_p, _c_p]),
+    "ssd_kgram_retrieve": (ctypes.c_int, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p,
+                                          _c_p, _c_p, _c_p, _c_p]),
+    "ssd_verify_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     _i32, ctypes.c_int]),
+    "ssd_blocktri_verify": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p, _c_p,
+                                           _c_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           ctypes.c_int, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
+                                           ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "ssd_accept_longest": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p,
+                                          _c_p, _c_p, _c_p]),
+}
+
+
+class SwitchSDError(RuntimeError):
+    pass
+
+
+def load(path=LIB_PATH):
+    """Load the C-ABI library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m copy_draft_verification_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load().ssd_status_string(status).decode()
+        raise SwitchSDError(f"{what} failed: status {status} ({msg})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SwitchSDError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise SwitchSDError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise SwitchSDError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t):
+    return SSD_BF16 if t.dtype == torch.bfloat16 else SSD_F32
+
+
+def abi_version():
+    return load().ssd_abi_version()
+
+
+def probe_score(h, w, tau, z_out=None, fire_out=None, stream=None):
+    """Probe decision per sequence.  h [B, hid] (fp32 | bf16), w [hid] fp32."""
+    _dev(h, "h", (torch.float32, torch.bfloat16))
+    _dev(w, "w", (torch.float32,))
+    B, hid = h.shape
+    if z_out is None:
+        z_out = torch.empty(B, dtype=torch.float32, device=h.device)
+    if fire_out is None:
+        fire_out = torch.empty(B, dtype=torch.uint8, device=h.device)
+    _check(load().ssd_probe_score(_ptr(h), _dt(h), _ptr(w), B, hid, float(tau), _ptr(z_out),
+                                  _ptr(fire_out), _stream(stream)), "probe_score")
+    return z_out, fire_out
+
+
+def kgram_retrieve(ids, cu_len, kappa, W, D, fire=None, out=None, stream=None):
+    """kappa-gram evidence + candidates.  Returns dict of match_end, n_match, cand,
+    cand_len, copy_gate (device tensors)."""
+    _dev(ids, "ids", (torch.int32,))
+    _dev(cu_len, "cu_len", (torch.int32,))
+    if fire is not None:
+        _dev(fire, "fire", (torch.uint8,))
+    B = cu_len.numel() - 1
+    dev = ids.device
+    if out is None:
+        out = {
+            "match_end": torch.empty(B, W, dtype=torch.int32, device=dev),
+            "n_match": torch.empty(B, dtype=torch.int32, device=dev),
+            "cand": torch.empty(B, W, D, dtype=torch.int32, device=dev),
+            "cand_len": torch.empty(B, W, dtype=torch.int32, device=dev),
+            "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev),
+        }
+    _check(load().ssd_kgram_retrieve(_ptr(ids), _ptr(cu_len), B, kappa, W, D, _ptr(fire),
+                                     _ptr(out["match_end"]), _ptr(out["n_match"]), _ptr(out["cand"]),
+                                     _ptr(out["cand_len"]), _ptr(out["copy_gate"]), _stream(stream)),
+           "kgram_retrieve")
+    return out
+
+
+def verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, dtype):
+    code = SSD_BF16 if dtype == torch.bfloat16 else SSD_F32
+    return int(load().ssd_verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, code))
+
+
+def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
+                    W, D, scale, attn_out=None, argmax_out=None, logits_out=None, workspace=None,
+                    events=None, stream=None):
+    """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
+    [B, W*D, Hkv, d]; lm_head [V, Hq*d].  Returns (attn_out, argmax_out)."""
+    dts = (torch.float32, torch.bfloat16)
+    for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
+                 (v_cand, "v_cand"), (lm_head, "lm_head")):
+        _dev(t, n, dts)
+        if t.dtype != q.dtype:
+            raise SwitchSDError(f"{n} dtype {t.dtype} differs from q dtype {q.dtype}")
+    _dev(cu_len, "cu_len", (torch.int32,))
+    _dev(cand_len, "cand_len", (torch.int32,))
+    _dev(copy_gate, "copy_gate", (torch.uint8,))
+    B, R, Hq, d = q.shape
+    Hkv = k_pre.shape[1]
+    V = lm_head.shape[0]
+    dev = q.device
+    if attn_out is None:
+        attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
+    if argmax_out is None:
+        argmax_out = torch.empty(B, R, dtype=torch.int32, device=dev)
+    need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ev0, ev1 = (None, None) if events is None else (ctypes.c_void_p(events[0].cuda_event),
+                                                    ctypes.c_void_p(events[1].cuda_event))
+    _check(load().ssd_blocktri_verify(
+        _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
+        _ptr(cand_len), _ptr(copy_gate), _ptr(lm_head), B, W, D, Hq, Hkv, d, V, _dt(q),
+        float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)), "blocktri_verify")
+    return attn_out, argmax_out
+
+
+def accept_longest(cand, cand_len, copy_gate, argmax, W, D, out=None, stream=None):
+    """Longest accepted continuation.  Returns dict accept_len, best_w, best_len, next_token."""
+    for t, n in ((cand, "cand"), (cand_len, "cand_len"), (argmax, "argmax")):
+        _dev(t, n, (torch.int32,))
+    _dev(copy_gate, "copy_gate", (torch.uint8,))
+    B = copy_gate.numel()
+    dev = cand.device
+    if out is None:
+        out = {
+            "accept_len": torch.empty(B, W, dtype=torch.int32, device=dev),
+            "best_w": torch.empty(B, dtype=torch.int32, device=dev),
+            "best_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        }
+    _check(load().ssd_accept_longest(_ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(argmax), B, W,
+                                     D, _ptr(out["accept_len"]), _ptr(out["best_w"]),
+                                     _ptr(out["best_len"]), _ptr(out["next_token"]), _stream(stream)),
+           "accept_longest")
+    return out

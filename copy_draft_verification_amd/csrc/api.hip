@@ -1,0 +1,140 @@
+// C ABI of the copy-speculation path: argument validation, launch planning and
+// dispatch.  No allocation, no synchronisation, no global state.
+#include <cmath>
+
+#include "../../include/switchsd.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(ssd_dtype_t t) { return t == SSD_F32 || t == SSD_BF16; }
+
+ssd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+// shape checks shared by the workspace query and the verify call
+ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
+                                int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dt) {
+  if (B < 1 || max_n < 1 || W < 1 || D < 1 || Hq < 1 || Hkv < 1 || d < 1 || V < 1)
+    return SSD_ERR_INVALID_ARG;
+  if (W > SSD_MAX_W || D > SSD_MAX_D || Hq % Hkv != 0 || !valid_dtype(dt)) return SSD_ERR_INVALID_ARG;
+  const long long R = 1 + static_cast<long long>(W) * D;
+  if (static_cast<long long>(B) * R * Hq * d > (1ll << 40)) return SSD_ERR_INVALID_ARG;
+  if (dt == SSD_BF16) {
+    if (d != 128 || (static_cast<long long>(Hq) * d) % 64 != 0) return SSD_ERR_UNSUPPORTED;
+  } else {
+    if (d != 64 && d != 128) return SSD_ERR_UNSUPPORTED;
+  }
+  return SSD_OK;
+}
+
+struct VerifyLayout {
+  ssd::AttnPlan attn;
+  ssd::LmPlan lm;
+  size_t attn_bytes, lm_bytes;
+};
+
+VerifyLayout verify_layout(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq, int32_t Hkv,
+                           int32_t d, int32_t V, bool bf16) {
+  VerifyLayout L;
+  const int R = 1 + W * D;
+  L.attn = ssd::attn_plan(B, max_n, R, Hq, Hkv, bf16);
+  L.lm = ssd::lm_plan(B * R, V, bf16);
+  L.attn_bytes = align_up(ssd::attn_workspace_bytes(L.attn, B, R, Hq, d));
+  L.lm_bytes = align_up(ssd::lm_workspace_bytes(L.lm, B * R));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+ssd_status_t ssd_probe_score(const void* h, ssd_dtype_t h_dtype, const float* w, int32_t B,
+                             int32_t hidden, float tau, float* z_out, uint8_t* fire_out,
+                             hipStream_t stream) {
+  if (!h || !w || !fire_out || B < 1 || hidden < 1 || !valid_dtype(h_dtype))
+    return SSD_ERR_INVALID_ARG;
+  if (!(tau > 0.f && tau < 1.f)) return SSD_ERR_INVALID_ARG;
+  const double t = static_cast<double>(tau);
+  const float thr = static_cast<float>(std::log(t / (1.0 - t)));
+  return from_hip(ssd::launch_probe(h, h_dtype == SSD_BF16, w, B, hidden, thr, z_out, fire_out, stream));
+}
+
+ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32_t B,
+                                int32_t kappa, int32_t W, int32_t D, const uint8_t* fire,
+                                int32_t* match_end, int32_t* n_match, int32_t* cand,
+                                int32_t* cand_len, uint8_t* copy_gate, hipStream_t stream) {
+  if (!ids || !cu_len || !match_end || !n_match || !cand || !cand_len || !copy_gate)
+    return SSD_ERR_INVALID_ARG;
+  if (B < 1 || kappa < 1 || kappa > SSD_MAX_KAPPA || W < 1 || W > SSD_MAX_W || D < 1 || D > SSD_MAX_D)
+    return SSD_ERR_INVALID_ARG;
+  return from_hip(ssd::launch_kgram(ids, cu_len, B, kappa, W, D, fire, match_end, n_match, cand,
+                                    cand_len, copy_gate, stream));
+}
+
+size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
+                                  int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype) {
+  if (check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype) != SSD_OK) return 0;
+  const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, dtype == SSD_BF16);
+  return L.attn_bytes + L.lm_bytes;
+}
+
+ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
+                                 const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                 const void* v_cand, const int32_t* cand_len,
+                                 const uint8_t* copy_gate, const void* lm_head, int32_t B,
+                                 int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                                 int32_t* argmax_out, float* logits_out, void* workspace,
+                                 size_t workspace_bytes, hipEvent_t lm_begin, hipEvent_t lm_end,
+                                 hipStream_t stream) {
+  if (!q || !k_pre || !v_pre || !cu_len || !k_cand || !v_cand || !cand_len || !copy_gate ||
+      !lm_head || !attn_out || !argmax_out)
+    return SSD_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return SSD_ERR_INVALID_ARG;
+  const ssd_status_t st = check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype);
+  if (st != SSD_OK) return st;
+  const bool bf16 = dtype == SSD_BF16;
+  const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, bf16);
+  if (!workspace || workspace_bytes < L.attn_bytes + L.lm_bytes) return SSD_ERR_WORKSPACE;
+  float* ws_attn = static_cast<float*>(workspace);
+  void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
+  const int R = 1 + W * D;
+  hipError_t e = ssd::launch_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
+                                       B, W, D, Hq, Hkv, d, bf16, scale, L.attn, attn_out, ws_attn,
+                                       stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
+                         lm_begin, lm_end, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, R, W, D, cand_len, copy_gate,
+                                            argmax_out, stream));
+}
+
+ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
+                                const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
+                                int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,
+                                int32_t* best_len, int32_t* next_token, hipStream_t stream) {
+  if (!cand || !cand_len || !copy_gate || !argmax || !accept_len || !best_w || !best_len || !next_token)
+    return SSD_ERR_INVALID_ARG;
+  if (B < 1 || W < 1 || W > SSD_MAX_W || D < 1 || D > SSD_MAX_D) return SSD_ERR_INVALID_ARG;
+  return from_hip(ssd::launch_accept(cand, cand_len, copy_gate, argmax, B, W, D, accept_len, best_w,
+                                     best_len, next_token, stream));
+}
+
+}  // extern "C"

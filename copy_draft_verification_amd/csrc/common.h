@@ -1,0 +1,67 @@
+// Device helpers shared by the gfx950 kernels of the copy-speculation path.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p, size_t i);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename T> __device__ __forceinline__ void store_f32(T* p, size_t i, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, size_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// (value, index) order used by every argmax: larger value wins, equal values
+// go to the lower index.  NaN never wins.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Is row r (0 <= r < 1 + W*D) of sequence b a real query row?
+__device__ __forceinline__ bool real_row(int r, int D, const int32_t* cand_len_b, bool gate) {
+  if (!gate) return false;
+  if (r == 0) return true;
+  int w = (r - 1) / D, j = (r - 1) - w * D;
+  int L = cand_len_b[w];
+  L = L < 0 ? 0 : (L > D ? D : L);
+  return j < L;
+}
+
+}  // namespace ssd

@@ -1,0 +1,51 @@
+// Internal launchers (host side) for the copy-speculation kernels.  Each returns
+// hipGetLastError() after its launches.  Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace ssd {
+
+hipError_t launch_probe(const void* h, bool bf16, const float* w, int B, int hidden, float thr,
+                        float* z_out, uint8_t* fire_out, hipStream_t s);
+
+hipError_t launch_kgram(const int32_t* ids, const int32_t* cu_len, int B, int kappa, int W, int D,
+                        const uint8_t* fire, int32_t* match_end, int32_t* n_match, int32_t* cand,
+                        int32_t* cand_len, uint8_t* copy_gate, hipStream_t s);
+
+hipError_t launch_accept(const int32_t* cand, const int32_t* cand_len, const uint8_t* copy_gate,
+                         const int32_t* argmax, int B, int W, int D, int32_t* accept_len,
+                         int32_t* best_w, int32_t* best_len, int32_t* next_token, hipStream_t s);
+
+// Split of the prefix keys over workgroups for block-triangular attention.
+struct AttnPlan {
+  int nsplit;   // splits of the prefix per (sequence, kv head, row tile)
+  int chunk;    // keys per split (multiple of 64); the last split runs to n_b
+  int qtiles;   // row tiles per (sequence, kv head)
+};
+AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16);
+size_t attn_workspace_bytes(const AttnPlan& p, int B, int R, int Hq, int d);
+
+hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
+                            const int32_t* cu_len, const void* k_cand, const void* v_cand,
+                            const int32_t* cand_len, const uint8_t* copy_gate, int B, int W,
+                            int D, int Hq, int Hkv, int d, bool bf16, float scale,
+                            const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s);
+
+struct LmPlan {
+  int vtiles;   // vocabulary tiles (one workgroup column each)
+  int mchunks;  // row chunks
+};
+LmPlan lm_plan(int rows, int V, bool bf16);
+size_t lm_workspace_bytes(const LmPlan& p, int rows);
+
+hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
+                         bool bf16, const LmPlan& plan, float* logits_out, void* ws,
+                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s);
+
+hipError_t launch_argmax_reduce(const void* ws, const LmPlan& plan, int rows, int R, int W, int D,
+                                const int32_t* cand_len, const uint8_t* copy_gate,
+                                int32_t* argmax_out, hipStream_t s);
+
+}  // namespace ssd

@@ -1,0 +1,176 @@
+/*
+ * switchsd.h — C ABI of the SwitchSD copy-speculation hot path on MI355X (gfx950).
+ *
+ * The method is SwitchSD ("To Copy or Not to Copy: Controlling Speculative
+ * Decoding via Intrinsic Model Signals", arXiv 2609.20186).  One decoding step
+ * of its copy path is four calls, all asynchronous on one HIP stream:
+ *
+ *   ssd_probe_score     copy-intent probe on the layer-l hidden state
+ *   ssd_kgram_retrieve  kappa-gram evidence + up to W recency-ordered candidates
+ *   ssd_blocktri_verify one verification pass: block-triangular attention, then
+ *                       LM-head projection and greedy (T = 0) argmax per row
+ *   ssd_accept_longest  longest accepted continuation and the token after it
+ *
+ * Conventions shared by every call:
+ *  - Pointers to arrays are DEVICE pointers (hipMalloc / torch CUDA tensors);
+ *    scalars are passed by value from the host.  Arrays are dense, row-major,
+ *    with the layouts stated per argument.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronizes, keeps no global state, and may be called concurrently on
+ *    different streams with disjoint output and workspace buffers.
+ *  - Arguments are validated on the host before anything is launched; a call
+ *    that returns an error launches nothing.  SSD_ERR_HIP reports a launch
+ *    failure (hipGetLastError after the launches).
+ *  - Device-side data contracts that the host cannot check are the caller's:
+ *    cu_len is non-decreasing with cu_len[0] = 0, every context holds at least
+ *    one token, token ids are non-negative.  Violations give wrong results,
+ *    never out-of-range accesses outside the arrays described by cu_len.
+ *  - bfloat16 arrays hold raw bf16 bit patterns (uint16); float arrays hold
+ *    IEEE binary32.
+ *
+ * Row layout of the verification pass (paper §3.3 "Parallel Verification with
+ * Block-Triangular Attention"): per sequence R = 1 + W*D query rows; row 0 is
+ * the anchor (newest context token), row 1 + w*D + j is token j of candidate w.
+ */
+#ifndef SWITCHSD_H
+#define SWITCHSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* null pointer, size out of range, tau outside (0,1), ... */
+  SSD_ERR_UNSUPPORTED = 2, /* valid but not implemented shape (e.g. bf16 head dim != 128) */
+  SSD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ssd_verify_workspace_bytes */
+  SSD_ERR_HIP = 4          /* a kernel launch failed */
+} ssd_status_t;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Limits checked by validation. */
+#define SSD_MAX_W 64      /* candidates per sequence */
+#define SSD_MAX_D 64      /* tokens per candidate */
+#define SSD_MAX_KAPPA 64  /* kappa-gram length */
+
+int ssd_abi_version(void);
+const char* ssd_status_string(int status);
+
+/*
+ * Copy-intent probe.  Paper §3.2 "Layer and Threshold Selection" and §3.3:
+ * copy drafting is allowed only when PR(H_i^(l)) >= tau; write-up §2.3: the
+ * probe is a bias-free linear projection trained with binary cross-entropy.
+ * Computes z_b = sum_k w_k h_{b,k} (fp32 accumulation) and
+ * fire_b = [sigmoid(z_b) >= tau], evaluated as z_b >= ln(tau / (1 - tau)).
+ *   h        [B][hidden], dtype h_dtype (the anchor's layer-l state per sequence)
+ *   w        [hidden] float (probe direction)
+ *   z_out    [B] float, may be NULL
+ *   fire_out [B] uint8 (1 = probe fired)
+ * Errors: INVALID_ARG for null h/w/fire_out, B < 1, hidden < 1, tau not in (0,1).
+ */
+ssd_status_t ssd_probe_score(const void* h, ssd_dtype_t h_dtype, const float* w, int32_t B,
+                             int32_t hidden, float tau, float* z_out, uint8_t* fire_out,
+                             hipStream_t stream);
+
+/*
+ * kappa-gram evidence and candidate retrieval.  Write-up §2.5 (dual gate):
+ * copying needs the probe to fire AND the kappa-gram ending at the current
+ * token to have occurred earlier in the context.  Paper §3.3 "Copy-Based
+ * Speculative Generation" / write-up §2.6: up to W continuations of up to D
+ * tokens, ranked by recency.
+ * For sequence b with ids x[0..n-1] = ids[cu_len[b] .. cu_len[b+1]-1]:
+ *   earlier occurrences are end positions p, kappa-1 <= p <= n-2, with
+ *   x[p-kappa+1..p] == x[n-kappa..n-1]; the W largest are kept, newest first;
+ *   L_w = min(D, n-1-p_w), cand[w][j] = x[p_w+1+j] for j < L_w.
+ *   If fire != NULL and fire[b] == 0 nothing is retrieved for b.
+ *   ids       [cu_len[B]] int32
+ *   cu_len    [B+1] int32 offsets
+ *   fire      [B] uint8 or NULL (NULL = every probe fired)
+ *   match_end [B][W] int32, -1 padded      n_match [B] int32 = M
+ *   cand      [B][W][D] int32, -1 padded   cand_len [B][W] int32 (0 for w >= M)
+ *   copy_gate [B] uint8 = fired && M > 0
+ * Errors: INVALID_ARG for null pointers (fire excepted), B < 1,
+ *   kappa not in [1, SSD_MAX_KAPPA], W not in [1, SSD_MAX_W], D not in [1, SSD_MAX_D].
+ */
+ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32_t B,
+                                int32_t kappa, int32_t W, int32_t D, const uint8_t* fire,
+                                int32_t* match_end, int32_t* n_match, int32_t* cand,
+                                int32_t* cand_len, uint8_t* copy_gate, hipStream_t stream);
+
+/* Bytes of scratch that ssd_blocktri_verify needs for these sizes (0 on bad sizes). */
+size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
+                                  int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype);
+
+/*
+ * One verification pass.  Paper §3.3 "Parallel Verification with
+ * Block-Triangular Attention": candidates follow the anchor; a token of
+ * candidate w attends to the whole prefix and to candidate w's tokens up to
+ * and including itself, never to another candidate; all candidates are checked
+ * in one target pass.  Write-up §3.1: decoding at T = 0, so each row's
+ * verdict is the argmax of its logits.
+ * Attention (per query head h, key/value head h / (Hq/Hkv), scores scale*q.k):
+ *   q        [B][R][Hq][d]          queries (post positional encoding)
+ *   k_pre, v_pre [cu_len[B]][Hkv][d] prefix cache (entry n_b-1 is the anchor)
+ *   k_cand, v_cand [B][W*D][Hkv][d] candidate keys/values
+ *   cand_len [B][W], copy_gate [B]  from ssd_kgram_retrieve; sequences whose gate
+ *                                   is closed are skipped entirely
+ *   attn_out [B][R][Hq*d]           head-major concatenation; rows that are not
+ *                                   real (gate closed, w >= M, j >= L_w) are zeros
+ * LM head + argmax:
+ *   lm_head  [V][Hq*d]              transposed projection (row v = weights of token v)
+ *   argmax_out [B][R] int32         lowest index among equal maxima; -1 on rows
+ *                                   that are not real
+ *   logits_out [B][R][V] float or NULL (debug output; written for every row)
+ * dtype: SSD_F32 (all float) or SSD_BF16 (all bf16, fp32 accumulation).
+ * max_n is a host-side upper bound on the context lengths used to size the
+ * launch; results do not depend on it.
+ * workspace: device scratch of at least ssd_verify_workspace_bytes(...) bytes;
+ *   its contents on entry do not matter.
+ * lm_begin, lm_end: optional events (may be NULL) recorded on `stream`
+ *   immediately before and after the LM-head contraction kernel, for timing.
+ * Errors: INVALID_ARG (nulls, sizes < 1, Hq % Hkv != 0, scale not finite > 0,
+ *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 64 != 0;
+ *   fp32 with d not in {64, 128}), WORKSPACE.
+ */
+ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
+                                 const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                 const void* v_cand, const int32_t* cand_len,
+                                 const uint8_t* copy_gate, const void* lm_head, int32_t B,
+                                 int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                                 int32_t* argmax_out, float* logits_out, void* workspace,
+                                 size_t workspace_bytes, hipEvent_t lm_begin, hipEvent_t lm_end,
+                                 hipStream_t stream);
+
+/*
+ * Longest accepted continuation at T = 0.  Paper §3.3: the longest validated
+ * continuation is kept; greedy verification stops at the first disagreement.
+ *   pred(w, -1) = argmax[b][0]; pred(w, j) = argmax[b][1 + w*D + j]
+ *   a_w = largest k <= L_w with cand[w][j] == pred(w, j-1) for all j < k
+ *   best_w = argmax_w a_w (lowest w on ties), best_len = a_{best_w},
+ *   next_token = pred(best_w, best_len - 1) (the target's token after the
+ *   accepted ones; argmax[b][0] when best_len = 0).
+ *   Closed gate: accept_len = 0, best_w = -1, best_len = 0, next_token = -1.
+ *   cand [B][W][D], cand_len [B][W], copy_gate [B], argmax [B][R] (inputs)
+ *   accept_len [B][W], best_w [B], best_len [B], next_token [B] (int32 outputs)
+ * Errors: INVALID_ARG for nulls, B < 1, W or D outside [1, limit].
+ */
+ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
+                                const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
+                                int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,
+                                int32_t* best_len, int32_t* next_token, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWITCHSD_H */

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the same
+seeded inputs.  Bars are stated in parity_lib.  Every test prints the case it runs
+before touching the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import copy_draft_verification_amd as cdv
+import oracle
+from parity_lib import (DEV, Dev, check_accept, check_kgram, check_probe, check_verify, host,
+                        up)
+from workloads import generate, generate_with_ids, spec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    cdv.load()
+
+
+def _chain(wl, rows_att=None, rows_lm=None, logits=True):
+    print(f"[case] {wl.spec.name} B={wl.spec.B} n={np.diff(wl.cu_len).tolist()[:8]} "
+          f"V={wl.spec.V} dtype={wl.spec.dtype} lm_std={wl.spec.lm_std} q_scale={wl.spec.q_scale}",
+          flush=True)
+    d = Dev(wl)
+    fire_dev, po, ties = check_probe(wl, d)
+    fire_host = host(fire_dev).astype(bool)
+    g, ko = check_kgram(wl, d, fire_dev, fire_host)
+    attn, am, st = check_verify(wl, d, g, rows_att=rows_att, rows_lm=rows_lm, logits=logits)
+    check_accept(wl, g, am)
+    st.update(ties=ties, gates=int(ko["copy_gate"].sum()), M=ko["n_match"].tolist()[:8])
+    print(f"[ok] {wl.spec.name} {st}", flush=True)
+    return st
+
+
+# ------------------------------------------------------------------ small shapes, every row
+def test_tiny_fp32_chain():
+    st = _chain(generate("tiny"))
+    assert st["gates"] == 1 and st["M"] == [3]
+
+
+@pytest.mark.parametrize("variant", [{}, {"lm_std": 1.0}, {"q_scale": 4.0}])
+def test_small_bf16_chain(variant):
+    st = _chain(generate("small_bf16", **variant))
+    if variant.get("lm_std") == 1.0:
+        assert st["margin_excluded"] <= 0.1 * st["argmax_rows"]
+
+
+@pytest.mark.parametrize("variant", [{}, {"lm_std": 1.0}, {"q_scale": 4.0, "Hq": 4, "Hkv": 2, "hid": 256}])
+def test_small_fp32_chain(variant):
+    _chain(generate("small_f32", **variant))
+
+
+def test_small_natural_anchors():
+    # natural anchor mode: gates open and close by the data; short accidental repeats
+    _chain(generate("small_bf16", anchor="natural", B=6, seed=2101, lm_std=1.0))
+
+
+# ------------------------------------------------------------------ edge cases
+def test_edge_contexts_bf16():
+    rng = np.random.default_rng(7)
+    ids = [
+        [1, 2, 3],                                   # n <= kappa: no match
+        [5] * 40,                                    # constant: L = 1..W
+        list(range(300)),                            # all distinct: no match
+        ([1, 2, 3, 4, 5, 6, 7] * 30)[:205],          # periodic, ragged
+        list(rng.integers(0, 3, 517)),               # tiny vocabulary: many matches
+        [9] * 6,                                     # n = kappa + 1
+    ]
+    wl = generate_with_ids(spec("small_bf16", lm_std=1.0), ids)
+    _chain(wl)
+
+
+def test_edge_contexts_fp32_probe_closed():
+    ids = [[4, 4, 4, 4, 4, 4, 4, 4], list(range(50)) + list(range(45, 50))]
+    wl = generate_with_ids(spec("small_f32"), ids, anchor_copy=[False, True])
+    d = Dev(wl)
+    # force the first probe shut and the second open, whatever the scores
+    fire = torch.tensor([0, 1], dtype=torch.uint8, device=DEV)
+    g, ko = check_kgram(wl, d, fire, np.array([False, True]))
+    assert ko["n_match"].tolist() == [0, 1]
+    attn, am, st = check_verify(wl, d, g)
+    a, ao = check_accept(wl, g, am)
+    assert ao["best_w"].tolist()[0] == -1 and ao["next_token"].tolist()[0] == -1
+    assert np.all(host(am)[0] == -1) and torch.all(attn[0] == 0)
+
+
+def test_all_gates_closed():
+    wl = generate("small_bf16")
+    d = Dev(wl)
+    fire = torch.zeros(wl.spec.B, dtype=torch.uint8, device=DEV)
+    g, ko = check_kgram(wl, d, fire, np.zeros(wl.spec.B, dtype=bool))
+    attn, am, st = check_verify(wl, d, g)
+    assert st["att_rows"] == 0 and torch.all(am == -1)
+    check_accept(wl, g, am)
+
+
+@pytest.mark.parametrize("W,D,kappa", [(3, 7, 2), (1, 1, 1), (64, 64, 5), (10, 20, 64)])
+def test_kgram_accept_other_limits(W, D, kappa):
+    rng = np.random.default_rng(W * 100 + D)
+    ids = [list(rng.integers(0, 4, int(rng.integers(1, 400)))) for _ in range(5)]
+    ids.append([7] * 150)
+    wl = generate_with_ids(spec("small_f32", W=W, D=D), ids)
+    print(f"[case] kgram W={W} D={D} kappa={kappa}", flush=True)
+    d = Dev(wl, tensors=False)
+    g, ko = check_kgram(wl, d, None, None, W=W, D=D, kappa=kappa)
+    # accept on planted predictions that follow the candidates for a random length
+    B, R = len(ids), 1 + W * D
+    am = rng.integers(0, 4, (B, R)).astype(np.int32)
+    cand, cl = ko["cand"], ko["cand_len"]
+    for b in range(B):
+        if ko["n_match"][b]:
+            am[b, 0] = cand[b, 0, 0]
+        for w in range(W):
+            stop = int(rng.integers(0, D + 1))
+            for j in range(min(stop, D - 1)):
+                if cand[b, w, j + 1] >= 0:
+                    am[b, 1 + w * D + j] = cand[b, w, j + 1]
+    check_accept(wl, g, up(am), W=W, D=D)
+
+
+def test_kgram_long_context_matches_far_back():
+    # 3 chunks of scanning before the first (and only) earlier occurrence at p = 104
+    n = 20000
+    x = list(range(1000, 1000 + n))
+    x[100:105] = x[n - 5:]
+    wl = generate_with_ids(spec("small_f32"), [x, x[:9000] + x[n - 5:]])
+    print("[case] kgram long context", flush=True)
+    d = Dev(wl, tensors=False)
+    g, ko = check_kgram(wl, d, None, None)
+    assert ko["match_end"][0, 0] == 104 and ko["n_match"][0] == 1
+
+
+def test_accept_planted_agreements():
+    wl = generate("small_bf16")
+    s = wl.spec
+    d = Dev(wl, tensors=False)
+    g, ko = check_kgram(wl, d, None, None)
+    rng = np.random.default_rng(3)
+    R = wl.R
+    for trial in range(20):
+        am = rng.integers(0, 50, (s.B, R)).astype(np.int32)
+        for b in range(s.B):
+            am[b, 0] = ko["cand"][b, rng.integers(0, s.W), 0]
+            for w in range(s.W):
+                stop = int(rng.integers(0, s.D + 1))
+                for j in range(min(stop, s.D - 1)):
+                    am[b, 1 + w * s.D + j] = ko["cand"][b, w, j + 1]
+        a, ao = check_accept(wl, g, up(am))
+    assert ao["best_len"].max() > 0
+
+
+# ------------------------------------------------------------------ metamorphic
+def test_candidate_isolation_bitwise():
+    wl = generate("small_bf16", lm_std=1.0)
+    s = wl.spec
+    d = Dev(wl)
+    g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, None)
+    a0, m0 = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                 g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    a0, m0 = a0.clone(), m0.clone()
+    wbad = 3
+    kc2, vc2 = d.kc.clone(), d.vc.clone()
+    kc2[:, wbad * s.D:(wbad + 1) * s.D] += 1.0
+    vc2[:, wbad * s.D:(wbad + 1) * s.D] *= -2.0
+    a1, m1 = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, kc2, vc2, g["cand_len"],
+                                 g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    torch.cuda.synchronize()
+    rows = [r for r in range(wl.R) if r == 0 or (r - 1) // s.D != wbad]
+    assert torch.equal(a0[:, rows], a1[:, rows]) and torch.equal(m0[:, rows], m1[:, rows])
+    bad = [1 + wbad * s.D + j for j in range(s.D)]
+    assert not torch.equal(a0[:, bad], a1[:, bad])
+
+
+def test_runs_are_deterministic():
+    wl = generate("small_bf16", B=2)
+    s = wl.spec
+    d = Dev(wl)
+    outs = []
+    for _ in range(2):
+        z, f = cdv.probe_score(d.h, d.w, s.tau)
+        g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, f)
+        a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                   g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+        acc = cdv.accept_longest(g["cand"], g["cand_len"], g["copy_gate"], m, s.W, s.D)
+        torch.cuda.synchronize()
+        outs.append([z.clone(), a.clone(), m.clone()] + [v.clone() for v in g.values()]
+                    + [v.clone() for v in acc.values()])
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_max_n_only_sizes_the_launch():
+    # an under-estimated max_n must not change results (the last split runs to n_b)
+    wl = generate("small_bf16", lm_std=1.0)
+    s = wl.spec
+    d = Dev(wl)
+    g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, None)
+    outs = []
+    for mn in (wl.max_n, 64, 4 * wl.max_n):
+        a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, mn, d.kc, d.vc, g["cand_len"],
+                                   g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+        torch.cuda.synchronize()
+        outs.append((widen(a), host(m)))
+    for a, m in outs[1:]:
+        assert np.max(np.abs(a - outs[0][0])) <= 2e-2
+        agree = np.mean(m == outs[0][1])
+        assert agree > 0.97
+
+
+def widen(t):
+    from parity_lib import widen_out
+    return widen_out(t)
+
+
+# ------------------------------------------------------------------ full sizes
+def _sample_rows(wl, k, seed):
+    rng = np.random.default_rng(seed)
+    rows = [(b, 0) for b in range(wl.spec.B)]
+    rows += [(int(rng.integers(0, wl.spec.B)), int(rng.integers(1, wl.R))) for _ in range(k)]
+    return rows
+
+
+def test_full_llama8b_b1_every_row():
+    _chain(generate("llama8b_b1"), logits=False)
+
+
+def test_full_llama8b_b1_wide_head_every_row():
+    st = _chain(generate("llama8b_b1", lm_std=1.0), logits=True)
+    assert st["margin_excluded"] <= 0.1 * st["argmax_rows"]
+
+
+@pytest.mark.parametrize("name,over", [("llama8b_b32", {}), ("llama8b_b32", {"anchor": "natural"}),
+                                       ("qwen3_8b_b8", {}), ("llama70b_b4", {"lm_std": 1.0})])
+def test_full_configs_sampled(name, over):
+    wl = generate(name, **over)
+    _chain(wl, rows_att=_sample_rows(wl, 24, 1), rows_lm=_sample_rows(wl, 12, 2), logits=False)

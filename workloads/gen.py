@@ -357,3 +357,35 @@ def to_torch(arr, device):
     if a.dtype == np.bool_:
         return torch.from_numpy(a.astype(np.uint8)).to(device)
     return torch.from_numpy(a).to(device)
+
+
+def generate_with_ids(s, id_lists, anchor_copy=None):
+    """Workload whose contexts are given explicitly (edge cases); float tensors are
+    drawn as in `generate`.  anchor_copy[b] marks the anchor as a copy position."""
+    B = len(id_lists)
+    s = replace(s, B=B)
+    ns = [len(x) for x in id_lists]
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ns)
+    ids = np.concatenate([np.asarray(x, dtype=np.int32) for x in id_lists])
+    copy_pos = np.zeros(len(ids), dtype=bool)
+    w = _rng(s.seed, _TAGS["w"]).standard_normal(s.hid, dtype=np.float32) / np.float32(np.sqrt(s.hid))
+    hs = []
+    for b in range(B):
+        hb = _rng(s.seed, _TAGS["h"], b).standard_normal(s.hid, dtype=np.float32)
+        if anchor_copy is None or anchor_copy[b]:
+            hb = hb + np.float32(3.0) * w / np.float32(np.linalg.norm(w))
+            copy_pos[cu[b + 1] - 1] = True
+        hs.append(hb.astype(np.float32))
+    h = np.stack(hs)
+    if s.dtype == "bf16":
+        h = f32_to_bf16_bits(h)
+    R = 1 + s.W * s.D
+    N = int(cu[-1])
+    return Workload(s, ids, cu, copy_pos, h, w,
+                    _normal(s.seed, "q", (B, R, s.Hq, s.d), s.q_scale, s.dtype),
+                    _normal(s.seed, "kp", (N, s.Hkv, s.d), 1.0, s.dtype),
+                    _normal(s.seed, "vp", (N, s.Hkv, s.d), 1.0, s.dtype),
+                    _normal(s.seed, "kc", (B, s.W * s.D, s.Hkv, s.d), 1.0, s.dtype),
+                    _normal(s.seed, "vc", (B, s.W * s.D, s.Hkv, s.d), 1.0, s.dtype),
+                    _normal(s.seed, "lm", (s.V, s.hid), s.lm_std, s.dtype))
