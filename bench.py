@@ -36,7 +36,50 @@ def parse():
     p.add_argument("--workload", default="llama8b_b1")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (the reference point that scales the "
+                        "HBM byte counters) and exit")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_bf16_kernel.llama8b_b1.traffic.txt")
+LM_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "lmhead.hip")
+
+
+def calibrate_copy():
+    """A plain device copy of COPY_BYTES, five times: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    over this run give the counters' reading for a known number of bytes."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(5):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[copy] {i} copied {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the LM-head kernel from the committed counter summary,
+    or None when it does not cover this workload or the kernel source changed since."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    with open(LM_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("workload") != workload or kv.get("source_sha256") != sha:
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def lm_algorithmic(s, R_tot):
@@ -120,6 +163,9 @@ def main():
               f"(the path shards over sequences with no exchange; see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     import copy_draft_verification_amd as cdv
     from workloads import generate, to_torch
@@ -167,6 +213,11 @@ def main():
     torch.cuda.synchronize()
     lm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(a.steps)]
+    # torch creates an event on its first record(): record each pair once here, outside
+    # the timed region, so that the library can record the handles around the kernel
+    for e0, e1 in lm_ev:
+        e0.record(stream)
+        e1.record(stream)
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -198,7 +249,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(tflops / mfma_peak, 4)}
-    roof.update({"traffic": None, "kernel": "lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel",
+    roof.update({"traffic": measured_traffic(s.name), "kernel": "lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel",
                  "kernel_ms": round(lm_ms, 4), "algorithmic_bytes": int(lm_bytes),
                  "algorithmic_flops": lm_flops, "mfma_tflops": round(tflops, 1)})
 

@@ -157,8 +157,13 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
     need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    ev0, ev1 = (None, None) if events is None else (ctypes.c_void_p(events[0].cuda_event),
-                                                    ctypes.c_void_p(events[1].cuda_event))
+    ev0 = ev1 = None
+    if events is not None:
+        # torch creates an event on its first record(); a handle of 0 would make the
+        # library skip the record silently, so refuse it here
+        if not events[0].cuda_event or not events[1].cuda_event:
+            raise SwitchSDError("events must be created (recorded once) before they are passed")
+        ev0, ev1 = ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event)
     _check(load().ssd_blocktri_verify(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
         _ptr(cand_len), _ptr(copy_gate), _ptr(lm_head), B, W, D, Hq, Hkv, d, V, _dt(q),

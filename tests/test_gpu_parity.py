@@ -238,3 +238,26 @@ def test_full_llama8b_b1_wide_head_every_row():
 def test_full_configs_sampled(name, over):
     wl = generate(name, **over)
     _chain(wl, rows_att=_sample_rows(wl, 24, 1), rows_lm=_sample_rows(wl, 12, 2), logits=False)
+
+
+def test_lm_events_time_the_contraction():
+    # events handed to blocktri_verify bracket the LM-head kernel; results are unchanged
+    wl = generate("small_bf16", lm_std=1.0)
+    s = wl.spec
+    d = Dev(wl)
+    print(f"[case] lm events {s.name} B={s.B}", flush=True)
+    g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, None)
+    a0, m0 = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                 g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    a0, m0 = a0.clone(), m0.clone()
+    fresh = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    with pytest.raises(cdv.SwitchSDError):
+        cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                            g["copy_gate"], d.lm, s.W, s.D, wl.scale, events=fresh)
+    for e in fresh:
+        e.record()
+    a1, m1 = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                 g["copy_gate"], d.lm, s.W, s.D, wl.scale, events=fresh)
+    torch.cuda.synchronize()
+    assert fresh[0].elapsed_time(fresh[1]) > 0.0
+    assert torch.equal(a0, a1) and torch.equal(m0, m1)
