@@ -2,7 +2,7 @@
 // dispatch.  No allocation, no synchronisation, no global state.
 #include <cmath>
 
-#include "../../include/switchsd.h"
+#include "switchsd.h"
 #include "kernels.h"
 
 namespace {
@@ -23,7 +23,7 @@ ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, 
   const long long R = 1 + static_cast<long long>(W) * D;
   if (static_cast<long long>(B) * R * Hq * d > (1ll << 40)) return SSD_ERR_INVALID_ARG;
   if (dt == SSD_BF16) {
-    if (d != 128 || (static_cast<long long>(Hq) * d) % 64 != 0) return SSD_ERR_UNSUPPORTED;
+    if (d != 128 || (static_cast<long long>(Hq) * d) % 256 != 0) return SSD_ERR_UNSUPPORTED;
   } else {
     if (d != 64 && d != 128) return SSD_ERR_UNSUPPORTED;
   }

@@ -48,6 +48,18 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no
+// swizzle, offset addressing): loads past num_records return zero.
+constexpr int kBufFlags = 0x00020000;
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences global
+// memory, which makes the compiler wait for every outstanding global load (the
+// register prefetches included) before the barrier; here only LDS operations are
+// drained.  The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // (value, index) order used by every argmax: larger value wins, equal values
 // go to the lower index.  NaN never wins.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {

@@ -13,7 +13,7 @@
 // ids after each match.
 #include "common.h"
 #include "kernels.h"
-#include "../../include/switchsd.h"
+#include "switchsd.h"
 
 namespace ssd {
 

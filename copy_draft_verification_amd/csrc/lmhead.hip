@@ -13,117 +13,161 @@
 // reduces the tiles.  An fp32 variant on the vector ALU serves fp32 inputs.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace ssd {
 
-constexpr int kLmVT = 256;               // vocabulary per workgroup (4 waves x 64)
-constexpr int kLmMC = 224;               // rows per chunk (7 MFMA tiles of 32)
-constexpr int kLmMT = kLmMC / 32;        // row tiles
-constexpr int kLmKS = 64;                // k per iteration (4 MFMA k-steps)
-constexpr int kLmOStride = kLmKS + 8;    // bf16 per LDS row (144 B)
-constexpr int kLmOChunks = kLmMC * (kLmKS / 8);  // 16-byte chunks per O stage (1792)
-constexpr int kLmOPer = kLmOChunks / 256;        // per thread (7)
+// bf16 path.  Workgroup = 4 waves = 256 vocabulary entries (64 per wave, two
+// 32-wide MFMA tiles) x one chunk of 224 rows (seven tiles of 32).
+// v_mfma_f32_32x32x16_bf16: A = 32 vocabulary x 16 k (this lane: vocabulary l32,
+// k 8h..8h+7 of the step), B = 16 k x 32 rows (same lane/k pairing), D = 32 x 32
+// with lane (l32, h) holding vocabulary 8(r/4) + 4h + r%4 of row l32 in element r.
+// The k order inside a step is the same on both sides, so the lane-to-k
+// assignment does not change the contraction.
+constexpr int kLmWaves = 4;
+constexpr int kLmVA = 2;                          // A tiles (32 vocabulary) per wave
+constexpr int kLmVT = kLmWaves * kLmVA * 32;      // vocabulary per workgroup (256)
+constexpr int kLmNT = 7;                          // row tiles of 32 per chunk
+constexpr int kLmMC = kLmNT * 32;                 // rows per chunk (224)
+constexpr int kLmKS = 64;                         // k per iteration (four MFMA k-steps)
+constexpr int kLmOStride = kLmKS + 8;             // bf16 per LDS row (144 B: conflict-free b128 reads)
+constexpr int kLmOChunks = kLmMC * (kLmKS / 8);   // 16-byte chunks per O stage (1792)
+constexpr int kLmOPer = kLmOChunks / 256;         // per thread (7)
+constexpr int kLmSlots = 4;                       // weight register slots (iterations it..it+3)
+constexpr int kLmKAlign = kLmKS * kLmSlots;       // the hidden size must be a multiple of this
+constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in flight
+
+template <int N> using IntC = std::integral_constant<int, N>;
 
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int rows, int K, int V,
-    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles) {
+    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles, int mchunks) {
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][kLmMC * kLmOStride];
-  __shared__ float red_v[4][kLmMC];
-  __shared__ int red_i[4][kLmMC];
+  __shared__ float red_v[kLmWaves][kLmMC];
+  __shared__ int red_i[kLmWaves][kLmMC];
 
-  const int mc = blockIdx.x;            // row chunk varies fastest: chunks of one tile run together
-  const int vt = blockIdx.y;
+  const int mc = static_cast<int>(blockIdx.x % mchunks);  // chunks of one tile are adjacent
+  const int vt = static_cast<int>(blockIdx.x / mchunks);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int h = lane >> 5, l32 = lane & 31;
   const int row0 = mc * kLmMC;
-  const int vbase = vt * kLmVT + wave * 64;
+  const int vbase = vt * kLmVT + wave * kLmVA * 32;
 
-  // A operand rows (vocabulary) of this lane; out-of-range rows read row V-1
-  const uint16_t* ap[2];
+  // Buffer resources: this workgroup's vocabulary tile of the weights and its row
+  // chunk of O.  Reads past either range return zero (vocabulary past V, rows past
+  // `rows`, k past the end of the last row), so the pipeline needs no guards.
+  const int v_in_tile = min(kLmVT, V - vt * kLmVT);
+  const int r_in_chunk = min(kLmMC, rows - row0);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, v_in_tile * K * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(O + static_cast<size_t>(row0) * K), 0, r_in_chunk * K * 2, kBufFlags);
+  int aoff[kLmVA];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    int v = vbase + a * 32 + l32;
-    v = v < V ? v : V - 1;
-    ap[a] = Wt + static_cast<size_t>(v) * K + 8 * h;
-  }
+  for (int a = 0; a < kLmVA; ++a) aoff[a] = ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
+  const int ooff = ((tid >> 3) * K + (tid & 7) * 8) * 2;  // row tid/8 (+32 per chunk), k chunk tid%8
 
-  f32x16 acc[2][kLmMT];
+  f32x16 acc[kLmVA][kLmNT];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
-    for (int t = 0; t < kLmMT; ++t)
+    for (int t = 0; t < kLmNT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
 
-  uint4 afrag[2][4], anext[2][4], ostage[kLmOPer];
-  auto load_a = [&](uint4 (&dst)[2][4], int kk) {
+  uint4 aw[kLmSlots][kLmVA][4];
+  uint4 ost[kLmOPer];
+  auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dst[a][s] = *reinterpret_cast<const uint4*>(ap[a] + kk + 16 * s);
+      for (int s = 0; s < 4; ++s)
+        dst[a][s] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[a], it * kLmKS * 2 + 32 * s, 0));
   };
-  auto load_o = [&](int kk) {
+  auto load_o = [&](int it) {
 #pragma unroll
-    for (int c = 0; c < kLmOPer; ++c) {
-      const int idx = tid + c * 256;
-      const int rr = idx >> 3, part8 = idx & 7;
-      const int row = row0 + rr;
-      ostage[c] = row < rows ? *reinterpret_cast<const uint4*>(O + static_cast<size_t>(row) * K + kk + part8 * 8)
-                             : make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < kLmOPer; ++c)
+      ost[c] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(ores, ooff, (32 * c * K + it * kLmKS) * 2, 0));
   };
   auto store_o = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < kLmOPer; ++c) {
-      const int idx = tid + c * 256;
-      const int rr = idx >> 3, part8 = idx & 7;
-      *reinterpret_cast<uint4*>(&o_lds[buf][rr * kLmOStride + part8 * 8]) = ostage[c];
+    for (int c = 0; c < kLmOPer; ++c)
+      *reinterpret_cast<uint4*>(&o_lds[buf][((tid >> 3) + 32 * c) * kLmOStride + (tid & 7) * 8]) = ost[c];
+  };
+  // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
+  // MFMAs.  The LDS reads run kLmBAhead fragments ahead of their use; the
+  // scheduling groups pin that order (first kLmBAhead reads, then two MFMAs and one
+  // read at a time) so that the compiler does not sink the reads next to their use.
+  auto compute = [&](const uint4 (&w)[kLmVA][4], int buf) {
+    constexpr int NB = 4 * kLmNT;
+    const uint16_t* ob = &o_lds[buf][l32 * kLmOStride + 8 * h];
+    uint4 bq[kLmBAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kLmBAhead; ++i)
+      bq[i] = *reinterpret_cast<const uint4*>(ob + (i % kLmNT) * 32 * kLmOStride + 16 * (i / kLmNT));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = i / kLmNT, t = i % kLmNT;
+      if (i + kLmBAhead < NB) {
+        const int j = i + kLmBAhead;
+        bq[j % (kLmBAhead + 1)] =
+            *reinterpret_cast<const uint4*>(ob + (j % kLmNT) * 32 * kLmOStride + 16 * (j / kLmNT));
+      }
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, bq[i % (kLmBAhead + 1)]);
+#pragma unroll
+      for (int a = 0; a < kLmVA; ++a)
+        acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[a][s]), bfr,
+                                                            acc[a][t], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kLmBAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kLmVA, 0);    // MFMAs
+      if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
+  // Software pipeline, unrolled by the slot count so every slot index is static.
+  // Loads complete in issue order, so each iteration issues the rows for it+1 before
+  // the weights for it+3: waiting for the rows (to stage them in LDS at the end of
+  // the iteration) forces only weights issued earlier.
   const int nit = K / kLmKS;
+  auto step = [&](auto U_c, int it) {
+    constexpr int U = decltype(U_c)::value;
+    lds_barrier();  // stage it&1 complete; stage (it+1)&1 no longer read
+    load_o(it + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: rows, then weights
+    load_a(aw[(U + 3) % kLmSlots], it + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(aw[U], U & 1);
+    store_o((U + 1) & 1);
+  };
   load_o(0);
   store_o(0);
-  load_a(afrag, 0);
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    __syncthreads();
-    const bool more = it + 1 < nit;
-    if (more) {
-      load_a(anext, (it + 1) * kLmKS);
-      load_o((it + 1) * kLmKS);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int t = 0; t < kLmMT; ++t) {
-        const uint4 u = *reinterpret_cast<const uint4*>(&o_lds[buf][(t * 32 + l32) * kLmOStride + 16 * s + 8 * h]);
-        const bf16x8 bfr = __builtin_bit_cast(bf16x8, u);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, afrag[a][s]), bfr,
-                                                              acc[a][t], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_o(buf ^ 1);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) afrag[a][s] = anext[a][s];
-    }
+  load_a(aw[0], 0);
+  load_a(aw[1], 1);
+  load_a(aw[2], 2);
+  for (int it0 = 0; it0 < nit; it0 += kLmSlots) {
+    step(IntC<0>{}, it0);
+    step(IntC<1>{}, it0 + 1);
+    step(IntC<2>{}, it0 + 2);
+    step(IntC<3>{}, it0 + 3);
   }
 
-  // epilogue: per row (this lane's column l32 of each row tile) best over the tile
+  // epilogue: per row (this lane's column l32 of each row tile), the best
+  // (value, lowest index) over this workgroup's tile
 #pragma unroll
-  for (int t = 0; t < kLmMT; ++t) {
+  for (int t = 0; t < kLmNT; ++t) {
     const int row = row0 + t * 32 + l32;
     float bv = -INFINITY;
     int bi = INT_MAX;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -146,14 +190,15 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     float bv = red_v[0][i];
     int bi = red_i[0][i];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < kLmWaves; ++w)
       if (better(red_v[w][i], red_i[w][i], bv, bi)) { bv = red_v[w][i]; bi = red_i[w][i]; }
-    part[static_cast<size_t>(vt) * rows + row] = make_int2(__float_as_int(bv), bi);
+    part[static_cast<size_t>(row) * vtiles + vt] = make_int2(__float_as_int(bv), bi);
   }
 }
 
 // fp32: thread per vocabulary column, 32 rows per workgroup, O staged in LDS.
 constexpr int kLmF32Rows = 32;
+constexpr int kLmF32VT = 256;  // vocabulary per workgroup (one column per thread)
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     const float* __restrict__ O, const float* __restrict__ Wt, int rows, int K, int V,
     float* __restrict__ logits_out, int2* __restrict__ part, int vtiles) {
@@ -163,7 +208,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
   const int mc = blockIdx.x, vt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int row0 = mc * kLmF32Rows;
-  const int v = vt * 256 + tid;
+  const int v = vt * kLmF32VT + tid;
   const float* wr = Wt + static_cast<size_t>(v < V ? v : V - 1) * K;
   float acc[kLmF32Rows];
 #pragma unroll
@@ -208,35 +253,45 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
       int bi = red_i[0][tid];
       for (int w = 1; w < 4; ++w)
         if (better(red_v[w][tid], red_i[w][tid], bv, bi)) { bv = red_v[w][tid]; bi = red_i[w][tid]; }
-      part[static_cast<size_t>(vt) * rows + row] = make_int2(__float_as_int(bv), bi);
+      part[static_cast<size_t>(row) * vtiles + vt] = make_int2(__float_as_int(bv), bi);
     }
   }
 }
 
+// One wave per row: the row's tile partials are contiguous ([row][vtile]), each
+// lane scans every 64th of them, then a wave-wide (value desc, index asc) reduction.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(
     const int2* __restrict__ part, int vtiles, int rows, int R, int W, int D,
     const int32_t* __restrict__ cand_len, const uint8_t* __restrict__ copy_gate,
     int32_t* __restrict__ argmax_out) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
   if (row >= rows) return;
   const int b = row / R, r = row - b * R;
   if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0)) {
-    argmax_out[row] = -1;
+    if (lane == 0) argmax_out[row] = -1;
     return;
   }
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int t = 0; t < vtiles; ++t) {
-    const int2 p = part[static_cast<size_t>(t) * rows + row];
+  const int2* pr = part + static_cast<size_t>(row) * vtiles;
+  for (int t = lane; t < vtiles; t += kWave) {
+    const int2 p = pr[t];
     const float v = __int_as_float(p.x);
     if (better(v, p.y, bv, bi)) { bv = v; bi = p.y; }
   }
-  argmax_out[row] = bi;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (lane == 0) argmax_out[row] = bi;
 }
 
 LmPlan lm_plan(int rows, int V, bool bf16) {
   LmPlan p;
-  p.vtiles = (V + 255) / 256;
+  p.vtiles = bf16 ? (V + kLmVT - 1) / kLmVT : (V + kLmF32VT - 1) / kLmF32VT;
   p.mchunks = bf16 ? (rows + kLmMC - 1) / kLmMC : (rows + kLmF32Rows - 1) / kLmF32Rows;
   return p;
 }
@@ -251,9 +306,9 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   int2* part = static_cast<int2*>(ws);
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
+    hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(plan.mchunks * plan.vtiles), dim3(256), 0, s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
-                       rows, hid, V, logits_out, part, plan.vtiles);
+                       rows, hid, V, logits_out, part, plan.vtiles, plan.mchunks);
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
                        static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), rows,
@@ -266,7 +321,7 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
 hipError_t launch_argmax_reduce(const void* ws, const LmPlan& plan, int rows, int R, int W, int D,
                                 const int32_t* cand_len, const uint8_t* copy_gate,
                                 int32_t* argmax_out, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 255) / 256), dim3(256), 0, s,
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
                      static_cast<const int2*>(ws), plan.vtiles, rows, R, W, D, cand_len, copy_gate,
                      argmax_out);
   return hipGetLastError();

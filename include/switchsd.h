@@ -138,7 +138,7 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  * lm_begin, lm_end: optional events (may be NULL) recorded on `stream`
  *   immediately before and after the LM-head contraction kernel, for timing.
  * Errors: INVALID_ARG (nulls, sizes < 1, Hq % Hkv != 0, scale not finite > 0,
- *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 64 != 0;
+ *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 256 != 0;
  *   fp32 with d not in {64, 128}), WORKSPACE.
  */
 ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,

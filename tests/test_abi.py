@@ -96,6 +96,9 @@ def test_verify_validation(lib):
     assert f(*_verify_args(scale=float("inf"))) == 1
     assert f(*_verify_args(d=64)) == 2                     # unsupported for bf16
     assert f(*_verify_args(dtype=0, d=96)) == 2
+    assert f(*_verify_args(Hq=3, Hkv=1)) == 2               # bf16 hidden size not a multiple of 256
+    # fp32 has no such limit: the shape passes and the (too small) workspace is refused
+    assert f(*_verify_args(dtype=0, Hq=3, Hkv=1, ws_bytes=16)) == 3
     assert f(*_verify_args(ws_bytes=16)) == 3
     assert f(*_verify_args(ws=None)) == 3
 
