@@ -22,27 +22,69 @@ namespace ssd {
 constexpr int kAttD = 128;          // head dim of the MFMA path
 constexpr int kKB = 64;             // keys per LDS block
 constexpr int kKStride = kAttD + 8; // bf16 per K row in LDS (272 B: conflict-free b128 reads)
-constexpr int kVtStride = kKB + 4;  // bf16 per V^T row in LDS (136 B: conflict-free b64 reads)
 constexpr int kAttRowsPerBlock = 128;
+constexpr int kXcds = 8;            // workgroups are dealt round-robin over the 8 XCDs
+constexpr float kLazyRescale = 8.f; // the running max moves only when exceeded by 2^8
 
+// V^T in LDS: row d holds the block's 64 keys (128 B, no padding) as sixteen 8-byte
+// units of 4 keys; unit u sits at position u ^ vt_swz(d).  With this swizzle both the
+// transposing writes (16 lanes = 16 rows d = 8*dc + e, one unit) and the MFMA
+// A-operand reads (32 lanes = 32 consecutive rows, one unit) hit distinct banks.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 15; }
+
+// One workgroup = 128 query rows (the g query heads of one KV head packed together)
+// x one key range of one sequence.  Key ranges ("slots") 0..nsplit-1 split the
+// prefix; slot nsplit holds the W*D candidate keys, where row (w, j) may only see
+// keys (w, 0..j): that mask is evaluated in registers from the key and row
+// indices.  Each slot leaves a partial (running max m, sum l, unnormalised o) in
+// the workspace, in the exp2 domain; the merge kernel combines them.
+//
+// Grid: the (sequence, kv head, slot) groups are dealt to XCDs so that all row
+// tiles of a group share one XCD's L2 (they read the same keys).
 __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
-    const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int Hkv, int nsplit, int chunk,
-    float scale_log2, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o) {
+    const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
+    const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int Hkv, int W, int D,
+    int nsplit, int chunk, int qtiles, float scale_log2, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, float* __restrict__ ws_o) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kAttD * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kAttD * kKB];
 
-  const int qtile = blockIdx.x;
-  const int b = blockIdx.y / Hkv, kvh = blockIdx.y - b * Hkv;
-  const int split = blockIdx.z;
+  // XCD-aware decode: block L runs on XCD L % 8; groups g with g % 8 == x run there
+  const int nslots = nsplit + 1;
+  const int groups = B * Hkv * nslots;
+  const int xcd = static_cast<int>(blockIdx.x % kXcds), idx = static_cast<int>(blockIdx.x / kXcds);
+  const int qtile = idx % qtiles;
+  const int grp = (idx / qtiles) * kXcds + xcd;
+  if (grp >= groups) return;
+  const int slot = grp % nslots;
+  const int b = (grp / nslots) / Hkv, kvh = (grp / nslots) % Hkv;
   if (copy_gate[b] == 0) return;
   const int base = cu_len[b];
   const int n_b = cu_len[b + 1] - base;
-  const int k0 = split * chunk;
-  if (k0 >= n_b) return;
-  const int k1 = split == nsplit - 1 ? n_b : min(k0 + chunk, n_b);
+  const bool cand = slot == nsplit;
+  int k0, k1, nkeys;
+  const uint16_t *kp, *vp;
+  if (cand) {
+    k0 = 0;
+    k1 = nkeys = W * D;
+    kp = k_cand + static_cast<size_t>(b) * W * D * Hkv * kAttD;
+    vp = v_cand + static_cast<size_t>(b) * W * D * Hkv * kAttD;
+  } else {
+    k0 = slot * chunk;
+    if (k0 >= n_b) return;
+    k1 = slot == nsplit - 1 ? n_b : min(k0 + chunk, n_b);
+    nkeys = n_b;
+    kp = k_pre + static_cast<size_t>(base) * Hkv * kAttD;
+    vp = v_pre + static_cast<size_t>(base) * Hkv * kAttD;
+  }
+  // keys of this sequence (or its candidates); reads past the last key return zero
+  const int key_bytes = Hkv * kAttD * 2;
+  const __amdgpu_buffer_rsrc_t kres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, nkeys * key_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t vres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), 0, nkeys * key_bytes, kBufFlags);
 
   const int g = Hq / Hkv, G = R * g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
@@ -50,6 +92,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
   const int i_row = qtile * kAttRowsPerBlock + wave * 32 + l32;  // this lane's query row (B operand column)
   const bool row_ok = i_row < G;
   const int r_row = row_ok ? i_row / g : 0, hh = row_ok ? i_row - (i_row / g) * g : 0;
+  // candidate mask of this row: keys cw*D .. cw*D + cj (none for the anchor row)
+  const int cw = r_row > 0 ? (r_row - 1) / D : -1;
+  const int cj = r_row > 0 ? (r_row - 1) - cw * D : -1;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16s + 8h .. +7]
   bf16x8 qf[8];
@@ -69,61 +114,50 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // staging registers for the next K / V block
+  // Staging of a 64-key block.  K: thread loads 16 B (d chunk tid%16) of keys
+  // tid/16 + 16c.  V: thread loads d chunk dc = tid%16 of the four keys 4kq..4kq+3,
+  // kq = tid/16, and writes them transposed as eight 8-byte units (one per d).
+  const int koff = ((tid >> 4) * Hkv + kvh) * kAttD * 2 + (tid & 15) * 16;
+  const int kq = tid >> 4, dc = tid & 15;
+  const int voff = ((4 * kq) * Hkv + kvh) * kAttD * 2 + dc * 16;
   uint4 kreg[4], vreg[4];
   auto load_block = [&](int kb) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + c * 256;          // 1024 chunks of 16 B
-      const int key = idx >> 4, part = idx & 15;
-      const int t = kb + key;
-      kreg[c] = t < k1 ? *reinterpret_cast<const uint4*>(
-                             k_pre + ((static_cast<size_t>(base) + t) * Hkv + kvh) * kAttD + part * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c)
+      kreg[c] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff, (kb + 16 * c) * key_bytes, 0));
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = tid + c * 256;          // 512 (key pair, d chunk) items
-      const int kp = idx >> 4, dc = idx & 15;
-      const int t0 = kb + 2 * kp;
-      vreg[2 * c] = t0 < k1 ? *reinterpret_cast<const uint4*>(
-                                  v_pre + ((static_cast<size_t>(base) + t0) * Hkv + kvh) * kAttD + dc * 8)
-                            : make_uint4(0, 0, 0, 0);
-      vreg[2 * c + 1] = t0 + 1 < k1 ? *reinterpret_cast<const uint4*>(
-                                          v_pre + ((static_cast<size_t>(base) + t0 + 1) * Hkv + kvh) * kAttD + dc * 8)
-                                    : make_uint4(0, 0, 0, 0);
-    }
+    for (int k = 0; k < 4; ++k)
+      vreg[k] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, (kb + k) * key_bytes, 0));
   };
   auto store_block = [&]() {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + c * 256;
-      const int key = idx >> 4, part = idx & 15;
-      *reinterpret_cast<uint4*>(&k_lds[key * kKStride + part * 8]) = kreg[c];
-    }
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint4*>(&k_lds[((tid >> 4) + 16 * c) * kKStride + (tid & 15) * 8]) = kreg[c];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = tid + c * 256;
-      const int kp = idx >> 4, dc = idx & 15;
-      const uint32_t* a = reinterpret_cast<const uint32_t*>(&vreg[2 * c]);
-      const uint32_t* bb = reinterpret_cast<const uint32_t*>(&vreg[2 * c + 1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = dc*8 + 2e (low halves) and dc*8 + 2e + 1 (high halves)
-        const uint32_t lo = (a[e] & 0xffffu) | (bb[e] << 16);
-        const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&vt_lds[(dc * 8 + 2 * e) * kVtStride + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&vt_lds[(dc * 8 + 2 * e + 1) * kVtStride + 2 * kp]) = hi;
+    for (int e = 0; e < 8; ++e) {
+      const int d = dc * 8 + e;
+      const uint32_t w0 = (&vreg[0].x)[e >> 1], w1 = (&vreg[1].x)[e >> 1];
+      const uint32_t w2 = (&vreg[2].x)[e >> 1], w3 = (&vreg[3].x)[e >> 1];
+      uint2 u;
+      if (e & 1) {
+        u.x = (w0 >> 16) | (w1 & 0xffff0000u);
+        u.y = (w2 >> 16) | (w3 & 0xffff0000u);
+      } else {
+        u.x = (w0 & 0xffffu) | (w1 << 16);
+        u.y = (w2 & 0xffffu) | (w3 << 16);
       }
+      *reinterpret_cast<uint2*>(&vt_lds[d * kKB + 4 * (kq ^ vt_swz(d))]) = u;
     }
   };
 
   load_block(k0);
   for (int kb = k0; kb < k1; kb += kKB) {
-    __syncthreads();
+    lds_barrier();  // every wave is done reading the previous block
     store_block();
-    __syncthreads();
-    if (kb + kKB < k1) load_block(kb + kKB);
+    lds_barrier();  // this block is in LDS
+    if (kb + kKB < k1) load_block(kb + kKB);  // overlaps the MFMAs below
 
     // S^T[key][row] for two 32-key subtiles
     f32x16 sacc[2];
@@ -137,21 +171,47 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[s], sacc[kt], 0, 0, 0);
       }
     }
-    // online softmax over this block (exp2 domain); lanes l and l^32 share a row
-    float mloc = -INFINITY;
+    // Online softmax in the exp2 domain; lanes l and l^32 share a row.  Keys past
+    // k1 and candidate keys outside this row's own prefix are masked (only partial
+    // prefix blocks and candidate blocks need the test).
+    float smax = -INFINITY;
+    if (!cand && kb + kKB <= k1) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float sv = key < k1 ? sacc[kt][r] * scale_log2 : -INFINITY;
-        sacc[kt][r] = sv;
-        mloc = fmaxf(mloc, sv);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kt][r]);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          bool vis = key < k1;
+          if (cand) {
+            const int kw = key / D;
+            vis = vis && kw == cw && key - kw * D <= cj;
+          }
+          if (!vis) sacc[kt][r] = -INFINITY;
+          smax = fmaxf(smax, sacc[kt][r]);
+        }
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    const float m_blk = smax * scale_log2;  // scale > 0: the max commutes with it
+    // Lazy rescale: keep the running max until a block exceeds it by more than 2^8
+    // (probabilities then stay <= 256, exact enough in bf16 and fp32).
+    const bool need = m_blk > m_run + kLazyRescale;
+    if (__ballot(need)) {
+      const float m_new = need ? m_blk : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    // a row with no visible key yet keeps m = -inf; exponentiate against 0 then
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     float psum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -160,26 +220,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kt][8 * s2 + e] - m_new);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s2 + e], scale_log2, neg_m));
           psum += p;
           pf[kt][s2][e] = static_cast<__bf16>(p);
         }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    l_run += psum;
     // O^T[d][row] += V^T[d][keys] P^T[keys][row]; key order of a P fragment element e
-    // for lane half h: kt*32 + 16*s2 + 8*(e/4) + 4*h + e%4 (the S^T output layout)
+    // for lane half h: kt*32 + 16*s2 + 8*(e/4) + 4*h + e%4 (the S^T output layout),
+    // i.e. 4-key units 8kt + 4s2 + h (e < 4) and that + 2 (e >= 4)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
+      const int d = dt * 32 + l32;
+      const uint16_t* vr = &vt_lds[d * kKB];
+      const int sw = vt_swz(d);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const uint16_t* vr = &vt_lds[(dt * 32 + l32) * kVtStride + kt * 32 + 16 * s2 + 4 * h];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          const int u0 = 8 * kt + 4 * s2 + h;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * (u0 ^ sw));
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4 * ((u0 + 2) ^ sw));
           const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[kt][s2], oacc[dt], 0, 0, 0);
         }
@@ -188,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (!row_ok) return;
-  const size_t po = ((static_cast<size_t>(split) * B + b) * R + r_row) * Hq + kvh * g + hh;
+  const size_t po = ((static_cast<size_t>(slot) * B + b) * R + r_row) * Hq + kvh * g + hh;
   if (h == 0) {
     ws_m[po] = m_run;
     ws_l[po] = l_tot;
@@ -202,6 +262,47 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
       *reinterpret_cast<float4*>(op + d0) =
           make_float4(oacc[dt][4 * rq], oacc[dt][4 * rq + 1], oacc[dt][4 * rq + 2], oacc[dt][4 * rq + 3]);
     }
+}
+
+// bf16 merge: one wave per (sequence, row, query head).  Combines the prefix slots
+// that hold keys of this sequence and the candidate slot (a row without visible
+// candidate keys left m = -inf there, which weighs 0), normalises and writes bf16.
+// Rows that are not real are written as 0.
+__global__ __launch_bounds__(256) void attn_merge_bf16_kernel(
+    const int32_t* __restrict__ cu_len, const int32_t* __restrict__ cand_len,
+    const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int W, int D, int nsplit,
+    int chunk, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
+    const float* __restrict__ ws_o, uint16_t* __restrict__ out) {
+  const size_t item = static_cast<size_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, r, hq)
+  const int lane = threadIdx.x & (kWave - 1);
+  if (item >= static_cast<size_t>(B) * R * Hq) return;
+  const int r = static_cast<int>((item / Hq) % R);
+  const int b = static_cast<int>(item / (static_cast<size_t>(Hq) * R));
+  uint16_t* op = out + item * kAttD;  // out[b][r][hq*d + ...]
+  if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0)) {
+    *reinterpret_cast<uint32_t*>(op + 2 * lane) = 0u;
+    return;
+  }
+  const int n_b = cu_len[b + 1] - cu_len[b];
+  const int nsp = min(nsplit, (n_b + chunk - 1) / chunk);
+  const size_t per_slot = static_cast<size_t>(B) * R * Hq;
+  const size_t row_item = item;  // == (b*R + r)*Hq + hq
+  float M = ws_m[static_cast<size_t>(nsplit) * per_slot + row_item];
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, ws_m[s * per_slot + row_item]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  auto add = [&](size_t po) {
+    const float f = __builtin_amdgcn_exp2f(ws_m[po] - M);
+    L += f * ws_l[po];
+    const float2 v = *reinterpret_cast<const float2*>(ws_o + po * kAttD + 2 * lane);
+    o0 += f * v.x;
+    o1 += f * v.y;
+  };
+  for (int s = 0; s < nsp; ++s) add(s * per_slot + row_item);
+  add(static_cast<size_t>(nsplit) * per_slot + row_item);
+  const float inv = 1.f / L;
+  const uint32_t packed = static_cast<uint32_t>(f32_to_bf16(o0 * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16(o1 * inv)) << 16);
+  *reinterpret_cast<uint32_t*>(op + 2 * lane) = packed;
 }
 
 // ----------------------------------------------------------------- fp32 VALU
@@ -344,11 +445,12 @@ AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
   if (ch < kKB) ch = kKB;
   p.nsplit = ns;
   p.chunk = ch;
+  p.nslots = bf16 ? ns + 1 : ns;  // bf16: one more slot for the candidate keys
   return p;
 }
 
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int R, int Hq, int d) {
-  const size_t rows = static_cast<size_t>(p.nsplit) * B * R * Hq;
+  const size_t rows = static_cast<size_t>(p.nslots) * B * R * Hq;
   return rows * sizeof(float) * (2 + static_cast<size_t>(d));
 }
 
@@ -358,7 +460,7 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                             int D, int Hq, int Hkv, int d, bool bf16, float scale,
                             const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s) {
   const int R = 1 + W * D;
-  const size_t rows = static_cast<size_t>(plan.nsplit) * B * R * Hq;
+  const size_t rows = static_cast<size_t>(plan.nslots) * B * R * Hq;
   float* ws_m = ws;
   float* ws_l = ws + rows;
   float* ws_o = ws + 2 * rows;
@@ -366,14 +468,16 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   const size_t items = static_cast<size_t>(B) * R * Hq;
   const dim3 mgrid(static_cast<unsigned>((items + 3) / 4));
   if (bf16) {
-    hipLaunchKernelGGL(attn_prefix_bf16_kernel, dim3(plan.qtiles, B * Hkv, plan.nsplit), dim3(256), 0, s,
+    const int groups = B * Hkv * plan.nslots;
+    const int per_xcd = (groups + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(attn_prefix_bf16_kernel, dim3(kXcds * per_xcd * plan.qtiles), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pre),
-                       static_cast<const uint16_t*>(v_pre), cu_len, copy_gate, B, R, Hq, Hkv,
-                       plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o);
-    hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 2>), mgrid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cand),
-                       static_cast<const uint16_t*>(v_cand), cu_len, cand_len, copy_gate, B, R, Hq,
-                       Hkv, W, D, plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o,
+                       static_cast<const uint16_t*>(v_pre), cu_len,
+                       static_cast<const uint16_t*>(k_cand), static_cast<const uint16_t*>(v_cand),
+                       copy_gate, B, R, Hq, Hkv, W, D, plan.nsplit, plan.chunk, plan.qtiles,
+                       scale_log2, ws_m, ws_l, ws_o);
+    hipLaunchKernelGGL(attn_merge_bf16_kernel, mgrid, dim3(256), 0, s, cu_len, cand_len, copy_gate,
+                       B, R, Hq, W, D, plan.nsplit, plan.chunk, ws_m, ws_l, ws_o,
                        static_cast<uint16_t*>(attn_out));
   } else {
     const dim3 pgrid(plan.qtiles, B, plan.nsplit);

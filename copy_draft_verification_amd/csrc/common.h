@@ -52,6 +52,12 @@ __device__ __forceinline__ float wave_max(float v) {
 // swizzle, offset addressing): loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of this wave are outstanding; the other counters are not waited on.
+constexpr int waitcnt_vm(int n) {
+  return ((n >> 4) & 3) << 14 | 0xf << 8 | 0x7 << 4 | (n & 0xf);
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences global
 // memory, which makes the compiler wait for every outstanding global load (the
 // register prefetches included) before the barrier; here only LDS operations are

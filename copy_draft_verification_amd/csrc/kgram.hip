@@ -62,8 +62,19 @@ __global__ __launch_bounds__(kKgThreads) void kgram_kernel(
       const int cbeg = max(lo, top - kKgChunk + 1);
       const int lbase = cbeg - kappa + 1;
       const int cnt = top - lbase + 1;
+      // stage the chunk: every thread issues all of its loads before storing any
+      int tmp[kKgPer + 1];
+#pragma unroll
+      for (int u = 0; u <= kKgPer; ++u) {
+        const int i = t + u * kKgThreads;
+        tmp[u] = i < cnt ? ids[base + lbase + i] : 0;
+      }
       __syncthreads();
-      for (int i = t; i < cnt; i += kKgThreads) s_ids[i] = ids[base + lbase + i];
+#pragma unroll
+      for (int u = 0; u <= kKgPer; ++u) {
+        const int i = t + u * kKgThreads;
+        if (i < cnt) s_ids[i] = tmp[u];
+      }
       __syncthreads();
       unsigned mask = 0;
       const int p0 = top - t * kKgPer;

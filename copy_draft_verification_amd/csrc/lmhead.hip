@@ -27,31 +27,55 @@ namespace ssd {
 // with lane (l32, h) holding vocabulary 8(r/4) + 4h + r%4 of row l32 in element r.
 // The k order inside a step is the same on both sides, so the lane-to-k
 // assignment does not change the contraction.
+//
+// Memory pipeline (one iteration = 64 k):
+//  * weights: straight from HBM into registers (the A operand), three iterations
+//    ahead, in four register slots;
+//  * rows: copied from global memory into LDS by buffer-to-LDS loads, also three
+//    iterations ahead, into four LDS stages.
+// Both streams run the same distance ahead because a wave's loads complete in
+// issue order: a short-latency row load issued after a weight load cannot be
+// consumed before that weight load has landed.
 constexpr int kLmWaves = 4;
 constexpr int kLmVA = 2;                          // A tiles (32 vocabulary) per wave
 constexpr int kLmVT = kLmWaves * kLmVA * 32;      // vocabulary per workgroup (256)
 constexpr int kLmNT = 7;                          // row tiles of 32 per chunk
 constexpr int kLmMC = kLmNT * 32;                 // rows per chunk (224)
 constexpr int kLmKS = 64;                         // k per iteration (four MFMA k-steps)
-constexpr int kLmOStride = kLmKS + 8;             // bf16 per LDS row (144 B: conflict-free b128 reads)
-constexpr int kLmOChunks = kLmMC * (kLmKS / 8);   // 16-byte chunks per O stage (1792)
-constexpr int kLmOPer = kLmOChunks / 256;         // per thread (7)
-constexpr int kLmSlots = 4;                       // weight register slots (iterations it..it+3)
+constexpr int kLmStage = kLmMC * kLmKS;           // bf16 per LDS stage (224 rows x 128 B, no padding)
+constexpr int kLmBlocks = kLmMC / 8;              // 1 KB load blocks per stage (8 rows each)
+constexpr int kLmBlocksPerWave = kLmBlocks / kLmWaves;  // 7
+constexpr int kLmSlots = 4;                       // weight register slots = LDS stages
 constexpr int kLmKAlign = kLmKS * kLmSlots;       // the hidden size must be a multiple of this
 constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in flight
+// loads a wave issues per iteration: row blocks, then weight fragments
+constexpr int kLmLoadsPerIter = kLmBlocksPerWave + kLmVA * 4;
+static_assert(kLmBlocks % kLmWaves == 0, "row blocks split evenly over the waves");
+static_assert(kLmLoadsPerIter * 3 <= 63, "vmcnt holds the loads of three iterations");
 
 template <int N> using IntC = std::integral_constant<int, N>;
+
+// Row r of a stage keeps its eight 16-byte k chunks in swizzled order:
+// logical chunk c sits at position c ^ ((r >> 1) & 7).  Sixteen consecutive rows
+// read at one logical chunk then cover all 64 LDS banks once.
+__device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int rows, int K, int V,
     float* __restrict__ logits_out, int2* __restrict__ part, int vtiles, int mchunks) {
-  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][kLmMC * kLmOStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[kLmStage];
   __shared__ float red_v[kLmWaves][kLmMC];
   __shared__ int red_i[kLmWaves][kLmMC];
 
   const int mc = static_cast<int>(blockIdx.x % mchunks);  // chunks of one tile are adjacent
   const int vt = static_cast<int>(blockIdx.x / mchunks);
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // wave index in a scalar register: the LDS destination of a buffer-to-LDS load
+  // (M0) must be wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int h = lane >> 5, l32 = lane & 31;
   const int row0 = mc * kLmMC;
   const int vbase = vt * kLmVT + wave * kLmVA * 32;
@@ -68,7 +92,15 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   int aoff[kLmVA];
 #pragma unroll
   for (int a = 0; a < kLmVA; ++a) aoff[a] = ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
-  const int ooff = ((tid >> 3) * K + (tid & 7) * 8) * 2;  // row tid/8 (+32 per chunk), k chunk tid%8
+  // Row blocks of this wave: block b = wave*7 + j holds rows 8b..8b+7; lane i fills
+  // row 8b + i/8 at swizzled position i%8.  The swizzle depends on the block's
+  // parity only, so two offsets cover all seven blocks (plus 16*K bytes per block).
+  int ooff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int r = 8 * par + (lane >> 3);
+    ooff[par] = ((lane >> 3) * K + lm_swz(r, lane & 7) * 8) * 2;
+  }
 
   f32x16 acc[kLmVA][kLmNT];
 #pragma unroll
@@ -79,7 +111,6 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
 
   uint4 aw[kLmSlots][kLmVA][4];
-  uint4 ost[kLmOPer];
   auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
 #pragma unroll
     for (int a = 0; a < kLmVA; ++a)
@@ -88,36 +119,34 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
         dst[a][s] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[a], it * kLmKS * 2 + 32 * s, 0));
   };
-  auto load_o = [&](int it) {
+  auto load_o = [&](uint16_t* stage, int it) {
 #pragma unroll
-    for (int c = 0; c < kLmOPer; ++c)
-      ost[c] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(ores, ooff, (32 * c * K + it * kLmKS) * 2, 0));
-  };
-  auto store_o = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < kLmOPer; ++c)
-      *reinterpret_cast<uint4*>(&o_lds[buf][((tid >> 3) + 32 * c) * kLmOStride + (tid & 7) * 8]) = ost[c];
+    for (int j = 0; j < kLmBlocksPerWave; ++j) {
+      const int b = wave * kLmBlocksPerWave + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ores, (__attribute__((address_space(3))) void*)(stage + b * 512), 16,
+          ooff[b & 1], (8 * b * K + it * kLmKS) * 2, 0, 0);
+    }
   };
   // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
   // MFMAs.  The LDS reads run kLmBAhead fragments ahead of their use; the
   // scheduling groups pin that order (first kLmBAhead reads, then two MFMAs and one
   // read at a time) so that the compiler does not sink the reads next to their use.
-  auto compute = [&](const uint4 (&w)[kLmVA][4], int buf) {
+  auto compute = [&](const uint4 (&w)[kLmVA][4], const uint16_t* stage) {
     constexpr int NB = 4 * kLmNT;
-    const uint16_t* ob = &o_lds[buf][l32 * kLmOStride + 8 * h];
+    const uint16_t* ob = stage + l32 * kLmKS;
+    const int sw = (l32 >> 1) & 7;
+    auto frag = [&](int j) {
+      const int s = j / kLmNT, t = j % kLmNT;
+      return *reinterpret_cast<const uint4*>(ob + t * 32 * kLmKS + (((2 * s + h) ^ sw) << 3));
+    };
     uint4 bq[kLmBAhead + 1];
 #pragma unroll
-    for (int i = 0; i < kLmBAhead; ++i)
-      bq[i] = *reinterpret_cast<const uint4*>(ob + (i % kLmNT) * 32 * kLmOStride + 16 * (i / kLmNT));
+    for (int i = 0; i < kLmBAhead; ++i) bq[i] = frag(i);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s = i / kLmNT, t = i % kLmNT;
-      if (i + kLmBAhead < NB) {
-        const int j = i + kLmBAhead;
-        bq[j % (kLmBAhead + 1)] =
-            *reinterpret_cast<const uint4*>(ob + (j % kLmNT) * 32 * kLmOStride + 16 * (j / kLmNT));
-      }
+      if (i + kLmBAhead < NB) bq[(i + kLmBAhead) % (kLmBAhead + 1)] = frag(i + kLmBAhead);
       const bf16x8 bfr = __builtin_bit_cast(bf16x8, bq[i % (kLmBAhead + 1)]);
 #pragma unroll
       for (int a = 0; a < kLmVA; ++a)
@@ -131,33 +160,42 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
+  uint16_t* const stages[kLmSlots] = {st0, st1, st2, st3};
 
-  // Software pipeline, unrolled by the slot count so every slot index is static.
-  // Loads complete in issue order, so each iteration issues the rows for it+1 before
-  // the weights for it+3: waiting for the rows (to stage them in LDS at the end of
-  // the iteration) forces only weights issued earlier.
+  // Step U of the unrolled loop works on iteration it (it % 4 == U): wait until this
+  // wave's rows and weights of iteration it have landed (everything but the two
+  // newer iterations' loads), barrier so every wave's row blocks are in LDS and
+  // stage (U+3)%4 is no longer read, issue iteration it+3, compute iteration it.
   const int nit = K / kLmKS;
   auto step = [&](auto U_c, int it) {
     constexpr int U = decltype(U_c)::value;
-    lds_barrier();  // stage it&1 complete; stage (it+1)&1 no longer read
-    load_o(it + 1);
+    // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLmLoadsPerIter));
+    lds_barrier();
+    load_o(stages[(U + 3) % kLmSlots], it + 3);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: rows, then weights
     load_a(aw[(U + 3) % kLmSlots], it + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(aw[U], U & 1);
-    store_o((U + 1) & 1);
+    compute(aw[U], stages[U]);
   };
-  load_o(0);
-  store_o(0);
+  load_o(st0, 0);
   load_a(aw[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_o(st1, 1);
   load_a(aw[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_o(st2, 2);
   load_a(aw[2], 2);
+  __builtin_amdgcn_sched_barrier(0);
   for (int it0 = 0; it0 < nit; it0 += kLmSlots) {
     step(IntC<0>{}, it0);
     step(IntC<1>{}, it0 + 1);
     step(IntC<2>{}, it0 + 2);
     step(IntC<3>{}, it0 + 3);
   }
+  // the last three iterations' loads (past the end: zeros) must land before the
+  // workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // epilogue: per row (this lane's column l32 of each row tile), the best
   // (value, lowest index) over this workgroup's tile
@@ -275,10 +313,19 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(
   float bv = -INFINITY;
   int bi = INT_MAX;
   const int2* pr = part + static_cast<size_t>(row) * vtiles;
-  for (int t = lane; t < vtiles; t += kWave) {
-    const int2 p = pr[t];
-    const float v = __int_as_float(p.x);
-    if (better(v, p.y, bv, bi)) { bv = v; bi = p.y; }
+  // eight partials in flight per lane (512 per wave per round)
+  for (int t0 = 0; t0 < vtiles; t0 += 8 * kWave) {
+    int2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + u * kWave + lane;
+      p[u] = t < vtiles ? pr[t] : make_int2(__float_as_int(-INFINITY), INT_MAX);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = __int_as_float(p[u].x);
+      if (better(v, p[u].y, bv, bi)) { bv = v; bi = p[u].y; }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
