@@ -19,6 +19,7 @@ Modules, one per step of the copy path:
 * ``attention`` – block-triangular attention over prefix + own candidate.
 * ``lmhead``  – LM-head logits and greedy (T=0) argmax with top-2 margin.
 * ``accept``  – longest accepted continuation and the token after it.
+* ``commit``  – copying the accepted rows' K/V into the cache, extending the context.
 * ``bf16``    – exact widening of bfloat16 bit patterns to float64.
 
 Every function states the passage it follows.  Readings of points the pages
@@ -32,9 +33,10 @@ from .kgram import kgram_matches, kgram_retrieve
 from .attention import allowed_keys, attention_row, blocktri_attention
 from .lmhead import lm_logits, argmax_with_margin, lmhead_argmax
 from .accept import accept_longest
+from .commit import commit_accepted
 
 __all__ = [
     "bf16_bits_to_f64", "probe_score", "logit", "kgram_matches", "kgram_retrieve",
     "allowed_keys", "attention_row", "blocktri_attention", "lm_logits",
-    "argmax_with_margin", "lmhead_argmax", "accept_longest",
+    "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted",
 ]

@@ -54,6 +54,19 @@ def test_small_fp32_chain(variant):
     _chain(generate("small_f32", **variant))
 
 
+@pytest.mark.parametrize("W,D", [(3, 7), (16, 5), (1, 64), (64, 1), (12, 33)])
+def test_bf16_chain_other_candidate_shapes(W, D):
+    # the candidate mask is evaluated in registers from W, D and the row index, and
+    # the candidate keys form blocks of 64 that W*D need not fill
+    st = _chain(generate("small_bf16", W=W, D=D, lm_std=1.0, q_scale=4.0))
+    assert st["att_rows"] > 0
+
+
+@pytest.mark.parametrize("W,D", [(3, 7), (64, 1)])
+def test_f32_chain_other_candidate_shapes(W, D):
+    _chain(generate("small_f32", W=W, D=D, lm_std=1.0))
+
+
 def test_small_natural_anchors():
     # natural anchor mode: gates open and close by the data; short accidental repeats
     _chain(generate("small_bf16", anchor="natural", B=6, seed=2101, lm_std=1.0))
