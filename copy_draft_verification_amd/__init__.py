@@ -5,7 +5,9 @@ include/switchsd.h).  This package holds its sources (csrc/), the build script
 (build.py) and a thin ctypes binding (binding.py) with the ABI's names.
 """
 from .binding import (SSD_BF16, SSD_F32, SwitchSDError, abi_version, accept_longest,
-                      blocktri_verify, kgram_retrieve, load, probe_score, verify_workspace_bytes)
+                      blocktri_verify, commit_accepted, kgram_retrieve, load, probe_score,
+                      verify_workspace_bytes)
 
 __all__ = ["SSD_BF16", "SSD_F32", "SwitchSDError", "abi_version", "accept_longest",
-           "blocktri_verify", "kgram_retrieve", "load", "probe_score", "verify_workspace_bytes"]
+           "blocktri_verify", "commit_accepted", "kgram_retrieve", "load", "probe_score",
+           "verify_workspace_bytes"]

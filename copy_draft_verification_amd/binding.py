@@ -33,6 +33,9 @@ _SIGS = {
                                            ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ssd_accept_longest": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p,
                                           _c_p, _c_p, _c_p]),
+    "ssd_commit_accepted": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
+                                           _i32, _i32, ctypes.c_int, _c_p, _c_p, ctypes.c_int64,
+                                           _c_p, _c_p, _c_p, _c_p]),
 }
 
 
@@ -190,4 +193,33 @@ def accept_longest(cand, cand_len, copy_gate, argmax, W, D, out=None, stream=Non
                                      D, _ptr(out["accept_len"]), _ptr(out["best_w"]),
                                      _ptr(out["best_len"]), _ptr(out["next_token"]), _stream(stream)),
            "accept_longest")
+    return out
+
+
+def commit_accepted(k_cand, v_cand, cand, best_w, best_len, next_token, W, D, k_cache, v_cache,
+                    cache_off, out=None, stream=None):
+    """Copy the accepted candidate rows' K/V into the cache and list the tokens that
+    extend the context.  k_cand/v_cand [B, W*D, Hkv, d]; k_cache/v_cache [rows, Hkv, d]
+    (same dtype); cache_off [B] int64.  Returns dict tokens [B, D+1], n_tokens [B]."""
+    dts = (torch.float32, torch.bfloat16)
+    for t, n in ((k_cand, "k_cand"), (v_cand, "v_cand"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n, dts)
+        if t.dtype != k_cand.dtype:
+            raise SwitchSDError(f"{n} dtype {t.dtype} differs from k_cand dtype {k_cand.dtype}")
+    for t, n in ((cand, "cand"), (best_w, "best_w"), (best_len, "best_len"),
+                 (next_token, "next_token")):
+        _dev(t, n, (torch.int32,))
+    _dev(cache_off, "cache_off", (torch.int64,))
+    B, _, Hkv, d = k_cand.shape
+    if k_cache.shape[1:] != k_cand.shape[2:] or v_cache.shape != k_cache.shape:
+        raise SwitchSDError("k_cache / v_cache must be [rows, Hkv, d] matching k_cand")
+    dev = k_cand.device
+    if out is None:
+        out = {"tokens": torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+               "n_tokens": torch.empty(B, dtype=torch.int32, device=dev)}
+    _check(load().ssd_commit_accepted(
+        _ptr(k_cand), _ptr(v_cand), _ptr(cand), _ptr(best_w), _ptr(best_len), _ptr(next_token),
+        B, W, D, Hkv, d, _dt(k_cand), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        _ptr(cache_off), _ptr(out["tokens"]), _ptr(out["n_tokens"]), _stream(stream)),
+        "commit_accepted")
     return out

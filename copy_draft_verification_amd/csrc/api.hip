@@ -137,4 +137,24 @@ ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
                                      best_len, next_token, stream));
 }
 
+ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const int32_t* cand,
+                                 const int32_t* best_w, const int32_t* best_len,
+                                 const int32_t* next_token, int32_t B, int32_t W, int32_t D,
+                                 int32_t Hkv, int32_t d, ssd_dtype_t dtype, void* k_cache,
+                                 void* v_cache, int64_t cache_rows, const int64_t* cache_off,
+                                 int32_t* tokens_out, int32_t* n_tokens_out, hipStream_t stream) {
+  if (!k_cand || !v_cand || !cand || !best_w || !best_len || !next_token || !k_cache || !v_cache ||
+      !cache_off || !tokens_out || !n_tokens_out)
+    return SSD_ERR_INVALID_ARG;
+  if (B < 1 || W < 1 || W > SSD_MAX_W || D < 1 || D > SSD_MAX_D || Hkv < 1 || d < 1 ||
+      cache_rows < 1 || !valid_dtype(dtype))
+    return SSD_ERR_INVALID_ARG;
+  const long long row_bytes = static_cast<long long>(Hkv) * d * (dtype == SSD_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0 || row_bytes > (1ll << 30)) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_commit(k_cand, v_cand, cand, best_w, best_len, next_token, B, W, D,
+                                     static_cast<int>(row_bytes), k_cache, v_cache, cache_rows,
+                                     reinterpret_cast<const long long*>(cache_off), tokens_out,
+                                     n_tokens_out, stream));
+}
+
 }  // extern "C"

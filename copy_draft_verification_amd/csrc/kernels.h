@@ -49,4 +49,10 @@ hipError_t launch_argmax_reduce(const void* ws, const LmPlan& plan, int rows, in
                                 const int32_t* cand_len, const uint8_t* copy_gate,
                                 int32_t* argmax_out, hipStream_t s);
 
+hipError_t launch_commit(const void* k_cand, const void* v_cand, const int32_t* cand,
+                         const int32_t* best_w, const int32_t* best_len, const int32_t* next_token,
+                         int B, int W, int D, int row_bytes, void* k_cache, void* v_cache,
+                         long long cache_rows, const long long* cache_off, int32_t* tokens_out,
+                         int32_t* n_tokens_out, hipStream_t s);
+
 }  // namespace ssd

@@ -11,6 +11,9 @@
  *                       LM-head projection and greedy (T = 0) argmax per row
  *   ssd_accept_longest  longest accepted continuation and the token after it
  *
+ * and, after accept, ssd_commit_accepted copies the accepted tokens' keys and
+ * values into the caller's KV cache and lists the tokens that extend the context.
+ *
  * Conventions shared by every call:
  *  - Pointers to arrays are DEVICE pointers (hipMalloc / torch CUDA tensors);
  *    scalars are passed by value from the host.  Arrays are dense, row-major,
@@ -45,7 +48,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -168,6 +171,37 @@ ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
                                 const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
                                 int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,
                                 int32_t* best_len, int32_t* next_token, hipStream_t stream);
+
+/*
+ * Commit of the accepted draft into the target's KV cache.  Paper §3.3: the
+ * longest validated continuation extends the context, and greedy decoding adds
+ * the target's token after it (the next anchor, whose K/V the caller computes
+ * in its next pass).  The verification pass already holds the accepted tokens'
+ * keys and values.  For every sequence b with best_w[b] >= 0, rows
+ * (best_w, 0..best_len-1) of k_cand / v_cand are copied, in order, to cache
+ * rows cache_off[b] .. cache_off[b] + best_len[b] - 1.
+ *   k_cand, v_cand [B][W*D][Hkv][d] (the verify inputs; dtype as given)
+ *   cand [B][W][D] int32; best_w, best_len, next_token [B] int32 (the
+ *   ssd_accept_longest outputs)
+ *   k_cache, v_cache [cache_rows][Hkv][d], same dtype: the caller's cache
+ *   cache_off [B] int64: first cache row written for sequence b (typically
+ *   where that sequence's context ends)
+ *   tokens_out [B][D+1] int32 (output): the accepted tokens then next_token,
+ *   padded with -1
+ *   n_tokens_out [B] int32 (output): best_len + 1; 0 for a closed gate; -1 when
+ *   best_w / best_len are out of range or the rows do not fit
+ *   (cache_off < 0 or cache_off + best_len > cache_rows).  Nothing is written
+ *   to the cache in the last two cases.
+ * Errors: INVALID_ARG (nulls, B < 1, W or D outside [1, limit], Hkv or d < 1,
+ *   cache_rows < 1, unknown dtype), UNSUPPORTED (Hkv*d*element size not a
+ *   multiple of 16 bytes).
+ */
+ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const int32_t* cand,
+                                 const int32_t* best_w, const int32_t* best_len,
+                                 const int32_t* next_token, int32_t B, int32_t W, int32_t D,
+                                 int32_t Hkv, int32_t d, ssd_dtype_t dtype, void* k_cache,
+                                 void* v_cache, int64_t cache_rows, const int64_t* cache_off,
+                                 int32_t* tokens_out, int32_t* n_tokens_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) >= {"ssd_probe_score", "ssd_kgram_retrieve", "ssd_blocktri_verify",
                           "ssd_accept_longest", "ssd_verify_workspace_bytes", "ssd_abi_version",
-                          "ssd_status_string"}
+                          "ssd_status_string", "ssd_commit_accepted"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -110,3 +110,23 @@ def test_accept_validation(lib):
         a = list(good)
         a[i] = bad
         assert f(*a) == 1, (i, bad)
+
+
+def test_commit_validation(lib):
+    f = lib.ssd_commit_accepted
+    good = dict(kc=FAKE, vc=FAKE, cand=FAKE, bw=FAKE, bl=FAKE, nt=FAKE, B=2, W=10, D=20, Hkv=8,
+                d=128, dtype=1, k_cache=FAKE, v_cache=FAKE, rows=1 << 20, off=FAKE, tok=FAKE,
+                ntok=FAKE, stream=None)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return f(*a.values())
+
+    for k in ("kc", "vc", "cand", "bw", "bl", "nt", "k_cache", "v_cache", "off", "tok", "ntok"):
+        assert call(**{k: None}) == 1, k
+    for k, bad in (("B", 0), ("W", 0), ("W", 65), ("D", 0), ("D", 65), ("Hkv", 0), ("d", 0),
+                   ("rows", 0), ("dtype", 5)):
+        assert call(**{k: bad}) == 1, (k, bad)
+    assert call(Hkv=1, d=3) == 2                        # 6-byte rows: not 16-byte pieces
+    assert call(dtype=0, Hkv=1, d=2) == 2               # 8-byte fp32 rows

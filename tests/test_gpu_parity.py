@@ -274,3 +274,43 @@ def test_lm_events_time_the_contraction():
     torch.cuda.synchronize()
     assert fresh[0].elapsed_time(fresh[1]) > 0.0
     assert torch.equal(a0, a1) and torch.equal(m0, m1)
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("small_bf16", {}),
+                                       ("small_bf16", {"anchor": "natural", "B": 6, "seed": 2101}),
+                                       ("llama8b_b1", {})])
+def test_commit_accepted_bitwise(name, over):
+    # commit after a device chain: cache rows and context tokens equal the oracle's
+    # copy of the same accept outputs, bit for bit; one sequence does not fit
+    wl = generate(name, **over)
+    s = wl.spec
+    print(f"[case] commit {s.name} B={s.B} W={s.W} D={s.D}", flush=True)
+    d = Dev(wl)
+    z, fire = cdv.probe_score(d.h, d.w, s.tau)
+    g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, fire)
+    attn, am = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                   g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    acc = cdv.accept_longest(g["cand"], g["cand_len"], g["copy_gate"], am, s.W, s.D)
+    torch.cuda.synchronize()
+    B, D = s.B, s.D
+    rows = int(wl.cu_len[-1]) + B * D
+    off = np.array([int(wl.cu_len[b + 1]) + b * D for b in range(B)], dtype=np.int64)
+    bl = host(acc["best_len"])
+    if B > 1 and bl[-1] > 1:
+        off[-1] = rows - 1          # needs best_len rows: does not fit
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    k_cache = torch.randn(rows, s.Hkv, s.d, device=DEV, generator=gen).to(d.kc.dtype)
+    v_cache = torch.randn(rows, s.Hkv, s.d, device=DEV, generator=gen).to(d.kc.dtype)
+    raw = (lambda t: host(t.view(torch.int16)).view(np.uint16)) if d.kc.dtype == torch.bfloat16 \
+        else host
+    kc_ref, vc_ref = raw(k_cache).copy(), raw(v_cache).copy()
+    out = cdv.commit_accepted(d.kc, d.vc, g["cand"], acc["best_w"], acc["best_len"],
+                              acc["next_token"], s.W, D, k_cache, v_cache, up(off))
+    torch.cuda.synchronize()
+    tok, nt = oracle.commit_accepted(raw(d.kc), raw(d.vc), host(g["cand"]), host(acc["best_w"]),
+                                     bl, host(acc["next_token"]), s.W, D, kc_ref, vc_ref, off)
+    assert np.array_equal(host(out["tokens"]), tok)
+    assert np.array_equal(host(out["n_tokens"]), nt)
+    assert np.array_equal(raw(k_cache), kc_ref) and np.array_equal(raw(v_cache), vc_ref)
+    print(f"[ok] commit n_tokens={nt.tolist()[:8]}", flush=True)
