@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama8b_b1")
+    p.add_argument("--anchor", default=None, choices=("full", "natural"),
+                   help="anchor mode of the synthetic contexts (default: the workload's own)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -170,7 +172,7 @@ def main():
     import copy_draft_verification_amd as cdv
     from workloads import generate, to_torch
 
-    wl = generate(a.workload)
+    wl = generate(a.workload, **({"anchor": a.anchor} if a.anchor else {}))
     s = wl.spec
     dev = "cuda:0"
     up = lambda x: to_torch(x, dev)  # noqa: E731
@@ -271,7 +273,7 @@ def main():
         "vs_baseline": None,
         "dtype": s.dtype,
         "data": "synthetic",
-        "config": {"workload": s.name, "B": B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
+        "config": {"workload": s.name, "anchor": s.anchor, "B": B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
                    "hid": s.hid, "Hq": s.Hq, "Hkv": s.Hkv, "d": s.d, "V": s.V, "kappa": s.kappa,
                    "W": s.W, "D": s.D, "tau": s.tau, "parallelism": "single-gpu"},
         "verified_cand_tokens_per_s": round(sum_L / (ms * 1e-3), 1),

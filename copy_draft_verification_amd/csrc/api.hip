@@ -119,11 +119,12 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
                                        B, W, D, Hq, Hkv, d, bf16, scale, L.attn, attn_out, ws_attn,
                                        stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
   e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
                          lm_begin, lm_end, stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
-  return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, R, W, D, cand_len, copy_gate,
-                                            argmax_out, stream));
+  return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream));
 }
 
 ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,

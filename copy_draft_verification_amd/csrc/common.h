@@ -82,4 +82,29 @@ __device__ __forceinline__ bool real_row(int r, int D, const int32_t* cand_len_b
   return j < L;
 }
 
+// Exclusive prefix sum of v over a workgroup of NT threads (NT / 64 waves), in
+// thread order; `total` receives the sum.  s_wave holds NT / 64 ints of LDS.
+// Contains two __syncthreads(): every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_wave[wv] = incl;
+  __syncthreads();
+  int woff = 0, tot = 0;
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int c = s_wave[i];
+    if (i < wv) woff += c;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return woff + incl - v;
+}
+
 }  // namespace ssd

@@ -37,6 +37,8 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
 struct LmPlan {
   int vtiles;   // vocabulary tiles (one workgroup column each)
   int mchunks;  // row chunks
+  int sv, sm;   // bf16: super-tile of sv vocabulary tiles x sm row chunks per XCD
+  int blocks;   // bf16: workgroups launched (super-tiles dealt round-robin to XCDs)
 };
 LmPlan lm_plan(int rows, int V, bool bf16);
 size_t lm_workspace_bytes(const LmPlan& p, int rows);
@@ -45,9 +47,13 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s);
 
-hipError_t launch_argmax_reduce(const void* ws, const LmPlan& plan, int rows, int R, int W, int D,
-                                const int32_t* cand_len, const uint8_t* copy_gate,
-                                int32_t* argmax_out, hipStream_t s);
+// Lists the real rows (open gate; row 0 or candidate token j < L_w) in the LM-head
+// workspace; the LM head then contracts only those rows.
+hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
+                               const uint8_t* copy_gate, hipStream_t s);
+
+hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,
+                                hipStream_t s);
 
 hipError_t launch_commit(const void* k_cand, const void* v_cand, const int32_t* cand,
                          const int32_t* best_w, const int32_t* best_len, const int32_t* next_token,

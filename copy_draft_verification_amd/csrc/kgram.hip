@@ -21,27 +21,6 @@ constexpr int kKgThreads = 1024;
 constexpr int kKgPer = 8;
 constexpr int kKgChunk = kKgThreads * kKgPer;
 
-__device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  if (lane == kWave - 1) s_wave[wv] = incl;
-  __syncthreads();
-  int woff = 0, tot = 0;
-  for (int i = 0; i < kKgThreads / kWave; ++i) {
-    int c = s_wave[i];
-    if (i < wv) woff += c;
-    tot += c;
-  }
-  __syncthreads();
-  total = tot;
-  return woff + incl - v;
-}
-
 __global__ __launch_bounds__(kKgThreads) void kgram_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_len, int kappa, int W, int D,
     const uint8_t* __restrict__ fire, int32_t* __restrict__ match_end, int32_t* __restrict__ n_match,
@@ -90,7 +69,7 @@ __global__ __launch_bounds__(kKgThreads) void kgram_kernel(
         }
       }
       int total;
-      int rank = found + block_excl_scan(__popc(mask), s_wave, total);
+      int rank = found + block_excl_scan<kKgThreads>(__popc(mask), s_wave, total);
       while (mask) {
         const int i = __ffs(mask) - 1;
         mask &= mask - 1;

@@ -48,6 +48,8 @@ constexpr int kLmBlocksPerWave = kLmBlocks / kLmWaves;  // 7
 constexpr int kLmSlots = 4;                       // weight register slots = LDS stages
 constexpr int kLmKAlign = kLmKS * kLmSlots;       // the hidden size must be a multiple of this
 constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in flight
+constexpr int kLmXcds = 8;                        // XCDs; workgroups are dealt round-robin
+constexpr int kLmXcdSlots = 32;                   // concurrent workgroups per XCD (one per CU)
 // loads a wave issues per iteration: row blocks, then weight fragments
 constexpr int kLmLoadsPerIter = kLmBlocksPerWave + kLmVA * 4;
 static_assert(kLmBlocks % kLmWaves == 0, "row blocks split evenly over the waves");
@@ -61,8 +63,10 @@ template <int N> using IntC = std::integral_constant<int, N>;
 __device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int rows, int K, int V,
-    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles, int mchunks) {
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
+    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles, int mchunks, int sv,
+    int sm) {
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
@@ -70,8 +74,20 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   __shared__ float red_v[kLmWaves][kLmMC];
   __shared__ int red_i[kLmWaves][kLmMC];
 
-  const int mc = static_cast<int>(blockIdx.x % mchunks);  // chunks of one tile are adjacent
-  const int vt = static_cast<int>(blockIdx.x / mchunks);
+  // XCD-aware tile order.  Workgroups are dealt round-robin over the XCDs (block L
+  // runs on XCD L % 8).  Super-tiles of sv vocabulary tiles x sm row chunks (about
+  // one XCD's worth of concurrent workgroups) are dealt to XCDs whole, so the
+  // workgroups resident together on an XCD share their weights and rows in its L2.
+  const int xcd = static_cast<int>(blockIdx.x % kLmXcds), li = static_cast<int>(blockIdx.x / kLmXcds);
+  const int per = sv * sm;
+  const int super = (li / per) * kLmXcds + xcd;
+  const int n_sm = (mchunks + sm - 1) / sm;
+  const int vt = (super / n_sm) * sv + (li % per) / sm;
+  const int mc = (super % n_sm) * sm + (li % per) % sm;
+  if (vt >= vtiles || mc >= mchunks) return;
+  // rows of this chunk are compact indices row0.. into the list of real rows
+  const int rows = *n_rows;
+  if (mc * kLmMC >= rows) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   // wave index in a scalar register: the LDS destination of a buffer-to-LDS load
   // (M0) must be wave-uniform
@@ -84,22 +100,25 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // chunk of O.  Reads past either range return zero (vocabulary past V, rows past
   // `rows`, k past the end of the last row), so the pipeline needs no guards.
   const int v_in_tile = min(kLmVT, V - vt * kLmVT);
-  const int r_in_chunk = min(kLmMC, rows - row0);
+  const int o_bytes = total_rows * K * 2;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, v_in_tile * K * 2, kBufFlags);
-  const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(O + static_cast<size_t>(row0) * K), 0, r_in_chunk * K * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ores =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
   int aoff[kLmVA];
 #pragma unroll
   for (int a = 0; a < kLmVA; ++a) aoff[a] = ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
-  // Row blocks of this wave: block b = wave*7 + j holds rows 8b..8b+7; lane i fills
-  // row 8b + i/8 at swizzled position i%8.  The swizzle depends on the block's
-  // parity only, so two offsets cover all seven blocks (plus 16*K bytes per block).
-  int ooff[2];
+  // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
+  // fills stage row 8b + i/8 at swizzled position i%8 from O row
+  // row_list[row0 + 8b + i/8].  Stage rows past the last real row read past the end
+  // of O, which returns zero.
+  int ooff[kLmBlocksPerWave];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int r = 8 * par + (lane >> 3);
-    ooff[par] = ((lane >> 3) * K + lm_swz(r, lane & 7) * 8) * 2;
+  for (int j = 0; j < kLmBlocksPerWave; ++j) {
+    const int sr = 8 * (wave * kLmBlocksPerWave + j) + (lane >> 3);
+    const int ci = row0 + sr;
+    const int orow = ci < rows ? row_list[ci] : -1;
+    ooff[j] = orow < 0 ? o_bytes : (orow * K + lm_swz(sr, lane & 7) * 8) * 2;
   }
 
   f32x16 acc[kLmVA][kLmNT];
@@ -125,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       const int b = wave * kLmBlocksPerWave + j;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ores, (__attribute__((address_space(3))) void*)(stage + b * 512), 16,
-          ooff[b & 1], (8 * b * K + it * kLmKS) * 2, 0, 0);
+          ooff[j], it * kLmKS * 2, 0, 0);
     }
   };
   // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
@@ -211,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
         const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const float x = acc[a][t][r];
         if (v < V && better(x, v, bv, bi)) { bv = x; bi = v; }
-        if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row) * V + v] = x;
+        if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row_list[row]) * V + v] = x;
       }
     const float ov = __shfl_xor(bv, 32, kWave);
     const int oi = __shfl_xor(bi, 32, kWave);
@@ -238,7 +257,8 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
 constexpr int kLmF32Rows = 32;
 constexpr int kLmF32VT = 256;  // vocabulary per workgroup (one column per thread)
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(
-    const float* __restrict__ O, const float* __restrict__ Wt, int rows, int K, int V,
+    const float* __restrict__ O, const float* __restrict__ Wt, int K, int V,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
     float* __restrict__ logits_out, int2* __restrict__ part, int vtiles) {
   __shared__ float o_lds[kLmF32Rows][64];
   __shared__ float red_v[4][kLmF32Rows];
@@ -246,6 +266,8 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
   const int mc = blockIdx.x, vt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int row0 = mc * kLmF32Rows;
+  const int rows = *n_rows;  // compact rows; O row of compact row i is row_list[i]
+  if (row0 >= rows) return;
   const int v = vt * kLmF32VT + tid;
   const float* wr = Wt + static_cast<size_t>(v < V ? v : V - 1) * K;
   float acc[kLmF32Rows];
@@ -257,7 +279,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     for (int e = tid; e < kLmF32Rows * 64; e += 256) {
       const int rr = e / 64, kk = e % 64;
       const int row = row0 + rr;
-      o_lds[rr][kk] = (row < rows && kk < kc) ? O[static_cast<size_t>(row) * K + k0 + kk] : 0.f;
+      o_lds[rr][kk] = (row < rows && kk < kc) ? O[static_cast<size_t>(row_list[row]) * K + k0 + kk] : 0.f;
     }
     __syncthreads();
     for (int kk = 0; kk < kc; ++kk) {
@@ -269,7 +291,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
 #pragma unroll
   for (int i = 0; i < kLmF32Rows; ++i) {
     const int row = row0 + i;
-    if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row) * V + v] = acc[i];
+    if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row_list[row]) * V + v] = acc[i];
     float bv = v < V ? acc[i] : -INFINITY;
     int bi = v < V ? v : INT_MAX;
 #pragma unroll
@@ -296,23 +318,49 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
   }
 }
 
+// Real rows (open gate, row 0 or j < L_w) in row order: row_list[i] = row of the
+// i-th real row, inv[row] = i or -1, n_rows = count.  One workgroup scans all rows.
+constexpr int kCompactThreads = 1024;
+__global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(
+    int rows, int R, int W, int D, const int32_t* __restrict__ cand_len,
+    const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
+    int32_t* __restrict__ inv, int32_t* __restrict__ n_rows) {
+  __shared__ int s_wave[kCompactThreads / kWave];
+  int base = 0;
+  for (int r0 = 0; r0 < rows; r0 += kCompactThreads) {
+    const int row = r0 + static_cast<int>(threadIdx.x);
+    bool real = false;
+    if (row < rows) {
+      const int b = row / R;
+      real = real_row(row - b * R, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0);
+    }
+    int total;
+    const int pos = base + block_excl_scan<kCompactThreads>(real ? 1 : 0, s_wave, total);
+    if (row < rows) {
+      inv[row] = real ? pos : -1;
+      if (real) row_list[pos] = row;
+    }
+    base += total;
+  }
+  if (threadIdx.x == 0) *n_rows = base;
+}
+
 // One wave per row: the row's tile partials are contiguous ([row][vtile]), each
 // lane scans every 64th of them, then a wave-wide (value desc, index asc) reduction.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(
-    const int2* __restrict__ part, int vtiles, int rows, int R, int W, int D,
-    const int32_t* __restrict__ cand_len, const uint8_t* __restrict__ copy_gate,
+    const int2* __restrict__ part, int vtiles, int rows, const int32_t* __restrict__ inv,
     int32_t* __restrict__ argmax_out) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= rows) return;
-  const int b = row / R, r = row - b * R;
-  if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0)) {
+  const int ci = inv[row];  // compact index, -1 for rows that are not real
+  if (ci < 0) {
     if (lane == 0) argmax_out[row] = -1;
     return;
   }
   float bv = -INFINITY;
   int bi = INT_MAX;
-  const int2* pr = part + static_cast<size_t>(row) * vtiles;
+  const int2* pr = part + static_cast<size_t>(ci) * vtiles;
   // eight partials in flight per lane (512 per wave per round)
   for (int t0 = 0; t0 < vtiles; t0 += 8 * kWave) {
     int2 p[8];
@@ -340,37 +388,74 @@ LmPlan lm_plan(int rows, int V, bool bf16) {
   LmPlan p;
   p.vtiles = bf16 ? (V + kLmVT - 1) / kLmVT : (V + kLmF32VT - 1) / kLmF32VT;
   p.mchunks = bf16 ? (rows + kLmMC - 1) / kLmMC : (rows + kLmF32Rows - 1) / kLmF32Rows;
+  // super-tiles of one XCD's worth of workgroups (bf16 path)
+  p.sm = p.mchunks < 8 ? p.mchunks : 8;
+  p.sv = kLmXcdSlots / p.sm;
+  const int n_super = ((p.vtiles + p.sv - 1) / p.sv) * ((p.mchunks + p.sm - 1) / p.sm);
+  p.blocks = kLmXcds * ((n_super + kLmXcds - 1) / kLmXcds) * p.sv * p.sm;
   return p;
 }
 
+// LM-head workspace: [n_rows (256 B)] [row_list: rows ints] [inv: rows ints]
+// [tile partials: rows x vtiles (value, index)], each region 256-byte aligned.
+namespace {
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+struct LmWs {
+  int32_t* n_rows;
+  int32_t* row_list;
+  int32_t* inv;
+  int2* part;
+};
+LmWs lm_ws(void* ws, int rows) {
+  char* p = static_cast<char*>(ws);
+  LmWs w;
+  w.n_rows = reinterpret_cast<int32_t*>(p);
+  p += 256;
+  w.row_list = reinterpret_cast<int32_t*>(p);
+  p += al256(sizeof(int32_t) * rows);
+  w.inv = reinterpret_cast<int32_t*>(p);
+  p += al256(sizeof(int32_t) * rows);
+  w.part = reinterpret_cast<int2*>(p);
+  return w;
+}
+}  // namespace
+
 size_t lm_workspace_bytes(const LmPlan& p, int rows) {
-  return static_cast<size_t>(p.vtiles) * rows * sizeof(int2);
+  return 256 + 2 * al256(sizeof(int32_t) * rows) + static_cast<size_t>(p.vtiles) * rows * sizeof(int2);
+}
+
+hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
+                               const uint8_t* copy_gate, hipStream_t s) {
+  const LmWs w = lm_ws(ws, rows);
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, s, rows, R, W, D,
+                     cand_len, copy_gate, w.row_list, w.inv, w.n_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s) {
-  int2* part = static_cast<int2*>(ws);
+  const LmWs w = lm_ws(ws, rows);
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(plan.mchunks * plan.vtiles), dim3(256), 0, s,
+    hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(plan.blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
-                       rows, hid, V, logits_out, part, plan.vtiles, plan.mchunks);
+                       rows, hid, V, w.row_list, w.n_rows, logits_out, w.part, plan.vtiles,
+                       plan.mchunks, plan.sv, plan.sm);
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
-                       static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), rows,
-                       hid, V, logits_out, part, plan.vtiles);
+                       static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), hid,
+                       V, w.row_list, w.n_rows, logits_out, w.part, plan.vtiles);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   return e;
 }
 
-hipError_t launch_argmax_reduce(const void* ws, const LmPlan& plan, int rows, int R, int W, int D,
-                                const int32_t* cand_len, const uint8_t* copy_gate,
-                                int32_t* argmax_out, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
-                     static_cast<const int2*>(ws), plan.vtiles, rows, R, W, D, cand_len, copy_gate,
-                     argmax_out);
+hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,
+                                hipStream_t s) {
+  const LmWs w = lm_ws(ws, rows);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, w.part,
+                     plan.vtiles, rows, w.inv, argmax_out);
   return hipGetLastError();
 }
 
