@@ -20,6 +20,7 @@ Modules, one per step of the copy path:
 * ``lmhead``  – LM-head logits and greedy (T=0) argmax with top-2 margin.
 * ``accept``  – longest accepted continuation and the token after it.
 * ``commit``  – copying the accepted rows' K/V into the cache, extending the context.
+* ``calibration`` – copy-mode labels, batched probe logits, F1-optimal threshold, ROC AUC.
 * ``bf16``    – exact widening of bfloat16 bit patterns to float64.
 
 Every function states the passage it follows.  Readings of points the pages
@@ -34,9 +35,11 @@ from .attention import allowed_keys, attention_row, blocktri_attention
 from .lmhead import lm_logits, argmax_with_margin, lmhead_argmax
 from .accept import accept_longest
 from .commit import commit_accepted
+from .calibration import copy_labels, probe_logits, threshold_sweep, calibrate
 
 __all__ = [
     "bf16_bits_to_f64", "probe_score", "logit", "kgram_matches", "kgram_retrieve",
     "allowed_keys", "attention_row", "blocktri_attention", "lm_logits",
-    "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted",
+    "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted", "copy_labels",
+    "probe_logits", "threshold_sweep", "calibrate",
 ]
