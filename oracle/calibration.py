@@ -92,5 +92,8 @@ def calibrate(z_layers, y):
         if per[l]["f1"] > per[layer]["f1"]:
             layer = l
     t = per[layer]["t"]
-    tau = 1.0 / (1.0 + math.exp(-t)) if math.isfinite(t) else 1.0
+    if math.isinf(t):
+        tau = 1.0 if t > 0 else 0.0        # the limits of sigma
+    else:
+        tau = 1.0 / (1.0 + math.exp(-t)) if t > -700 else 0.0
     return {"per_layer": per, "layer": layer, "t": t, "tau": tau}

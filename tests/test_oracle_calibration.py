@@ -117,3 +117,15 @@ def test_calibrate_picks_best_layer_lowest_on_ties():
     c = oracle.calibrate(z, y)
     assert c["layer"] == 1 and c["t"] == 2.0
     assert c["tau"] == pytest.approx(1 / (1 + math.exp(-2.0)))
+
+
+def test_calibrate_tau_at_infinite_thresholds():
+    # sigma's limits: t = -inf (every score is -inf, all copies) gives tau = 0,
+    # no positive at all gives t = +inf and tau = 1
+    inf = float("inf")
+    r = oracle.calibrate(np.array([[-inf, -inf]]), np.array([1, 1], np.uint8))
+    assert r["t"] == -inf and r["tau"] == 0.0 and r["per_layer"][0]["f1"] == 1.0
+    r = oracle.calibrate(np.array([[0.3, -2.0]]), np.array([0, 0], np.uint8))
+    assert r["t"] == inf and r["tau"] == 1.0
+    r = oracle.calibrate(np.array([[math.log(0.4 / 0.6), -5.0]]), np.array([1, 0], np.uint8))
+    assert abs(r["tau"] - 0.4) < 1e-15
