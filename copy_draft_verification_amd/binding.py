@@ -36,6 +36,14 @@ _SIGS = {
     "ssd_commit_accepted": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
                                            _i32, _i32, ctypes.c_int, _c_p, _c_p, ctypes.c_int64,
                                            _c_p, _c_p, _c_p, _c_p]),
+    "ssd_copy_labels_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
+    "ssd_copy_labels": (ctypes.c_int, [_c_p, _c_p, _i32, ctypes.c_int64, _i32, _c_p, _c_p,
+                                       ctypes.c_size_t, _c_p]),
+    "ssd_probe_logits": (ctypes.c_int, [_c_p, ctypes.c_int, _c_p, _i32, ctypes.c_int64, _i32, _c_p,
+                                        _c_p]),
+    "ssd_calibrate_workspace_bytes": (ctypes.c_size_t, [_i32, ctypes.c_int64]),
+    "ssd_calibrate": (ctypes.c_int, [_c_p, _c_p, _i32, ctypes.c_int64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                     _c_p, _c_p, ctypes.c_size_t, _c_p]),
 }
 
 
@@ -222,4 +230,74 @@ def commit_accepted(k_cand, v_cand, cand, best_w, best_len, next_token, W, D, k_
         B, W, D, Hkv, d, _dt(k_cand), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
         _ptr(cache_off), _ptr(out["tokens"]), _ptr(out["n_tokens"]), _stream(stream)),
         "commit_accepted")
+    return out
+
+
+def copy_labels_workspace_bytes(total_n):
+    return load().ssd_copy_labels_workspace_bytes(int(total_n))
+
+
+def copy_labels(ids, cu_len, n_train=5, labels=None, workspace=None, stream=None):
+    """Copy-mode label (uint8) of every position of the concatenated contexts.
+    ids [total_n] int32, cu_len [B+1] int32 (cu_len[B] == total_n)."""
+    _dev(ids, "ids", (torch.int32,))
+    _dev(cu_len, "cu_len", (torch.int32,))
+    n, B = ids.numel(), cu_len.numel() - 1
+    if labels is None:
+        labels = torch.empty(n, dtype=torch.uint8, device=ids.device)
+    _dev(labels, "labels", (torch.uint8,))
+    need = copy_labels_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    _check(load().ssd_copy_labels(_ptr(ids), _ptr(cu_len), B, n, n_train, _ptr(labels),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+           "copy_labels")
+    return labels
+
+
+def probe_logits(h, w, z_out=None, stream=None):
+    """z[l][i] = w[l] . h[l][i].  h [L, N, hid] (fp32 | bf16), w [L, hid] fp32 -> z [L, N] fp32."""
+    _dev(h, "h", (torch.float32, torch.bfloat16))
+    _dev(w, "w", (torch.float32,))
+    L, N, hid = h.shape
+    if tuple(w.shape) != (L, hid):
+        raise SwitchSDError(f"w must be [{L}, {hid}], got {tuple(w.shape)}")
+    if z_out is None:
+        z_out = torch.empty(L, N, dtype=torch.float32, device=h.device)
+    _dev(z_out, "z_out", (torch.float32,))
+    _check(load().ssd_probe_logits(_ptr(h), _dt(h), _ptr(w), L, N, hid, _ptr(z_out),
+                                   _stream(stream)), "probe_logits")
+    return z_out
+
+
+def calibrate_workspace_bytes(L, N):
+    return load().ssd_calibrate_workspace_bytes(int(L), int(N))
+
+
+def calibrate(z, labels, out=None, workspace=None, stream=None):
+    """Per-layer F1-optimal threshold and ROC AUC, then the layer and tau.  z [L, N] fp32,
+    labels [N] uint8.  Returns dict thr [L], counts [L, 4] (TP, FP, FN, P), u2 [L] int64,
+    auc [L], best_layer [1] int32, tau [1] fp32 (device tensors)."""
+    _dev(z, "z", (torch.float32,))
+    _dev(labels, "labels", (torch.uint8,))
+    L, N = z.shape
+    if labels.numel() != N:
+        raise SwitchSDError(f"labels must hold {N} entries, got {labels.numel()}")
+    dev = z.device
+    if out is None:
+        out = {"thr": torch.empty(L, dtype=torch.float32, device=dev),
+               "counts": torch.empty(L, 4, dtype=torch.int32, device=dev),
+               "u2": torch.empty(L, dtype=torch.int64, device=dev),
+               "auc": torch.empty(L, dtype=torch.float32, device=dev),
+               "best_layer": torch.empty(1, dtype=torch.int32, device=dev),
+               "tau": torch.empty(1, dtype=torch.float32, device=dev)}
+    need = calibrate_workspace_bytes(L, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", (torch.uint8,))
+    _check(load().ssd_calibrate(_ptr(z), _ptr(labels), L, N, _ptr(out["thr"]), _ptr(out["counts"]),
+                                _ptr(out["u2"]), _ptr(out["auc"]), _ptr(out["best_layer"]),
+                                _ptr(out["tau"]), _ptr(workspace), workspace.numel(),
+                                _stream(stream)), "calibrate")
     return out

@@ -158,4 +158,47 @@ ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const i
                                      n_tokens_out, stream));
 }
 
+size_t ssd_copy_labels_workspace_bytes(int64_t total_n) {
+  if (total_n < 1 || total_n >= (1ll << 30)) return 0;
+  return ssd::labels_workspace_bytes(total_n);
+}
+
+ssd_status_t ssd_copy_labels(const int32_t* ids, const int32_t* cu_len, int32_t B,
+                             int64_t total_n, int32_t n_train, uint8_t* labels, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!ids || !cu_len || !labels || B < 1 || total_n < 1 || total_n >= (1ll << 30) ||
+      n_train < 1 || n_train > SSD_MAX_NTRAIN)
+    return SSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < ssd::labels_workspace_bytes(total_n)) return SSD_ERR_WORKSPACE;
+  return from_hip(ssd::launch_copy_labels(ids, cu_len, B, static_cast<int>(total_n), n_train, labels,
+                                          workspace, stream));
+}
+
+ssd_status_t ssd_probe_logits(const void* h, ssd_dtype_t h_dtype, const float* w, int32_t L,
+                              int64_t N, int32_t hidden, float* z_out, hipStream_t stream) {
+  if (!h || !w || !z_out || L < 1 || L > SSD_MAX_CALIB_L || N < 1 || N >= (1ll << 36) ||
+      hidden < 1 || !valid_dtype(h_dtype))
+    return SSD_ERR_INVALID_ARG;
+  if (hidden > SSD_MAX_PROBE_HIDDEN) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_probe_logits(h, h_dtype == SSD_BF16, w, L, N, hidden, z_out, stream));
+}
+
+size_t ssd_calibrate_workspace_bytes(int32_t L, int64_t N) {
+  if (L < 1 || L > SSD_MAX_CALIB_L || N < 1 || N > SSD_MAX_CALIB_N) return 0;
+  return ssd::calibrate_workspace_bytes(L, N);
+}
+
+ssd_status_t ssd_calibrate(const float* z, const uint8_t* labels, int32_t L, int64_t N,
+                           float* thr_out, int32_t* counts_out, int64_t* u2_out, float* auc_out,
+                           int32_t* best_layer, float* tau_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!z || !labels || !thr_out || !counts_out || !u2_out || !auc_out || !best_layer || !tau_out ||
+      L < 1 || L > SSD_MAX_CALIB_L || N < 1 || N > SSD_MAX_CALIB_N)
+    return SSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < ssd::calibrate_workspace_bytes(L, N)) return SSD_ERR_WORKSPACE;
+  return from_hip(ssd::launch_calibrate(z, labels, L, static_cast<int>(N), thr_out, counts_out,
+                                        reinterpret_cast<long long*>(u2_out), auc_out, best_layer,
+                                        tau_out, workspace, stream));
+}
+
 }  // extern "C"

@@ -48,6 +48,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Eight consecutive elements of a bf16 (one 16-byte load) or fp32 (two) row.
+template <typename T> struct Chunk8;
+template <> struct Chunk8<uint16_t> {
+  uint4 v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ float at(int e) const {
+    const uint32_t w = (&v.x)[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ float at(int e) const { return e < 4 ? (&a.x)[e] : (&b.x)[e - 4]; }
+};
+
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no
 // swizzle, offset addressing): loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;

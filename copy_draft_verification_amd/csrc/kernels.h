@@ -61,4 +61,16 @@ hipError_t launch_commit(const void* k_cand, const void* v_cand, const int32_t* 
                          long long cache_rows, const long long* cache_off, int32_t* tokens_out,
                          int32_t* n_tokens_out, hipStream_t s);
 
+// Offline probe calibration: copy-mode labels, batched probe logits, and the
+// per-layer F1 / AUC sweep with the layer choice.
+size_t labels_workspace_bytes(long long total_n);
+hipError_t launch_copy_labels(const int32_t* ids, const int32_t* cu_len, int B, int total_n,
+                              int n_train, uint8_t* labels, void* ws, hipStream_t s);
+hipError_t launch_probe_logits(const void* h, bool bf16, const float* w, int L, long long N,
+                               int hid, float* z, hipStream_t s);
+size_t calibrate_workspace_bytes(int L, long long N);
+hipError_t launch_calibrate(const float* z, const uint8_t* labels, int L, int N, float* thr_out,
+                            int32_t* counts_out, long long* u2_out, float* auc_out,
+                            int32_t* best_layer, float* tau, void* ws, hipStream_t s);
+
 }  // namespace ssd

@@ -15,24 +15,6 @@ namespace ssd {
 constexpr int kPrThreads = 256;
 constexpr int kPrUnroll = 4;   // chunks in flight per thread (hidden <= 8192 in one pass)
 
-template <typename T> struct Chunk8;
-template <> struct Chunk8<uint16_t> {
-  uint4 v;
-  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ float at(int e) const {
-    const uint32_t w = (&v.x)[e >> 1];
-    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
-};
-template <> struct Chunk8<float> {
-  float4 a, b;
-  __device__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
-  }
-  __device__ float at(int e) const { return e < 4 ? (&a.x)[e] : (&b.x)[e - 4]; }
-};
-
 template <typename T>
 __global__ __launch_bounds__(kPrThreads) void probe_kernel(const T* __restrict__ h,
                                                            const float* __restrict__ w, int hidden,

@@ -14,6 +14,13 @@
  * and, after accept, ssd_commit_accepted copies the accepted tokens' keys and
  * values into the caller's KV cache and lists the tokens that extend the context.
  *
+ * Offline, before decoding, three calls calibrate the probe (paper §3.2):
+ *
+ *   ssd_copy_labels     copy-mode label of every position of whole contexts
+ *   ssd_probe_logits    probe logit of every position at every layer
+ *   ssd_calibrate       per layer the F1-optimal threshold and ROC AUC, then the
+ *                       layer and tau used by ssd_probe_score
+ *
  * Conventions shared by every call:
  *  - Pointers to arrays are DEVICE pointers (hipMalloc / torch CUDA tensors);
  *    scalars are passed by value from the host.  Arrays are dense, row-major,
@@ -48,7 +55,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -64,6 +71,10 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
 #define SSD_MAX_W 64      /* candidates per sequence */
 #define SSD_MAX_D 64      /* tokens per candidate */
 #define SSD_MAX_KAPPA 64  /* kappa-gram length */
+#define SSD_MAX_NTRAIN 64 /* copy-label window length (calibration) */
+#define SSD_MAX_PROBE_HIDDEN 16384 /* hidden size of the batched probe logits */
+#define SSD_MAX_CALIB_N (1 << 28)  /* scored positions per layer (calibration) */
+#define SSD_MAX_CALIB_L 65535      /* layers (calibration) */
 
 int ssd_abi_version(void);
 const char* ssd_status_string(int status);
@@ -202,6 +213,69 @@ ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const i
                                  int32_t Hkv, int32_t d, ssd_dtype_t dtype, void* k_cache,
                                  void* v_cache, int64_t cache_rows, const int64_t* cache_off,
                                  int32_t* tokens_out, int32_t* n_tokens_out, hipStream_t stream);
+
+/*
+ * Offline probe calibration, step 1: copy-mode labels.  Paper §3.2 "Problem
+ * Formulation": a position is a copy-mode instance when it lies inside a
+ * verbatim run of at least n_train tokens that also occurs earlier in the same
+ * context.  Computed as: labels[i] = 1 exactly when some n_train-window
+ * containing i (inside i's context) also starts at an earlier position of that
+ * context (the earlier occurrence may overlap it).
+ *   ids      [total_n] int32: the contexts, concatenated
+ *   cu_len   [B+1] int32: context b is ids[cu_len[b] .. cu_len[b+1]); the caller
+ *            guarantees cu_len[B] == total_n
+ *   labels   [total_n] uint8 (output): 1 = copy-mode, 0 = not
+ *   workspace at least ssd_copy_labels_workspace_bytes(total_n) bytes of device
+ *            memory, 8-byte aligned; its contents on entry do not matter
+ * Errors: INVALID_ARG (nulls, B < 1, total_n outside [1, 2^30), n_train outside
+ *   [1, SSD_MAX_NTRAIN]), WORKSPACE.
+ */
+size_t ssd_copy_labels_workspace_bytes(int64_t total_n);
+ssd_status_t ssd_copy_labels(const int32_t* ids, const int32_t* cu_len, int32_t B,
+                             int64_t total_n, int32_t n_train, uint8_t* labels, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Offline probe calibration, step 2: probe logits of every position at every
+ * layer (paper §3.2: a probe per layer, scored on the layer's hidden states;
+ * write-up §2.3: bias-free linear probe).
+ *   z[l][i] = sum_k w[l][k] * h[l][i][k]   (fp32 fused multiply-adds)
+ *   h  [L][N][hidden], dtype h_dtype
+ *   w  [L][hidden] float
+ *   z_out [L][N] float (output)
+ * Errors: INVALID_ARG (nulls, L outside [1, SSD_MAX_CALIB_L], N outside
+ *   [1, 2^36), hidden < 1, unknown dtype), UNSUPPORTED (hidden >
+ *   SSD_MAX_PROBE_HIDDEN).
+ */
+ssd_status_t ssd_probe_logits(const void* h, ssd_dtype_t h_dtype, const float* w, int32_t L,
+                              int64_t N, int32_t hidden, float* z_out, hipStream_t stream);
+
+/*
+ * Offline probe calibration, step 3: threshold and layer.  Paper §3.2 "Layer
+ * and Threshold Selection": per layer the decision threshold maximising F1 on
+ * the labelled set, and the layer with the highest F1; §4.3.3 reports the ROC AUC.
+ * Per layer l, over the thresholds t in {z[l][i]} with copy predicted when
+ * z >= t: the t with the highest F1 = 2TP / (2TP + FP + FN) (compared exactly as
+ * integer fractions; a tie goes to the higher t), and 2U, the Mann-Whitney
+ * statistic doubled (equal scores count one half each).  Then the layer with the
+ * highest F1 (the lower layer on ties) and tau = sigmoid(its t).
+ *   z       [L][N] float: scores (finite; -0 and +0 are one score)
+ *   labels  [N] uint8: nonzero = copy-mode (the same positions for every layer)
+ *   thr_out [L] float: the chosen t per layer; +inf when no t gives TP > 0
+ *   counts_out [L][4] int32: TP, FP, FN at that t, and the positives P
+ *   u2_out  [L] int64: 2U;  auc_out [L] float: 2U / (2 P (N - P)), NaN when
+ *           P = 0 or P = N
+ *   best_layer [1] int32, tau_out [1] float: the layer choice and
+ *           sigmoid(thr_out[best_layer]) (1 for t = +inf)
+ *   workspace at least ssd_calibrate_workspace_bytes(L, N) bytes, 8-byte aligned
+ * Errors: INVALID_ARG (nulls, L outside [1, SSD_MAX_CALIB_L], N outside
+ *   [1, SSD_MAX_CALIB_N]), WORKSPACE.
+ */
+size_t ssd_calibrate_workspace_bytes(int32_t L, int64_t N);
+ssd_status_t ssd_calibrate(const float* z, const uint8_t* labels, int32_t L, int64_t N,
+                           float* thr_out, int32_t* counts_out, int64_t* u2_out, float* auc_out,
+                           int32_t* best_layer, float* tau_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,9 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) >= {"ssd_probe_score", "ssd_kgram_retrieve", "ssd_blocktri_verify",
                           "ssd_accept_longest", "ssd_verify_workspace_bytes", "ssd_abi_version",
-                          "ssd_status_string", "ssd_commit_accepted"}
+                          "ssd_status_string", "ssd_commit_accepted", "ssd_copy_labels",
+                          "ssd_copy_labels_workspace_bytes", "ssd_probe_logits",
+                          "ssd_calibrate", "ssd_calibrate_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -130,3 +132,62 @@ def test_commit_validation(lib):
         assert call(**{k: bad}) == 1, (k, bad)
     assert call(Hkv=1, d=3) == 2                        # 6-byte rows: not 16-byte pieces
     assert call(dtype=0, Hkv=1, d=2) == 2               # 8-byte fp32 rows
+
+
+def test_copy_labels_validation(lib):
+    f = lib.ssd_copy_labels
+    ws = lib.ssd_copy_labels_workspace_bytes
+    assert ws(0) == 0 and ws(1 << 30) == 0
+    assert ws(1000) >= 2048 * 8 + 1000                  # table of >= 2n slots + repeat flags
+    good = dict(ids=FAKE, cu=FAKE, B=2, n=1000, n_train=5, labels=FAKE, ws=FAKE, wsb=ws(1000),
+                stream=None)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return f(*a.values())
+
+    for k in ("ids", "cu", "labels"):
+        assert call(**{k: None}) == 1, k
+    for k, bad in (("B", 0), ("n", 0), ("n", 1 << 30), ("n_train", 0), ("n_train", 65)):
+        assert call(**{k: bad}) == 1, (k, bad)
+    assert call(ws=None) == 3
+    assert call(wsb=ws(1000) - 1) == 3
+
+
+def test_probe_logits_validation(lib):
+    f = lib.ssd_probe_logits
+    good = dict(h=FAKE, dtype=1, w=FAKE, L=32, N=4096, hid=4096, z=FAKE, stream=None)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return f(*a.values())
+
+    for k in ("h", "w", "z"):
+        assert call(**{k: None}) == 1, k
+    for k, bad in (("L", 0), ("L", 65536), ("N", 0), ("N", 1 << 36), ("hid", 0), ("dtype", 2)):
+        assert call(**{k: bad}) == 1, (k, bad)
+    assert call(hid=16385) == 2
+
+
+def test_calibrate_validation(lib):
+    f = lib.ssd_calibrate
+    ws = lib.ssd_calibrate_workspace_bytes
+    assert ws(32, 4096) == 32 * 4096 * 8
+    assert ws(3, 5000) == 3 * 8192 * 8                  # padded to a power of two per layer
+    assert ws(0, 10) == 0 and ws(1, 0) == 0 and ws(1, (1 << 28) + 1) == 0
+    good = dict(z=FAKE, labels=FAKE, L=4, N=5000, thr=FAKE, counts=FAKE, u2=FAKE, auc=FAKE,
+                best=FAKE, tau=FAKE, ws=FAKE, wsb=ws(4, 5000), stream=None)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return f(*a.values())
+
+    for k in ("z", "labels", "thr", "counts", "u2", "auc", "best", "tau"):
+        assert call(**{k: None}) == 1, k
+    for k, bad in (("L", 0), ("L", 65536), ("N", 0), ("N", (1 << 28) + 1)):
+        assert call(**{k: bad}) == 1, (k, bad)
+    assert call(ws=None) == 3
+    assert call(wsb=ws(4, 5000) - 8) == 3

@@ -13,6 +13,8 @@ the write-up's CopyDiversity table (§2.2: 10.6 / 11.7 / 77.7 %) and the copy
 trigger rates of its Table 1 set the planted-repeat densities; no dataset item
 of any benchmark is used.
 """
-from .gen import CONFIGS, Workload, generate, spec, f32_to_bf16_bits, to_torch, generate_with_ids
+from .gen import (CALIB_CONFIGS, CONFIGS, CalibWorkload, Workload, f32_to_bf16_bits, generate,
+                  generate_calibration, generate_with_ids, spec, to_torch)
 
-__all__ = ["CONFIGS", "Workload", "generate", "spec", "f32_to_bf16_bits", "to_torch", "generate_with_ids"]
+__all__ = ["CALIB_CONFIGS", "CONFIGS", "CalibWorkload", "Workload", "f32_to_bf16_bits", "generate",
+           "generate_calibration", "generate_with_ids", "spec", "to_torch"]

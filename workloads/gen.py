@@ -389,3 +389,87 @@ def generate_with_ids(s, id_lists, anchor_copy=None):
                     _normal(s.seed, "kc", (B, s.W * s.D, s.Hkv, s.d), 1.0, s.dtype),
                     _normal(s.seed, "vc", (B, s.W * s.D, s.Hkv, s.d), 1.0, s.dtype),
                     _normal(s.seed, "lm", (s.V, s.hid), s.lm_std, s.dtype))
+
+
+# ---------------------------------------------------------------- probe calibration
+@dataclass(frozen=True)
+class CalibSpec:
+    name: str
+    B: int                   # contexts
+    n: tuple                 # (lo, hi): n_b ~ U{lo..hi}
+    V: int
+    zipf: float
+    coverage: float          # fraction of positions inside planted copies (spans >= 5)
+    span: tuple              # planted span lengths
+    short_frac: float        # accidental 2..4-token repeats (not copies), fraction of positions
+    L: int                   # layers
+    hid: int
+    dtype: str               # "f32" or "bf16"
+    seed: int
+    peak_layer: int          # layer where the planted copy signal is strongest
+    sep_peak: float = 3.0    # planted shift along the layer's probe direction at the peak
+    sep_floor: float = 0.3   # ... far from the peak
+    width: float = 5.0       # layers over which the shift decays (Gaussian profile)
+
+
+CALIB_CONFIGS = {
+    # full-size: one Llama-3.1-8B-shaped context, 32 layers of 4096-wide states
+    "calib_llama8b": CalibSpec("calib_llama8b", 1, (4096, 4096), 128256, 1.1, 0.106, (5, 200), 0.05,
+                               32, 4096, "bf16", 3001, 14),
+    # small parity shapes (ragged contexts, odd hidden size for the fp32 path)
+    "calib_small_bf16": CalibSpec("calib_small_bf16", 3, (300, 900), 400, 1.1, 0.15, (5, 60), 0.05,
+                                  6, 512, "bf16", 3002, 3),
+    "calib_small_f32": CalibSpec("calib_small_f32", 2, (200, 700), 300, 1.1, 0.15, (5, 60), 0.05,
+                                 5, 200, "f32", 3003, 2),
+}
+
+
+@dataclass
+class CalibWorkload:
+    spec: CalibSpec
+    ids: np.ndarray          # [sum n] int32
+    cu_len: np.ndarray       # [B+1] int32
+    copy_pos: np.ndarray     # [sum n] bool: destinations of the planted copies
+    H: np.ndarray            # [L, sum n, hid] float32 or bf16 bits: per-layer states
+    w: np.ndarray            # [L, hid] float32: per-layer probe vectors
+
+
+def generate_calibration(name, **overrides):
+    """Contexts with planted verbatim copies (>= 5 tokens) and accidental short repeats, and
+    per-layer states h = N(0, I) + sep_l * w_l / |w_l| at the planted copy positions, with
+    sep_l peaking at peak_layer.  The copy signal comes from the planted positions, not
+    from any labelling rule."""
+    s = CALIB_CONFIGS[name]
+    if overrides:
+        s = replace(s, **overrides)
+    nrng = _rng(s.seed, _TAGS["n"])
+    ns = [int(nrng.integers(s.n[0], s.n[1] + 1)) for _ in range(s.B)]
+    ids, copy = [], []
+    for b in range(s.B):
+        ctx = _Ctx(_rng(s.seed, _TAGS["ids"], b), ns[b], s.V, s.zipf)
+        ctx.random_spans(s.span[0], s.span[1], int(s.coverage * ns[b]), ns[b])
+        ctx.random_spans(2, 4, int(s.short_frac * ns[b]), ns[b], label=False)
+        ids.append(ctx.x)
+        copy.append(ctx.copy)
+    ids = np.concatenate(ids).astype(np.int32)
+    copy_pos = np.concatenate(copy)
+    cu = np.zeros(s.B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ns)
+    N = int(cu[-1])
+    w = np.empty((s.L, s.hid), np.float32)
+    H = np.empty((s.L, N, s.hid), np.float32 if s.dtype == "f32" else np.uint16)
+    rows = np.nonzero(copy_pos)[0]
+    for l in range(s.L):
+        wl = _rng(s.seed, _TAGS["w"], l).standard_normal(s.hid, dtype=np.float32) / np.float32(np.sqrt(s.hid))
+        w[l] = wl
+        sep = s.sep_floor + (s.sep_peak - s.sep_floor) * float(np.exp(-((l - s.peak_layer) / s.width) ** 2))
+        u = (wl / np.linalg.norm(wl)).astype(np.float32) * np.float32(sep)
+        rng = _rng(s.seed, _TAGS["h"], l)
+        step = max(1, (1 << 24) // s.hid)
+        for r0 in range(0, N, step):
+            r1 = min(N, r0 + step)
+            x = rng.standard_normal((r1 - r0, s.hid), dtype=np.float32)
+            sel = rows[(rows >= r0) & (rows < r1)] - r0
+            x[sel] += u
+            H[l, r0:r1] = x if s.dtype == "f32" else f32_to_bf16_bits(x)
+    return CalibWorkload(s, ids, cu, copy_pos, H, w)
