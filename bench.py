@@ -11,6 +11,12 @@ synthetic (seeded) and resident in HBM before timing starts.
 Prints one JSON line: copy-steps/s (whole job), verified candidate tokens/s,
 the LM-head kernel's roofline position (HIP events around that kernel in the
 timed region) and the CPU oracle timed on the host on a bounded sample.
+
+    python bench.py --calibration [--steps K] [--warmup W]
+
+measures the offline probe calibration instead: one pass is copy labels, probe
+logits at every position of every layer, and the per-layer F1 / AUC sweep with the
+layer choice, over a 32-layer, 4096-position, 4096-wide bf16 set.
 """
 import argparse
 import json
@@ -38,6 +44,8 @@ def parse():
                    help="anchor mode of the synthetic contexts (default: the workload's own)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--calibration", action="store_true",
+                   help="time the offline probe calibration pass instead of the decoding step")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference point that scales the "
                         "HBM byte counters) and exit")
@@ -47,6 +55,8 @@ def parse():
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_bf16_kernel.llama8b_b1.traffic.txt")
 LM_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "lmhead.hip")
+CAL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probe_logits_kernel.calib_llama8b.traffic.txt")
+CAL_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "calib.hip")
 
 
 def calibrate_copy():
@@ -62,19 +72,19 @@ def calibrate_copy():
         print(f"[copy] {i} copied {COPY_BYTES} bytes", file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the LM-head kernel from the committed counter summary,
-    or None when it does not cover this workload or the kernel source changed since."""
+def measured_traffic(workload, path=TRAFFIC_FILE, source=LM_SOURCE):
+    """HBM bytes per launch of a kernel from its committed counter summary, or None
+    when it does not cover this workload or the kernel source changed since."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    with open(LM_SOURCE, "rb") as f:
+    with open(source, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     if kv.get("workload") != workload or kv.get("source_sha256") != sha:
         return None
@@ -158,6 +168,134 @@ def cpu_baseline(wl, budget_s):
             "measured_s": round(t_int + t_att + t_lm + t_acc, 2)}
 
 
+def calibration_cpu_baseline(c, budget_s):
+    """The oracle's calibration on whole layers of the same set (labels once, then
+    probe logits and the sweep layer by layer) until the budget is spent; the
+    per-layer time is scaled to all layers."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    L = c.H.shape[0]
+    t0 = time.perf_counter()
+    y = oracle.copy_labels(c.ids, c.cu_len)
+    t_lab = time.perf_counter() - t0
+    t_layers, done = 0.0, 0
+    for l in range(L):
+        t0 = time.perf_counter()
+        z = oracle.probe_logits(c.H[l:l + 1], c.w[l:l + 1], c.spec.dtype)
+        oracle.threshold_sweep(z[0], y)
+        t_layers += time.perf_counter() - t0
+        done += 1
+        if t_lab + t_layers > budget_s:
+            break
+    t_pass = t_lab + t_layers * L / done
+    return {"value": 1.0 / t_pass, "unit": "calibration-passes/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"{c.spec.name}: labels of all {c.H.shape[1]} positions ({t_lab:.2f}s), "
+                       f"probe logits + F1/AUC sweep on {done} of {L} layers ({t_layers:.2f}s), "
+                       f"scaled to all layers: {t_pass:.2f}s per pass"),
+            "measured_s": round(t_lab + t_layers, 2)}
+
+
+def bench_calibration(a):
+    """Offline probe calibration: labels -> probe logits -> sweep + layer choice, no
+    host synchronisation inside a pass.  The roofline entry is the probe
+    logit GEMV (it streams every layer's states once from HBM)."""
+    import torch
+    import copy_draft_verification_amd as cdv
+    from workloads import generate_calibration, to_torch
+
+    c = generate_calibration("calib_llama8b")
+    s = c.spec
+    L, N, hid = c.H.shape
+    dev = "cuda:0"
+    up = lambda x: to_torch(x, dev)  # noqa: E731
+    ids, cu, H, w = up(c.ids), up(c.cu_len), up(c.H), up(c.w)
+    lab = torch.empty(N, dtype=torch.uint8, device=dev)
+    lws = torch.empty(cdv.copy_labels_workspace_bytes(N), dtype=torch.uint8, device=dev)
+    z = torch.empty(L, N, dtype=torch.float32, device=dev)
+    cws = torch.empty(cdv.calibrate_workspace_bytes(L, N), dtype=torch.uint8, device=dev)
+    out = {"thr": torch.empty(L, dtype=torch.float32, device=dev),
+           "counts": torch.empty(L, 4, dtype=torch.int32, device=dev),
+           "u2": torch.empty(L, dtype=torch.int64, device=dev),
+           "auc": torch.empty(L, dtype=torch.float32, device=dev),
+           "best_layer": torch.empty(1, dtype=torch.int32, device=dev),
+           "tau": torch.empty(1, dtype=torch.float32, device=dev)}
+    stream = torch.cuda.current_stream()
+    # the labels depend only on the token ids: they run on a second stream (default
+    # priority) beside the probe-logit GEMV and are joined before the sweep
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def one(ev=None):
+        fork.record(stream)
+        side.wait_event(fork)
+        cdv.copy_labels(ids, cu, 5, labels=lab, workspace=lws, stream=side)
+        join.record(side)
+        if ev is not None:
+            ev[0].record(stream)
+        cdv.probe_logits(H, w, z_out=z, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        stream.wait_event(join)
+        cdv.calibrate(z, lab, out=out, workspace=cws, stream=stream)
+
+    print(f"[bench] calibration {s.name} L={L} N={N} hid={hid} warmup={a.warmup} steps={a.steps}",
+          file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(a.steps):
+        one(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_begin.elapsed_time(t_end) / a.steps
+    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    elt = 2 if s.dtype == "bf16" else 4
+    k_bytes = L * N * hid * elt + L * hid * 4 + L * N * 4
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    print(f"[bench] {ms:.4f} ms/pass, probe-logits kernel {k_ms:.4f} ms ({achieved:.0f} GB/s), "
+          f"layer {int(out['best_layer'][0])} tau {float(out['tau'][0]):.4f}", file=sys.stderr, flush=True)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name, CAL_TRAFFIC_FILE, CAL_SOURCE),
+            "kernel": "probe_logits_kernel", "kernel_ms": round(k_ms, 4),
+            "algorithmic_bytes": int(k_bytes)}
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = calibration_cpu_baseline(c, a.cpu_budget_s)
+    line = {
+        "metric": "probe calibration passes/sec (labels + per-layer probe logits + F1/AUC sweep)",
+        "value": round(1.0 / (ms * 1e-3), 2),
+        "unit": "calibration-passes/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": s.name, "L": L, "N": N, "hid": hid, "n_train": 5,
+                   "parallelism": "single-gpu"},
+        "scored_positions_per_s": round(L * N / (ms * 1e-3), 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -167,6 +305,9 @@ def main():
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.calibration:
+        bench_calibration(a)
         return
     import torch
     import copy_draft_verification_amd as cdv

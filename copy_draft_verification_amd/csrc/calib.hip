@@ -15,11 +15,13 @@
 // contain each position.  Every output byte is written exactly once.
 //
 // Probe logits.  z[l][i] = w_l . H[l][i] is a batched GEMV that streams the
-// states once from HBM; w_l sits in LDS, one wave reduces one row.
+// states once from HBM with nontemporal loads (each state is read once); w_l
+// sits in LDS, shared by the 8 waves of a workgroup; one wave reduces one row.
 //
 // Sweep.  Per layer the (score, label) pairs are sorted by descending score
-// (a bitonic network: chunks of 8192 keys in LDS, longer strides as separate
-// global passes), then one workgroup walks the sorted keys carrying the running
+// (a bitonic network over a power of two of at least 1024 keys, padded with keys
+// that sort last: chunks of up to 8192 per workgroup in registers, wave shuffles
+// and LDS, longer strides as separate global passes), then one workgroup walks the sorted keys carrying the running
 // counts.  At the last element of each group of equal scores it evaluates the
 // threshold t = that score (copy predicted when z >= t): TP = positives so far,
 // FP = negatives so far.  F1 = 2TP / (2TP + FP + FN) is compared exactly as a
@@ -170,8 +172,8 @@ hipError_t launch_copy_labels(const int32_t* ids, const int32_t* cu_len, int B, 
 }
 
 // ---------------------------------------------------------------- probe logits
-constexpr int kPlThreads = 256;
-constexpr int kPlRowsPerWave = 8;
+constexpr int kPlThreads = 512;
+constexpr int kPlRowsPerWave = 16;
 constexpr int kPlRows = kPlRowsPerWave * (kPlThreads / kWave);   // rows per workgroup
 constexpr int kPlUnroll = 8;                                     // 16-byte loads in flight per lane
 
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kPlThreads) void probe_logits_kernel(const T* __res
 #pragma unroll
         for (int u = 0; u < kPlUnroll; ++u) {
           const int c = c0 + u * kWave + lane;
-          if (c < nch) hv[u].load(hr + 8 * c);
+          if (c < nch) hv[u].load_stream(hr + 8 * c);
         }
 #pragma unroll
         for (int u = 0; u < kPlUnroll; ++u) {
@@ -241,7 +243,7 @@ hipError_t launch_probe_logits(const void* h, bool bf16, const float* w, int L, 
 
 // ---------------------------------------------------------------- sweep
 constexpr int kSwThreads = 1024;
-constexpr int kSwChunk = 8192;   // keys sorted per workgroup in LDS (64 KiB)
+constexpr int kSwChunk = kSwThreads * 8;   // largest chunk sorted by one workgroup (64 KiB of LDS)
 constexpr int kScThreads = 512;  // workgroup of the scan (one per layer)
 constexpr int kSwPer = 8;        // keys per thread per pass of the scan
 constexpr unsigned long long kPadKey = ~0ull;
@@ -278,31 +280,83 @@ __global__ __launch_bounds__(256) void sweep_keys_kernel(const float* __restrict
 // (lo, lo + j), sorted ascending when bit k of lo (global index) is clear.
 __device__ __forceinline__ int pair_lo(int p, int j) { return ((p & ~(j - 1)) << 1) | (p & (j - 1)); }
 
-// k_merge == 0: sort each chunk with every stage k <= chunk.  Otherwise finish
-// the merge of size k_merge with the strides j < chunk.
+__device__ __forceinline__ void cmp_swap(unsigned long long& a, unsigned long long& b, bool up) {
+  const unsigned long long lo = a < b ? a : b, hi = a < b ? b : a;
+  a = up ? lo : hi;
+  b = up ? hi : lo;
+}
+
+// Strides below E stay inside one thread's E keys.
+template <int E, int J>
+__device__ __forceinline__ void reg_stage(unsigned long long (&r)[E], int gi0, int k) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((e & J) == 0) cmp_swap(r[e], r[e | J], ((gi0 + e) & k) == 0);
+}
+
+// One chunk of 1024 * E keys per workgroup (E = 1, 2, 4 or 8); thread t holds
+// keys E*t .. E*t+E-1 in registers.  Strides below E are exchanged in registers,
+// E .. 32*E between lanes of a wave (shuffles, no barrier), 64*E and up through
+// LDS, where key i sits at (i % E) * 1024 + i / E so that the lanes of a wave
+// touch consecutive words.  k_merge == 0: sort the chunk with every stage k up
+// to the chunk size.  Otherwise finish the merge of size k_merge (larger than
+// the chunk) with the strides below the chunk size.
+template <int E>
 __global__ __launch_bounds__(kSwThreads) void sort_local_kernel(unsigned long long* __restrict__ keys,
-                                                                int Np, int chunk, int k_merge) {
-  __shared__ unsigned long long s[kSwChunk];
-  unsigned long long* kl = keys + static_cast<size_t>(blockIdx.y) * Np + static_cast<size_t>(blockIdx.x) * chunk;
-  const int base = blockIdx.x * chunk;
-  for (int i = threadIdx.x; i < chunk; i += kSwThreads) s[i] = kl[i];
-  __syncthreads();
-  const int k0 = k_merge ? k_merge : 2, k1 = k_merge ? k_merge : chunk;
+                                                                int Np, int k_merge) {
+  constexpr int C = kSwThreads * E;
+  __shared__ unsigned long long s[C];
+  const int t = threadIdx.x;
+  const int base = blockIdx.x * C;
+  unsigned long long* kl = keys + static_cast<size_t>(blockIdx.y) * Np + base;
+  unsigned long long r[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) r[e] = kl[t * E + e];
+  const int gi0 = base + t * E;
+  const int k0 = k_merge ? k_merge : 2, k1 = k_merge ? k_merge : C;
   for (int k = k0; k <= k1; k <<= 1) {
-    for (int j = (k_merge ? chunk : k) >> 1; j > 0; j >>= 1) {
-      for (int p = threadIdx.x; p < chunk / 2; p += kSwThreads) {
-        const int lo = pair_lo(p, j), hi = lo + j;
-        const bool up = ((base + lo) & k) == 0;
-        const unsigned long long a = s[lo], b = s[hi];
-        if (up ? a > b : a < b) {
-          s[lo] = b;
-          s[hi] = a;
+    int j = (k_merge ? C : k) >> 1;
+    if (j >= E * kWave) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e * kSwThreads + t] = r[e];
+      __syncthreads();
+      for (; j >= E * kWave; j >>= 1) {
+        const int js = j / E;
+#pragma unroll
+        for (int q = 0; q < (E + 1) / 2; ++q) {
+          const int p = t + q * kSwThreads;
+          if (p < C / 2) {
+            const int e = p / (kSwThreads / 2), pm = p % (kSwThreads / 2);
+            const int mlo = pair_lo(pm, js);
+            unsigned long long a = s[e * kSwThreads + mlo], b = s[e * kSwThreads + mlo + js];
+            cmp_swap(a, b, ((base + mlo * E + e) & k) == 0);
+            s[e * kSwThreads + mlo] = a;
+            s[e * kSwThreads + mlo + js] = b;
+          }
         }
+        __syncthreads();
       }
+#pragma unroll
+      for (int e = 0; e < E; ++e) r[e] = s[e * kSwThreads + t];
       __syncthreads();
     }
+    for (; j >= E; j >>= 1) {
+      const int m = j / E;
+      const bool lower = (t & m) == 0;
+      const bool up = (gi0 & k) == 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long b = __shfl_xor(r[e], m, kWave);
+        const unsigned long long mn = r[e] < b ? r[e] : b, mx = r[e] < b ? b : r[e];
+        r[e] = (lower == up) ? mn : mx;
+      }
+    }
+    if constexpr (E > 4) { if (j >= 4) reg_stage<E, 4>(r, gi0, k); }
+    if constexpr (E > 2) { if (j >= 2) reg_stage<E, 2>(r, gi0, k); }
+    if constexpr (E > 1) { if (j >= 1) reg_stage<E, 1>(r, gi0, k); }
   }
-  for (int i = threadIdx.x; i < chunk; i += kSwThreads) kl[i] = s[i];
+#pragma unroll
+  for (int e = 0; e < E; ++e) kl[t * E + e] = r[e];
 }
 
 __global__ __launch_bounds__(256) void sort_global_kernel(unsigned long long* __restrict__ keys,
@@ -466,24 +520,47 @@ __global__ __launch_bounds__(kScThreads) void sweep_scan_kernel(
   }
 }
 
-// Layer with the highest F1 (the lowest layer on ties) and tau = sigma(t).
-__global__ void select_layer_kernel(const float* __restrict__ thr, const int32_t* __restrict__ counts,
-                                    int L, int32_t* __restrict__ best_layer, float* __restrict__ tau) {
-  if (threadIdx.x != 0) return;
-  int best = 0;
-  for (int l = 1; l < L; ++l) {
-    const int tp = counts[4 * l], tb = counts[4 * best];
+// Layer with the highest F1 (the lowest layer on ties) and tau = sigma(t).  One
+// wave: each lane keeps the best of its layers, then a butterfly keeps the best
+// of all (ties to the lower layer).
+__global__ __launch_bounds__(kWave) void select_layer_kernel(const float* __restrict__ thr,
+                                                             const int32_t* __restrict__ counts, int L,
+                                                             int32_t* __restrict__ best_layer,
+                                                             float* __restrict__ tau) {
+  const int lane = threadIdx.x;
+  int bl = 0x7fffffff, btp = 0;
+  long long bden = 1;
+  for (int l = lane; l < L; l += kWave) {
+    const int tp = counts[4 * l];
     const long long den = 2ll * tp + counts[4 * l + 1] + counts[4 * l + 2];
-    const long long db = 2ll * tb + counts[4 * best + 1] + counts[4 * best + 2];
-    if (tp > 0 && (tb == 0 || f1_higher(tp, den, tb, db))) best = l;
+    if (bl == 0x7fffffff || f1_higher(tp, den, btp, bden)) {
+      bl = l;
+      btp = tp;
+      bden = den;
+    }
   }
-  const double t = thr[best];
-  *best_layer = best;
-  *tau = static_cast<float>(isinf(t) ? (t > 0 ? 1.0 : 0.0) : 1.0 / (1.0 + exp(-t)));
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int ol = __shfl_xor(bl, o, kWave), otp = __shfl_xor(btp, o, kWave);
+    const long long oden = __shfl_xor(bden, o, kWave);
+    const bool take = ol != 0x7fffffff &&
+                      (bl == 0x7fffffff || f1_higher(otp, oden, btp, bden) ||
+                       (!f1_higher(btp, bden, otp, oden) && ol < bl));
+    if (take) {
+      bl = ol;
+      btp = otp;
+      bden = oden;
+    }
+  }
+  if (lane == 0) {
+    const double t = thr[bl];
+    *best_layer = bl;
+    *tau = static_cast<float>(isinf(t) ? (t > 0 ? 1.0 : 0.0) : 1.0 / (1.0 + exp(-t)));
+  }
 }
 
 int sweep_padded(long long N) {
-  int Np = 1;
+  int Np = kSwThreads;
   while (Np < N) Np <<= 1;
   return Np;
 }
@@ -496,15 +573,23 @@ hipError_t launch_calibrate(const float* z, const uint8_t* labels, int L, int N,
                             int32_t* counts_out, long long* u2_out, float* auc_out,
                             int32_t* best_layer, float* tau, void* ws, hipStream_t s) {
   const int Np = sweep_padded(N);
-  const int chunk = Np < kSwChunk ? Np : kSwChunk;
   auto* keys = static_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(sweep_keys_kernel, dim3((Np + 255) / 256, L), dim3(256), 0, s, z, labels, N, Np, keys);
+  const int chunk = Np < kSwChunk ? Np : kSwChunk;
   const dim3 lgrid(Np / chunk, L);
-  hipLaunchKernelGGL(sort_local_kernel, lgrid, dim3(kSwThreads), 0, s, keys, Np, chunk, 0);
+  auto local = [&](int k_merge) {
+    switch (chunk / kSwThreads) {
+      case 1: hipLaunchKernelGGL(sort_local_kernel<1>, lgrid, dim3(kSwThreads), 0, s, keys, Np, k_merge); break;
+      case 2: hipLaunchKernelGGL(sort_local_kernel<2>, lgrid, dim3(kSwThreads), 0, s, keys, Np, k_merge); break;
+      case 4: hipLaunchKernelGGL(sort_local_kernel<4>, lgrid, dim3(kSwThreads), 0, s, keys, Np, k_merge); break;
+      default: hipLaunchKernelGGL(sort_local_kernel<8>, lgrid, dim3(kSwThreads), 0, s, keys, Np, k_merge); break;
+    }
+  };
+  local(0);
   for (int k = 2 * chunk; k <= Np; k <<= 1) {
     for (int j = k >> 1; j >= chunk; j >>= 1)
       hipLaunchKernelGGL(sort_global_kernel, dim3((Np / 2 + 255) / 256, L), dim3(256), 0, s, keys, Np, k, j);
-    hipLaunchKernelGGL(sort_local_kernel, lgrid, dim3(kSwThreads), 0, s, keys, Np, chunk, k);
+    local(k);
   }
   hipLaunchKernelGGL(sweep_scan_kernel, dim3(L), dim3(kScThreads), 0, s, keys, N, Np, thr_out,
                      counts_out, u2_out, auc_out);

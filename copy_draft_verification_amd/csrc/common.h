@@ -11,6 +11,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -53,6 +54,12 @@ template <typename T> struct Chunk8;
 template <> struct Chunk8<uint16_t> {
   uint4 v;
   __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  // Streaming read (nontemporal hint): for data read once, so that it does not
+  // displace reused lines in the caches.
+  __device__ void load_stream(const uint16_t* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v = make_uint4(t.x, t.y, t.z, t.w);
+  }
   __device__ float at(int e) const {
     const uint32_t w = (&v.x)[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -63,6 +70,12 @@ template <> struct Chunk8<float> {
   __device__ void load(const float* p) {
     a = *reinterpret_cast<const float4*>(p);
     b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ void load_stream(const float* p) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+    a = make_float4(x[0], x[1], x[2], x[3]);
+    b = make_float4(y[0], y[1], y[2], y[3]);
   }
   __device__ float at(int e) const { return e < 4 ? (&a.x)[e] : (&b.x)[e - 4]; }
 };

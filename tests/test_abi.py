@@ -175,7 +175,8 @@ def test_calibrate_validation(lib):
     f = lib.ssd_calibrate
     ws = lib.ssd_calibrate_workspace_bytes
     assert ws(32, 4096) == 32 * 4096 * 8
-    assert ws(3, 5000) == 3 * 8192 * 8                  # padded to a power of two per layer
+    assert ws(2, 10) == 2 * 1024 * 8                    # at least 1024 keys per layer
+    assert ws(3, 20000) == 3 * 32768 * 8                # padded to a power of two per layer
     assert ws(0, 10) == 0 and ws(1, 0) == 0 and ws(1, (1 << 28) + 1) == 0
     good = dict(z=FAKE, labels=FAKE, L=4, N=5000, thr=FAKE, counts=FAKE, u2=FAKE, auc=FAKE,
                 best=FAKE, tau=FAKE, ws=FAKE, wsb=ws(4, 5000), stream=None)

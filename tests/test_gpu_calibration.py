@@ -202,7 +202,7 @@ def _rand_labels(rng, n, p):
     return (rng.random(n) < p).astype(np.uint8)
 
 
-@pytest.mark.parametrize("N,L,levels", [(1, 1, 0), (2, 2, 0), (777, 3, 0), (8192, 2, 0),
+@pytest.mark.parametrize("N,L,levels", [(1, 1, 0), (2, 2, 0), (777, 3, 0), (1500, 2, 0), (3000, 2, 40), (8192, 2, 0),
                                         (8193, 2, 0), (20000, 2, 0), (20000, 2, 300),
                                         (5000, 4, 3)])
 def test_calibrate_sweep_shapes(N, L, levels):
