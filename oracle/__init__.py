@@ -21,6 +21,8 @@ Modules, one per step of the copy path:
 * ``accept``  – longest accepted continuation and the token after it.
 * ``commit``  – copying the accepted rows' K/V into the cache, extending the context.
 * ``calibration`` – copy-mode labels, batched probe logits, F1-optimal threshold, ROC AUC.
+* ``sampling`` – verification at T > 0: candidate trie, recursive rejection with
+  point-mass drafts, Gumbel-max residual draws from Philox4x32-10.
 * ``bf16``    – exact widening of bfloat16 bit patterns to float64.
 
 Every function states the passage it follows.  Readings of points the pages
@@ -36,10 +38,12 @@ from .lmhead import lm_logits, argmax_with_margin, lmhead_argmax
 from .accept import accept_longest
 from .commit import commit_accepted
 from .calibration import copy_labels, probe_logits, threshold_sweep, calibrate
+from .sampling import candidate_trie, philox, sample_step, sample_verify
 
 __all__ = [
     "bf16_bits_to_f64", "probe_score", "logit", "kgram_matches", "kgram_retrieve",
     "allowed_keys", "attention_row", "blocktri_attention", "lm_logits",
     "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted", "copy_labels",
-    "probe_logits", "threshold_sweep", "calibrate",
+    "probe_logits", "threshold_sweep", "calibrate", "candidate_trie", "philox", "sample_step",
+    "sample_verify",
 ]
