@@ -44,6 +44,10 @@ def parse():
                    help="anchor mode of the synthetic contexts (default: the workload's own)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--temperature", type=float, default=0.0,
+                   help="> 0: verify by sampling at this temperature (blocktri_verify_sample + "
+                        "accept_sample) instead of greedy")
+    p.add_argument("--seed", type=int, default=0x5EED, help="sampling seed (with --temperature)")
     p.add_argument("--calibration", action="store_true",
                    help="time the offline probe calibration pass instead of the decoding step")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -54,6 +58,7 @@ def parse():
 
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_bf16_kernel.llama8b_b1.traffic.txt")
+SAMPLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_bf16_kernel_sample.llama8b_b1.traffic.txt")
 LM_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "lmhead.hip")
 CAL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probe_logits_kernel.calib_llama8b.traffic.txt")
 CAL_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "calib.hip")
@@ -339,10 +344,28 @@ def main():
             "best_len": torch.empty(B, dtype=torch.int32, device=dev),
             "next_token": torch.empty(B, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream()
+    T = a.temperature
+    if T > 0:
+        srows = {"n_children": torch.empty(B, R, dtype=torch.int32, device=dev),
+                 "children": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
+                 "child_w": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
+                 "child_logit": torch.empty(B, R, s.W, dtype=torch.float32, device=dev),
+                 "lse": torch.empty(B, R, dtype=torch.float32, device=dev),
+                 "resample": torch.empty(B, R, dtype=torch.int32, device=dev)}
 
-    def step(lm_events=None):
+    def step(lm_events=None, i=0):
         cdv.probe_score(h, w, s.tau, z_out=z, fire_out=fire, stream=stream)
         cdv.kgram_retrieve(ids, cu, s.kappa, s.W, s.D, fire, out=kout, stream=stream)
+        if T > 0:
+            seed = a.seed + i
+            cdv.blocktri_verify_sample(q, kp, vp, cu, wl.max_n, kc, vc, kout["cand"],
+                                       kout["cand_len"], kout["copy_gate"], lm, s.W, s.D, wl.scale,
+                                       T, seed, attn_out=attn, rows=srows, workspace=ws,
+                                       events=lm_events, stream=stream)
+            cdv.accept_sample(srows, kout["copy_gate"], s.W, s.D, seed,
+                              out={k: aout[k] for k in ("best_w", "best_len", "next_token")},
+                              stream=stream)
+            return
         cdv.blocktri_verify(q, kp, vp, cu, wl.max_n, kc, vc, kout["cand_len"], kout["copy_gate"], lm,
                             s.W, s.D, wl.scale, attn_out=attn, argmax_out=am, workspace=ws,
                             events=lm_events, stream=stream)
@@ -366,7 +389,7 @@ def main():
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(a.steps):
-        step(lm_ev[i])
+        step(lm_ev[i], i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_begin.elapsed_time(t_end) / a.steps
@@ -392,12 +415,14 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(tflops / mfma_peak, 4)}
-    roof.update({"traffic": measured_traffic(s.name), "kernel": "lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel",
+    roof.update({"traffic": measured_traffic(s.name, SAMPLE_TRAFFIC_FILE if T > 0 else TRAFFIC_FILE),
+                 "kernel": ("lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel") +
+                           ("<sample>" if T > 0 else ""),
                  "kernel_ms": round(lm_ms, 4), "algorithmic_bytes": int(lm_bytes),
                  "algorithmic_flops": lm_flops, "mfma_tflops": round(tflops, 1)})
 
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and T == 0:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, a.cpu_budget_s)
 
@@ -416,7 +441,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "anchor": s.anchor, "B": B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
                    "hid": s.hid, "Hq": s.Hq, "Hkv": s.Hkv, "d": s.d, "V": s.V, "kappa": s.kappa,
-                   "W": s.W, "D": s.D, "tau": s.tau, "parallelism": "single-gpu"},
+                   "W": s.W, "D": s.D, "tau": s.tau, "temperature": T, "parallelism": "single-gpu"},
         "verified_cand_tokens_per_s": round(sum_L / (ms * 1e-3), 1),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -5,11 +5,11 @@ include/switchsd.h).  This package holds its sources (csrc/), the build script
 (build.py) and a thin ctypes binding (binding.py) with the ABI's names.
 """
 from .binding import (SSD_BF16, SSD_F32, SwitchSDError, abi_version, accept_longest,
-                      blocktri_verify, calibrate, calibrate_workspace_bytes, commit_accepted,
+                      accept_sample, blocktri_verify, blocktri_verify_sample, calibrate, calibrate_workspace_bytes, commit_accepted,
                       copy_labels, copy_labels_workspace_bytes, kgram_retrieve, load,
                       probe_logits, probe_score, verify_workspace_bytes)
 
 __all__ = ["SSD_BF16", "SSD_F32", "SwitchSDError", "abi_version", "accept_longest",
-           "blocktri_verify", "calibrate", "calibrate_workspace_bytes", "commit_accepted",
+           "accept_sample", "blocktri_verify", "blocktri_verify_sample", "calibrate", "calibrate_workspace_bytes", "commit_accepted",
            "copy_labels", "copy_labels_workspace_bytes", "kgram_retrieve", "load",
            "probe_logits", "probe_score", "verify_workspace_bytes"]

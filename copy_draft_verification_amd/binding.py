@@ -36,6 +36,14 @@ _SIGS = {
     "ssd_commit_accepted": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
                                            _i32, _i32, ctypes.c_int, _c_p, _c_p, ctypes.c_int64,
                                            _c_p, _c_p, _c_p, _c_p]),
+    "ssd_blocktri_verify_sample": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p,
+                                                  _c_p, _c_p, _c_p, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, ctypes.c_int, ctypes.c_float,
+                                                  ctypes.c_float, ctypes.c_uint64, _c_p, _c_p, _c_p,
+                                                  _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t,
+                                                  _c_p, _c_p, _c_p]),
+    "ssd_accept_sample": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
+                                         ctypes.c_uint64, _c_p, _c_p, _c_p, _c_p]),
     "ssd_copy_labels_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
     "ssd_copy_labels": (ctypes.c_int, [_c_p, _c_p, _i32, ctypes.c_int64, _i32, _c_p, _c_p,
                                        ctypes.c_size_t, _c_p]),
@@ -181,6 +189,72 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)), "blocktri_verify")
     return attn_out, argmax_out
+
+
+def _events(events):
+    if events is None:
+        return None, None
+    if not events[0].cuda_event or not events[1].cuda_event:
+        raise SwitchSDError("events must be created (recorded once) before they are passed")
+    return ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event)
+
+
+def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand, cand_len,
+                           copy_gate, lm_head, W, D, scale, temperature, seed, attn_out=None,
+                           rows=None, workspace=None, events=None, stream=None):
+    """Verification pass at temperature > 0 (bf16).  Shapes as blocktri_verify; cand
+    [B, W, D] int32.  Returns (attn_out, rows) with rows a dict of n_children [B, R],
+    children / child_w [B, R, W], child_logit [B, R, W], lse [B, R], resample [B, R]."""
+    for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
+                 (v_cand, "v_cand"), (lm_head, "lm_head")):
+        _dev(t, n, (torch.bfloat16,))
+    _dev(cu_len, "cu_len", (torch.int32,))
+    _dev(cand, "cand", (torch.int32,))
+    _dev(cand_len, "cand_len", (torch.int32,))
+    _dev(copy_gate, "copy_gate", (torch.uint8,))
+    B, R, Hq, d = q.shape
+    Hkv = k_pre.shape[1]
+    V = lm_head.shape[0]
+    dev = q.device
+    if attn_out is None:
+        attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
+    if rows is None:
+        rows = {"n_children": torch.empty(B, R, dtype=torch.int32, device=dev),
+                "children": torch.empty(B, R, W, dtype=torch.int32, device=dev),
+                "child_w": torch.empty(B, R, W, dtype=torch.int32, device=dev),
+                "child_logit": torch.empty(B, R, W, dtype=torch.float32, device=dev),
+                "lse": torch.empty(B, R, dtype=torch.float32, device=dev),
+                "resample": torch.empty(B, R, dtype=torch.int32, device=dev)}
+    need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ev0, ev1 = _events(events)
+    _check(load().ssd_blocktri_verify_sample(
+        _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
+        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm_head), B, W, D, Hq, Hkv, d, V,
+        _dt(q), float(scale), float(temperature), int(seed) & ((1 << 64) - 1), _ptr(attn_out),
+        _ptr(rows["n_children"]), _ptr(rows["children"]), _ptr(rows["child_w"]),
+        _ptr(rows["child_logit"]), _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)),
+        "blocktri_verify_sample")
+    return attn_out, rows
+
+
+def accept_sample(rows, copy_gate, W, D, seed, out=None, stream=None):
+    """Acceptance walk at temperature > 0 over the rows written by
+    blocktri_verify_sample.  Returns dict best_w, best_len, next_token [B]."""
+    _dev(copy_gate, "copy_gate", (torch.uint8,))
+    B = copy_gate.numel()
+    dev = copy_gate.device
+    if out is None:
+        out = {k: torch.empty(B, dtype=torch.int32, device=dev)
+               for k in ("best_w", "best_len", "next_token")}
+    _check(load().ssd_accept_sample(
+        _ptr(rows["n_children"]), _ptr(rows["child_w"]), _ptr(rows["child_logit"]),
+        _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(copy_gate), B, W, D,
+        int(seed) & ((1 << 64) - 1), _ptr(out["best_w"]), _ptr(out["best_len"]),
+        _ptr(out["next_token"]), _stream(stream)), "accept_sample")
+    return out
 
 
 def accept_longest(cand, cand_len, copy_gate, argmax, W, D, out=None, stream=None):

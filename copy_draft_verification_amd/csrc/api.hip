@@ -127,6 +127,67 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
   return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream));
 }
 
+ssd_status_t ssd_blocktri_verify_sample(
+    const void* q, const void* k_pre, const void* v_pre, const int32_t* cu_len, int32_t max_n,
+    const void* k_cand, const void* v_cand, const int32_t* cand, const int32_t* cand_len,
+    const uint8_t* copy_gate, const void* lm_head, int32_t B, int32_t W, int32_t D, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype, float scale, float temperature,
+    uint64_t seed, void* attn_out, int32_t* n_children, int32_t* children, int32_t* child_w,
+    float* child_logit, float* lse, int32_t* resample, void* workspace, size_t workspace_bytes,
+    hipEvent_t lm_begin, hipEvent_t lm_end, hipStream_t stream) {
+  if (!q || !k_pre || !v_pre || !cu_len || !k_cand || !v_cand || !cand || !cand_len ||
+      !copy_gate || !lm_head || !attn_out || !n_children || !children || !child_w ||
+      !child_logit || !lse || !resample)
+    return SSD_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return SSD_ERR_INVALID_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SSD_ERR_INVALID_ARG;
+  const ssd_status_t st = check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype);
+  if (st != SSD_OK) return st;
+  if (dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  const float inv_t = 1.0f / temperature;
+  if (!std::isfinite(inv_t)) return SSD_ERR_INVALID_ARG;
+  const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, true);
+  if (!workspace || workspace_bytes < L.attn_bytes + L.lm_bytes) return SSD_ERR_WORKSPACE;
+  float* ws_attn = static_cast<float*>(workspace);
+  void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
+  const int R = 1 + W * D;
+  hipError_t e = ssd::launch_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
+                                       B, W, D, Hq, Hkv, d, true, scale, L.attn, attn_out, ws_attn,
+                                       stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_trie(cand, cand_len, copy_gate, B, W, D, n_children, children, child_w,
+                       child_logit, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  ssd::SampleArgs sa;
+  sa.inv_t = inv_t;
+  sa.k0 = static_cast<uint32_t>(seed & 0xffffffffu);
+  sa.k1 = static_cast<uint32_t>(seed >> 32);
+  sa.W = W;
+  sa.n_children = n_children;
+  sa.children = children;
+  sa.child_logit = child_logit;
+  e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, true, L.lm, nullptr, ws_lm, lm_begin,
+                         lm_end, stream, &sa);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  return from_hip(ssd::launch_sample_reduce(ws_lm, L.lm, B * R, lse, resample, stream));
+}
+
+ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w,
+                               const float* child_logit, const float* lse, const int32_t* resample,
+                               const uint8_t* copy_gate, int32_t B, int32_t W, int32_t D,
+                               uint64_t seed, int32_t* best_w, int32_t* best_len,
+                               int32_t* next_token, hipStream_t stream) {
+  if (!n_children || !child_w || !child_logit || !lse || !resample || !copy_gate || !best_w ||
+      !best_len || !next_token)
+    return SSD_ERR_INVALID_ARG;
+  if (B < 1 || W < 1 || W > SSD_MAX_W || D < 1 || D > SSD_MAX_D) return SSD_ERR_INVALID_ARG;
+  return from_hip(ssd::launch_accept_sample(n_children, child_w, child_logit, lse, resample,
+                                            copy_gate, B, W, D, seed, best_w, best_len, next_token,
+                                            stream));
+}
+
 ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
                                 const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
                                 int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,

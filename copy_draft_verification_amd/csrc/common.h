@@ -80,6 +80,54 @@ template <> struct Chunk8<float> {
   __device__ float at(int e) const { return e < 4 ? (&a.x)[e] : (&b.x)[e - 4]; }
 };
 
+// Philox4x32-10 block function (Salmon, Moraes, Dror and Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): counter (c0..c3), key (k0, k1) -> four
+// 32-bit words.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    // one 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32) instead of a
+    // separate high and low multiply
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    c0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    c1 = static_cast<uint32_t>(p1);
+    c2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c3 = static_cast<uint32_t>(p0);
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// 32-bit word -> (floor(w / 512) + 1/2) / 2^23, in (0, 1) and exact in binary32.
+__device__ __forceinline__ float word_uniform(uint32_t w) {
+  return fmaf(static_cast<float>(w >> 9), 0x1p-23f, 0x1p-24f);
+}
+
+// Gumbel noise -ln(-ln u) from two hardware base-2 logarithms (v_log_f32):
+// with e = -log2 u, -ln(-ln u) = -ln2 * log2(e) - ln(ln 2).  u >= 2^-24 and
+// e >= 8.5e-8 are normal floats, so the instruction needs no denormal scaling.
+// Measured on every u of the grid, -ln u from v_log_f32 is within 3.2 ulp
+// (relative) near u = 1 included, where -ln u is tiny and the noise largest; the
+// noise is within a few 1e-7 of the exact value.
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+  const float e = -__builtin_amdgcn_logf(word_uniform(w));
+  return fmaf(-0.69314718f, __builtin_amdgcn_logf(e), 0.36651292f);
+}
+
+// (max, sum of 2^(x - max)) pairs of a base-2 log-sum-exp, merged.
+__device__ __forceinline__ void lse2_merge(float& m, float& s, float om, float os) {
+  const float nm = fmaxf(m, om);
+  if (nm == -INFINITY) return;
+  s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(m - nm)) +
+      (om == -INFINITY ? 0.f : os * __builtin_amdgcn_exp2f(om - nm));
+  m = nm;
+}
+
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no
 // swizzle, offset addressing): loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;

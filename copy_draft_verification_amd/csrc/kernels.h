@@ -43,9 +43,22 @@ struct LmPlan {
 LmPlan lm_plan(int rows, int V, bool bf16);
 size_t lm_workspace_bytes(const LmPlan& p, int rows);
 
+// Sampling (T > 0) arguments of the LM head's epilogue: 1/T, the Philox key, the
+// trie's children per global row, and where the children's logits / T go.
+struct SampleArgs {
+  float inv_t;
+  uint32_t k0, k1;
+  int W;
+  const int32_t* n_children;  // [B*R]
+  const int32_t* children;    // [B*R][W]
+  float* child_logit;         // [B*R][W]
+};
+
+// sample == nullptr: greedy partials (value, index); otherwise sampling partials.
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
-                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s);
+                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
+                         const SampleArgs* sample = nullptr);
 
 // Lists the real rows (open gate; row 0 or candidate token j < L_w) in the LM-head
 // workspace; the LM head then contracts only those rows.
@@ -54,6 +67,19 @@ hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const in
 
 hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,
                                 hipStream_t s);
+
+// Verification at T > 0: the candidate trie (before the LM head), the reduction of
+// the sampling partials into lse / residual draw per row, and the acceptance walk.
+hipError_t launch_trie(const int32_t* cand, const int32_t* cand_len, const uint8_t* copy_gate,
+                       int B, int W, int D, int32_t* n_children, int32_t* children,
+                       int32_t* child_w, float* child_logit, hipStream_t s);
+hipError_t launch_sample_reduce(void* ws, const LmPlan& plan, int rows, float* lse,
+                                int32_t* resample, hipStream_t s);
+hipError_t launch_accept_sample(const int32_t* n_children, const int32_t* child_w,
+                                const float* child_logit, const float* lse,
+                                const int32_t* resample, const uint8_t* copy_gate, int B, int W,
+                                int D, unsigned long long seed, int32_t* best_w,
+                                int32_t* best_len, int32_t* next_token, hipStream_t s);
 
 hipError_t launch_commit(const void* k_cand, const void* v_cand, const int32_t* cand,
                          const int32_t* best_w, const int32_t* best_len, const int32_t* next_token,

@@ -14,6 +14,7 @@
 #include <limits.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -57,22 +58,159 @@ static_assert(kLmLoadsPerIter * 3 <= 63, "vmcnt holds the loads of three iterati
 
 template <int N> using IntC = std::integral_constant<int, N>;
 
+template <typename F, int... Ts>
+__device__ __forceinline__ void for_each_tile(F& f, std::integer_sequence<int, Ts...>) {
+  (f(IntC<Ts>{}), ...);
+}
+
 // Row r of a stage keeps its eight 16-byte k chunks in swizzled order:
 // logical chunk c sits at position c ^ ((r >> 1) & 7).  Sixteen consecutive rows
 // read at one logical chunk then cover all 64 LDS banks once.
 __device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// Sampling epilogue (T > 0).  Per row and this workgroup's vocabulary tile:
+// the base-2 log-sum-exp pair (max, sum 2^(t2 - max)) of t2 = log2(e) * logit / T
+// over every token,
+// and the best t + Gumbel noise over the tokens that are not children of the
+// row's trie node (the residual draw's candidates).  The children's t values are
+// stored for the acceptance tests.  Lane (l32, h) holds, per A tile a and
+// register r, token vbase + 32a + 8(r/4) + 4h + r%4: groups of four consecutive
+// tokens, one Philox block each.
+__device__ __forceinline__ void sample_epilogue(
+    const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows, int vbase, int V, int vt, int vtiles,
+    int wave, int tid, int l32, int h, const int32_t* __restrict__ row_list, const SampleArgs& sa,
+    float (&red_y)[kLmWaves][kLmMC], int (&red_x)[kLmWaves][kLmMC],
+    float (&red_m)[kLmWaves][kLmMC], float (&red_s)[kLmWaves][kLmMC], float4* __restrict__ part) {
+  // The rows' trie data first, for all seven row tiles at once and before any
+  // store, so that the three dependent loads (row list, child count, child
+  // tokens) cost three memory latencies rather than three per tile.
+  int growv[kLmNT], ncv[kLmNT];
+  uint32_t exclv[kLmNT];
+#pragma unroll
+  for (int t = 0; t < kLmNT; ++t) {
+    const int row = row0 + t * 32 + l32;
+    growv[t] = row < rows ? row_list[row] : -1;
+  }
+#pragma unroll
+  for (int t = 0; t < kLmNT; ++t)
+    ncv[t] = growv[t] >= 0 ? min(max(sa.n_children[growv[t]], 0), sa.W) : 0;
+  // children that fall on this lane's 32 tokens, as a bit mask over (a, r).  The
+  // first four child slots of every tile's row are loaded unconditionally (slot
+  // indices clamped into the row's W slots) so that all 28 loads are in flight
+  // together; rows with more children (the anchor's) finish in a loop.
+  auto child_bit = [&](int c) -> uint32_t {
+    const int dd = c - vbase;
+    if (dd >= 0 && dd < kLmVA * 32 && ((dd >> 2) & 1) == h) {
+      const int rem = dd & 31;
+      return 1u << ((dd >> 5) * 16 + ((rem >> 3) << 2) + (rem & 3));
+    }
+    return 0u;
+  };
+  constexpr int kFastKids = 4;
+  int cfast[kLmNT][kFastKids];
+#pragma unroll
+  for (int t = 0; t < kLmNT; ++t) {
+    const int32_t* ch = sa.children + static_cast<size_t>(growv[t] < 0 ? 0 : growv[t]) * sa.W;
+#pragma unroll
+    for (int k = 0; k < kFastKids; ++k) cfast[t][k] = ch[min(k, sa.W - 1)];
+  }
+#pragma unroll
+  for (int t = 0; t < kLmNT; ++t) {
+    uint32_t excl = 0;
+#pragma unroll
+    for (int k = 0; k < kFastKids; ++k)
+      if (k < ncv[t]) excl |= child_bit(cfast[t][k]);
+    const int32_t* ch = sa.children + static_cast<size_t>(growv[t] < 0 ? 0 : growv[t]) * sa.W;
+    for (int k = kFastKids; k < ncv[t]; ++k) excl |= child_bit(ch[k]);
+    exclv[t] = excl;
+  }
+  const float inv_t2 = sa.inv_t * kLog2e;
+  // one call per row tile with a compile-time tile index, so that the
+  // accumulators stay in registers (a loop this large is not unrolled)
+  auto tile = [&](auto Tc) {
+    constexpr int t = decltype(Tc)::value;
+    const int grow = growv[t], nc = ncv[t];
+    const uint32_t excl = exclv[t];
+    const int32_t* ch = sa.children + static_cast<size_t>(grow < 0 ? 0 : grow) * sa.W;
+    // log-sum-exp in the base-2 domain (t * log2 e), converted at the end
+    float m = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (v < V) m = fmaxf(m, acc[a][t][r] * inv_t2);
+      }
+    float s = 0.f, by = -INFINITY;
+    int bx = INT_MAX;
+#pragma unroll
+    for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int x0 = vbase + a * 32 + 8 * q + 4 * h;
+        const uint4 wd = philox4x32_10(static_cast<uint32_t>(x0 >> 2), static_cast<uint32_t>(grow), 0, 0,
+                                       sa.k0, sa.k1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q + i, x = x0 + i;
+          if (x < V) {
+            const float tv = acc[a][t][r] * sa.inv_t;
+            s += __builtin_amdgcn_exp2f(acc[a][t][r] * inv_t2 - m);
+            if ((excl >> (a * 16 + r)) & 1u) {
+              if (grow >= 0)
+                for (int k = 0; k < nc; ++k)
+                  if (ch[k] == x) sa.child_logit[static_cast<size_t>(grow) * sa.W + k] = tv;
+            } else {
+              const float y = tv + gumbel_of(i == 0 ? wd.x : i == 1 ? wd.y : i == 2 ? wd.z : wd.w);
+              if (better(y, x, by, bx)) { by = y; bx = x; }
+            }
+          }
+        }
+      }
+    {
+      const float om = __shfl_xor(m, 32, kWave), os = __shfl_xor(s, 32, kWave);
+      const float oy = __shfl_xor(by, 32, kWave);
+      const int ox = __shfl_xor(bx, 32, kWave);
+      lse2_merge(m, s, om, os);
+      if (better(oy, ox, by, bx)) { by = oy; bx = ox; }
+    }
+    if (h == 0) {
+      red_m[wave][t * 32 + l32] = m;
+      red_s[wave][t * 32 + l32] = s;
+      red_y[wave][t * 32 + l32] = by;
+      red_x[wave][t * 32 + l32] = bx;
+    }
+  };
+  for_each_tile(tile, std::make_integer_sequence<int, kLmNT>{});
+  __syncthreads();
+  for (int i = tid; i < kLmMC; i += 256) {
+    const int row = row0 + i;
+    if (row >= rows) continue;
+    float m = red_m[0][i], s = red_s[0][i], by = red_y[0][i];
+    int bx = red_x[0][i];
+#pragma unroll
+    for (int w = 1; w < kLmWaves; ++w) {
+      lse2_merge(m, s, red_m[w][i], red_s[w][i]);
+      if (better(red_y[w][i], red_x[w][i], by, bx)) { by = red_y[w][i]; bx = red_x[w][i]; }
+    }
+    part[static_cast<size_t>(row) * vtiles + vt] = make_float4(m, s, by, __int_as_float(bx));
+  }
+}
+
+template <bool kSample>
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
     const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
-    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles, int mchunks, int sv,
-    int sm) {
+    float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
+    int sm, SampleArgs sa) {
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st3[kLmStage];
   __shared__ float red_v[kLmWaves][kLmMC];
   __shared__ int red_i[kLmWaves][kLmMC];
+  __shared__ float red_m[kSample ? kLmWaves : 1][kLmMC];
+  __shared__ float red_s[kSample ? kLmWaves : 1][kLmMC];
 
   // XCD-aware tile order.  Workgroups are dealt round-robin over the XCDs (block L
   // runs on XCD L % 8).  Super-tiles of sv vocabulary tiles x sm row chunks (about
@@ -216,6 +354,13 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if constexpr (kSample) {
+    sample_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, sa,
+                    red_v, red_i, reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_m),
+                    reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_s), static_cast<float4*>(part_out));
+    return;
+  }
+  int2* const part = static_cast<int2*>(part_out);
   // epilogue: per row (this lane's column l32 of each row tile), the best
   // (value, lowest index) over this workgroup's tile
 #pragma unroll
@@ -384,6 +529,57 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(
   if (lane == 0) argmax_out[row] = bi;
 }
 
+// One wave per row: merges the row's per-tile (max, sum-exp, best score, best
+// token) over the vocabulary tiles into lse = logsumexp(logits / T) and the
+// residual draw.  The (max, sum) pairs are in base 2: max of t*log2(e) and the
+// sum of 2^(t*log2(e) - max).  Rows that are not real get lse = -inf and draw -1.
+__global__ __launch_bounds__(256) void sample_reduce_kernel(const float4* __restrict__ part,
+                                                            int vtiles, int rows,
+                                                            const int32_t* __restrict__ inv,
+                                                            float* __restrict__ lse,
+                                                            int32_t* __restrict__ resample) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= rows) return;
+  const int ci = inv[row];
+  if (ci < 0) {
+    if (lane == 0) {
+      lse[row] = -INFINITY;
+      resample[row] = -1;
+    }
+    return;
+  }
+  float m = -INFINITY, s = 0.f, by = -INFINITY;
+  int bx = INT_MAX;
+  const float4* pr = part + static_cast<size_t>(ci) * vtiles;
+  for (int t0 = 0; t0 < vtiles; t0 += 4 * kWave) {
+    float4 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kWave + lane;
+      p[u] = t < vtiles ? pr[t] : make_float4(-INFINITY, 0.f, -INFINITY, __int_as_float(INT_MAX));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lse2_merge(m, s, p[u].x, p[u].y);
+      const int x = __float_as_int(p[u].w);
+      if (better(p[u].z, x, by, bx)) { by = p[u].z; bx = x; }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
+    const float oy = __shfl_xor(by, o, kWave);
+    const int ox = __shfl_xor(bx, o, kWave);
+    lse2_merge(m, s, om, os);
+    if (better(oy, ox, by, bx)) { by = oy; bx = ox; }
+  }
+  if (lane == 0) {
+    lse[row] = (m + log2f(s)) * 0.69314718f;   // base-2 pair -> natural log-sum-exp
+    resample[row] = bx == INT_MAX ? -1 : bx;
+  }
+}
+
 LmPlan lm_plan(int rows, int V, bool bf16) {
   LmPlan p;
   p.vtiles = bf16 ? (V + kLmVT - 1) / kLmVT : (V + kLmF32VT - 1) / kLmF32VT;
@@ -397,7 +593,7 @@ LmPlan lm_plan(int rows, int V, bool bf16) {
 }
 
 // LM-head workspace: [n_rows (256 B)] [row_list: rows ints] [inv: rows ints]
-// [tile partials: rows x vtiles (value, index)], each region 256-byte aligned.
+// [tile partials: rows x vtiles x 16 B], each region 256-byte aligned.
 namespace {
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 struct LmWs {
@@ -420,8 +616,10 @@ LmWs lm_ws(void* ws, int rows) {
 }
 }  // namespace
 
+// The tile partials take 16 bytes per (row, tile): (value, index) at T = 0,
+// (max, sum-exp, best score, best token) when sampling.
 size_t lm_workspace_bytes(const LmPlan& p, int rows) {
-  return 256 + 2 * al256(sizeof(int32_t) * rows) + static_cast<size_t>(p.vtiles) * rows * sizeof(int2);
+  return 256 + 2 * al256(sizeof(int32_t) * rows) + static_cast<size_t>(p.vtiles) * rows * sizeof(float4);
 }
 
 hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
@@ -434,14 +632,20 @@ hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const in
 
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
-                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s) {
+                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
+                         const SampleArgs* sample) {
   const LmWs w = lm_ws(ws, rows);
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
-  if (bf16)
-    hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(plan.blocks), dim3(256), 0, s,
+  if (bf16 && sample)
+    hipLaunchKernelGGL(lmhead_bf16_kernel<true>, dim3(plan.blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
-                       rows, hid, V, w.row_list, w.n_rows, logits_out, w.part, plan.vtiles,
-                       plan.mchunks, plan.sv, plan.sm);
+                       rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
+                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, *sample);
+  else if (bf16)
+    hipLaunchKernelGGL(lmhead_bf16_kernel<false>, dim3(plan.blocks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
+                       rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
+                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{});
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
                        static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), hid,
@@ -456,6 +660,14 @@ hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t*
   const LmWs w = lm_ws(ws, rows);
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, w.part,
                      plan.vtiles, rows, w.inv, argmax_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_reduce(void* ws, const LmPlan& plan, int rows, float* lse,
+                                int32_t* resample, hipStream_t s) {
+  const LmWs w = lm_ws(ws, rows);
+  hipLaunchKernelGGL(sample_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(w.part), plan.vtiles, rows, w.inv, lse, resample);
   return hipGetLastError();
 }
 

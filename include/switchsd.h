@@ -13,6 +13,8 @@
  *
  * and, after accept, ssd_commit_accepted copies the accepted tokens' keys and
  * values into the caller's KV cache and lists the tokens that extend the context.
+ * At temperature T > 0, ssd_blocktri_verify_sample and ssd_accept_sample take the
+ * place of ssd_blocktri_verify and ssd_accept_longest.
  *
  * Offline, before decoding, three calls calibrate the probe (paper §3.2):
  *
@@ -55,7 +57,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -213,6 +215,71 @@ ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const i
                                  int32_t Hkv, int32_t d, ssd_dtype_t dtype, void* k_cache,
                                  void* v_cache, int64_t cache_rows, const int64_t* cache_off,
                                  int32_t* tokens_out, int32_t* n_tokens_out, hipStream_t stream);
+
+/*
+ * Verification pass at temperature T > 0 (bf16 only).  The pages give no rule
+ * for copy candidates at T > 0; they require that verification by the target
+ * keeps speculative decoding's guarantee (paper §3.3 "Overall Framework", §2
+ * "Speculative Decoding"; lossless acceptance as on the VIA-SD page "Draft-Verify
+ * and Lossy Acceptance").  Each candidate is a point-mass draft: its token is
+ * accepted with the target probability left after the tokens already rejected at
+ * the same node of the candidates' trie, and the next token is drawn from the
+ * target distribution without the rejected children (recursive rejection
+ * sampling; every emitted token then follows the target's law).
+ * Attention is as in ssd_blocktri_verify.  Then, per real row g = b*R + r (the
+ * LM head's epilogue; logits are never written):
+ *   - the trie: a node is identified by the row of its distribution (the anchor
+ *     row for the root; row (w, j-1) for the node after j tokens, w the lowest
+ *     candidate with those tokens); its children are the distinct next tokens of
+ *     its candidates, ordered by lowest candidate.
+ *   n_children [B*R] int32 (out): children of the node at row g, 0 for rows that
+ *                                 are no node
+ *   children, child_w [B*R][W] int32 (out): token and lowest candidate of child k,
+ *                                 k < n_children[g]
+ *   child_logit [B*R][W] float (out): logits[g][children[g][k]] / T; -inf for a
+ *                                 token outside [0, V)
+ *   lse [B*R] float (out): log-sum-exp over the vocabulary of logits[g] / T; -inf
+ *                          on rows that are not real
+ *   resample [B*R] int32 (out): the residual draw: argmax over the tokens x that
+ *                          are not children of row g of logits[g][x] / T + G(g, x),
+ *                          lowest x on ties; -1 on rows that are not real
+ * G(g, x) = -ln(-ln u), u = (floor(w / 512) + 1/2) / 2^23 with w word x%4 of
+ * Philox4x32-10(counter (x/4, g, 0, 0), key (seed low, seed high)).
+ *   cand [B][W][D] int32: the retrieval's candidates (ssd_kgram_retrieve)
+ *   temperature: finite, > 0, with a finite reciprocal
+ * Other arguments, workspace and events as for ssd_blocktri_verify.
+ * Errors: as ssd_blocktri_verify; INVALID_ARG for a bad temperature or a null
+ *   output; UNSUPPORTED for SSD_F32.
+ */
+ssd_status_t ssd_blocktri_verify_sample(
+    const void* q, const void* k_pre, const void* v_pre, const int32_t* cu_len, int32_t max_n,
+    const void* k_cand, const void* v_cand, const int32_t* cand, const int32_t* cand_len,
+    const uint8_t* copy_gate, const void* lm_head, int32_t B, int32_t W, int32_t D, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype, float scale, float temperature,
+    uint64_t seed, void* attn_out, int32_t* n_children, int32_t* children, int32_t* child_w,
+    float* child_logit, float* lse, int32_t* resample, void* workspace, size_t workspace_bytes,
+    hipEvent_t lm_begin, hipEvent_t lm_end, hipStream_t stream);
+
+/*
+ * Acceptance at T > 0: the walk over the trie written by
+ * ssd_blocktri_verify_sample (same seed).  From the root, child k of the node at
+ * row g is accepted when u < r, with u from word 0 of Philox4x32-10(counter
+ * (k, g, 1, 0), key (seed low, seed high)) as above and
+ * r = p / max(1 - tried, p), p = exp(child_logit - lse[g]), tried = the p of the
+ * children rejected before it (r = 0 when p = 0).  An accepted child moves the
+ * walk to row 1 + child_w*D + j; when no child is accepted the walk ends with
+ * next_token = resample[g].
+ *   best_w [B] int32: lowest candidate of the accepted path (0 when nothing is
+ *                     accepted; -1 for a closed gate)
+ *   best_len [B] int32: accepted tokens (0 for a closed gate)
+ *   next_token [B] int32: the token drawn after them (-1 for a closed gate)
+ * Errors: INVALID_ARG (nulls, B < 1, W or D outside [1, limit]).
+ */
+ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w,
+                               const float* child_logit, const float* lse, const int32_t* resample,
+                               const uint8_t* copy_gate, int32_t B, int32_t W, int32_t D,
+                               uint64_t seed, int32_t* best_w, int32_t* best_len,
+                               int32_t* next_token, hipStream_t stream);
 
 /*
  * Offline probe calibration, step 1: copy-mode labels.  Paper §3.2 "Problem

@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_accept_longest", "ssd_verify_workspace_bytes", "ssd_abi_version",
                           "ssd_status_string", "ssd_commit_accepted", "ssd_copy_labels",
                           "ssd_copy_labels_workspace_bytes", "ssd_probe_logits",
-                          "ssd_calibrate", "ssd_calibrate_workspace_bytes"}
+                          "ssd_calibrate", "ssd_calibrate_workspace_bytes",
+                          "ssd_blocktri_verify_sample", "ssd_accept_sample"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -192,3 +193,35 @@ def test_calibrate_validation(lib):
         assert call(**{k: bad}) == 1, (k, bad)
     assert call(ws=None) == 3
     assert call(wsb=ws(4, 5000) - 8) == 3
+
+
+def _sample_args(**over):
+    a = dict(q=FAKE, k_pre=FAKE, v_pre=FAKE, cu_len=FAKE, max_n=4096, k_cand=FAKE, v_cand=FAKE,
+             cand=FAKE, cand_len=FAKE, copy_gate=FAKE, lm_head=FAKE, B=1, W=10, D=20, Hq=32, Hkv=8,
+             d=128, V=128256, dtype=1, scale=0.088, temperature=1.0, seed=7, attn_out=FAKE,
+             n_children=FAKE, children=FAKE, child_w=FAKE, child_logit=FAKE, lse=FAKE,
+             resample=FAKE, ws=FAKE, ws_bytes=16, ev0=None, ev1=None, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_verify_sample_validation(lib):
+    f = lib.ssd_blocktri_verify_sample
+    for k in ("q", "cand", "n_children", "children", "child_w", "child_logit", "lse", "resample"):
+        assert f(*_sample_args(**{k: None})) == 1, k
+    for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert f(*_sample_args(temperature=t)) == 1, t           # 1e-45: 1/T overflows
+    assert f(*_sample_args(dtype=0, d=64, Hq=1, Hkv=1)) == 2      # sampling is bf16 only
+    assert f(*_sample_args(d=64)) == 2
+    assert f(*_sample_args()) == 3                                # workspace too small
+    assert f(*_sample_args(seed=(1 << 64) - 1)) == 3              # any 64-bit seed is accepted
+
+
+def test_accept_sample_validation(lib):
+    f = lib.ssd_accept_sample
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 10, 20, 7, FAKE, FAKE, FAKE, None]
+    for i, bad in ((0, None), (4, None), (5, None), (6, 0), (7, 0), (7, 65), (8, 0), (8, 65),
+                   (12, None)):
+        a = list(good)
+        a[i] = bad
+        assert f(*a) == 1, (i, bad)
