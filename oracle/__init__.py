@@ -23,6 +23,9 @@ Modules, one per step of the copy path:
 * ``calibration`` – copy-mode labels, batched probe logits, F1-optimal threshold, ROC AUC.
 * ``sampling`` – verification at T > 0: candidate trie, recursive rejection with
   point-mass drafts, Gumbel-max residual draws from Philox4x32-10.
+* ``forward`` – the verification pass as a full target forward: embedding, decoder
+  layers (RMSNorm, projections, RoPE at positions n-1 / n+j, block-triangular
+  attention, SwiGLU MLP), final norm and LM head.
 * ``bf16``    – exact widening of bfloat16 bit patterns to float64.
 
 Every function states the passage it follows.  Readings of points the pages
@@ -39,11 +42,12 @@ from .accept import accept_longest
 from .commit import commit_accepted
 from .calibration import copy_labels, probe_logits, threshold_sweep, calibrate
 from .sampling import candidate_trie, philox, sample_step, sample_verify
+from .forward import decoder_layer, verify_forward
 
 __all__ = [
     "bf16_bits_to_f64", "probe_score", "logit", "kgram_matches", "kgram_retrieve",
     "allowed_keys", "attention_row", "blocktri_attention", "lm_logits",
     "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted", "copy_labels",
     "probe_logits", "threshold_sweep", "calibrate", "candidate_trie", "philox", "sample_step",
-    "sample_verify",
+    "sample_verify", "decoder_layer", "verify_forward",
 ]

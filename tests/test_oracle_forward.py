@@ -1,0 +1,203 @@
+"""Pins of the multi-layer verification forward (oracle/forward.py).
+
+The main pin is the definition of block-triangular verification (SwitchSD paper
+§3.3 "Parallel Verification with Block-Triangular Attention"): one pass over the
+anchor and W candidates gives, for candidate token j of w, the target's output
+after the context followed by c_w[0..j], as separate ordinary passes would.  The
+reference below is an independent causal forward, one position at a time, over
+each such sequence; the prefix caches come from its pass over the context.
+Further pins: RoPE's rotation, norm and relative-position properties, RMSNorm and
+SiLU closed forms, bf16 rounding against torch, the residual structure."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import forward as F
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-6, 6, 5000),
+                        [1 + 2 ** -8, 1 + 3 * 2 ** -9, -(1 + 2 ** -8), 0.0, 65504.0, 1e-30]])
+    want = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(F.round_bf16(x), want)
+    assert F.round_bf16(np.array([1 + 2 ** -8]))[0] == 1.0          # tie to even
+    assert F.round_bf16(np.array([1 + 3 * 2 ** -9]))[0] == 1 + 2 ** -7
+
+
+def test_rope_hand_and_properties():
+    # d = 2: one pair, angle = pos
+    r = F.rope(np.array([1.0, 0.0]), 1, 500000.0)
+    assert np.allclose(r, [math.cos(1.0), math.sin(1.0)], atol=1e-15)
+    rng = np.random.default_rng(1)
+    q, k = rng.standard_normal(8), rng.standard_normal(8)
+    assert np.allclose(F.rope(q, 0, 10000.0), q)                      # position 0: identity
+    rq = F.rope(q, 37, 10000.0)
+    assert np.allclose((rq.reshape(4, 2) ** 2).sum(1), (q.reshape(4, 2) ** 2).sum(1))  # pairs keep norms
+    # scores depend on the distance only
+    a = F.rope(q, 50, 10000.0) @ F.rope(k, 20, 10000.0)
+    b = F.rope(q, 130, 10000.0) @ F.rope(k, 100, 10000.0)
+    assert abs(a - b) < 1e-12
+    # pair i turns by pos * base^(-2i/d): the last pair of d = 8 at base 10000 turns by pos / 1000
+    e = np.zeros(8)
+    e[6] = 1.0
+    assert np.allclose(F.rope(e, 5, 10000.0)[6:], [math.cos(5e-3), math.sin(5e-3)])
+
+
+def test_rmsnorm_and_silu_closed_forms():
+    g = np.array([2.0, 1.0, 0.5])
+    y = F.rmsnorm(np.full(3, 3.0), g, 1e-5)
+    assert np.allclose(y, g * 3.0 / math.sqrt(9.0 + 1e-5))
+    x = np.array([1.0, -2.0, 4.0])
+    assert np.allclose(F.rmsnorm(7.0 * x, np.ones(3), 0.0), F.rmsnorm(x, np.ones(3), 0.0))
+    assert F.silu(np.array([0.0]))[0] == 0.0
+    assert abs(F.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(F.silu(np.array([-40.0]))[0]) < 1e-15
+
+
+# ------------------------------------------------------------------ tiny target
+V, HID, HQ, HKV, DH, INTER, NL, BASE, EPS = 13, 8, 2, 1, 4, 12, 2, 10000.0, 1e-5
+
+
+def _model(seed):
+    rng = np.random.default_rng(seed)
+    s = 0.5
+    layers = []
+    for _ in range(NL):
+        layers.append({"attn_norm": 1 + 0.1 * rng.standard_normal(HID),
+                       "wq": rng.standard_normal((HQ * DH, HID)) * s,
+                       "wk": rng.standard_normal((HKV * DH, HID)) * s,
+                       "wv": rng.standard_normal((HKV * DH, HID)) * s,
+                       "wo": rng.standard_normal((HID, HQ * DH)) * s,
+                       "mlp_norm": 1 + 0.1 * rng.standard_normal(HID),
+                       "w_gate": rng.standard_normal((INTER, HID)) * s,
+                       "w_up": rng.standard_normal((INTER, HID)) * s,
+                       "w_down": rng.standard_normal((HID, INTER)) * s})
+    return {"embed": rng.standard_normal((V, HID)), "layers": layers,
+            "final_norm": 1 + 0.1 * rng.standard_normal(HID),
+            "lm_head": rng.standard_normal((V, HID))}
+
+
+def _causal(m, seq):
+    """Independent reference: an ordinary causal forward over `seq`, one position at a
+    time.  Returns (logits at every position, per-layer keys and values)."""
+    n = len(seq)
+    x = [m["embed"][t].copy() for t in seq]
+    keys, vals = [], []
+    for L in m["layers"]:
+        K = np.zeros((n, HKV, DH))
+        Vv = np.zeros((n, HKV, DH))
+        Q = np.zeros((n, HQ, DH))
+        for p in range(n):
+            xv = x[p]
+            h = xv / math.sqrt(float(np.mean(xv * xv)) + EPS) * L["attn_norm"]
+            qp = (L["wq"] @ h).reshape(HQ, DH)
+            kp = (L["wk"] @ h).reshape(HKV, DH)
+            Vv[p] = (L["wv"] @ h).reshape(HKV, DH)
+            for hh in range(HQ):
+                Q[p, hh] = _rot(qp[hh], p)
+            for hh in range(HKV):
+                K[p, hh] = _rot(kp[hh], p)
+        keys.append(K)
+        vals.append(Vv)
+        new_x = []
+        for p in range(n):
+            out = np.zeros(HQ * DH)
+            for hh in range(HQ):
+                kv = hh // (HQ // HKV)
+                sc = np.array([Q[p, hh] @ K[t, kv] for t in range(p + 1)]) / math.sqrt(DH)
+                w = np.exp(sc - sc.max())
+                w /= w.sum()
+                out[hh * DH:(hh + 1) * DH] = sum(w[t] * Vv[t, kv] for t in range(p + 1))
+            xv = x[p] + L["wo"] @ out
+            h = xv / math.sqrt(float(np.mean(xv * xv)) + EPS) * L["mlp_norm"]
+            gte, up = L["w_gate"] @ h, L["w_up"] @ h
+            new_x.append(xv + L["w_down"] @ (gte / (1 + np.exp(-gte)) * up))
+        x = new_x
+    logits = []
+    for p in range(n):
+        h = x[p] / math.sqrt(float(np.mean(x[p] * x[p])) + EPS) * m["final_norm"]
+        logits.append(m["lm_head"] @ h)
+    return np.array(logits), keys, vals
+
+
+def _rot(v, p):
+    out = v.copy()
+    for i in range(DH // 2):
+        a = p * BASE ** (-2.0 * i / DH)
+        out[2 * i] = v[2 * i] * math.cos(a) - v[2 * i + 1] * math.sin(a)
+        out[2 * i + 1] = v[2 * i] * math.sin(a) + v[2 * i + 1] * math.cos(a)
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_one_pass_equals_separate_causal_passes(seed):
+    m = _model(seed)
+    rng = np.random.default_rng(50 + seed)
+    W, D = 3, 3
+    contexts = [rng.integers(0, V, 7).tolist(), rng.integers(0, V, 5).tolist()]
+    cand = np.array([[[4, 5, 6], [4, 5, 9], [1, 0, 0]],      # shared prefix, a short one
+                     [[2, 2, 2], [7, 8, 0], [3, 0, 0]]])
+    cand_len = np.array([[3, 3, 1], [3, 2, 1]])
+    ids = np.concatenate(contexts)
+    cu = np.array([0, 7, 12])
+    layers = []
+    kv = [_causal(m, c) for c in contexts]
+    for li, L in enumerate(m["layers"]):
+        d = dict(L)
+        d["k_cache"] = np.concatenate([kv[b][1][li] for b in range(2)])
+        d["v_cache"] = np.concatenate([kv[b][2][li] for b in range(2)])
+        layers.append(d)
+    out = F.verify_forward(ids, cu, cand, cand_len, np.array([1, 1]), m["embed"], layers,
+                           m["final_norm"], m["lm_head"], HQ, HKV, DH, W, D, base=BASE, eps=EPS,
+                           storage_bf16=False)
+    got = {rc: out["logits"][i] for i, rc in enumerate(out["rows"])}
+    checked = 0
+    for b in range(2):
+        ref0, _, _ = _causal(m, contexts[b])
+        assert np.allclose(got[(b, 0)], ref0[-1], rtol=1e-9, atol=1e-9)    # the anchor row
+        for w in range(W):
+            for j in range(cand_len[b, w]):
+                seq = contexts[b] + cand[b, w, :j + 1].tolist()
+                ref, _, _ = _causal(m, seq)
+                assert np.allclose(got[(b, 1 + w * D + j)], ref[-1], rtol=1e-9, atol=1e-9), (b, w, j)
+                checked += 1
+    assert checked == 13
+
+
+def test_zero_projections_keep_the_residual():
+    # with W_o = 0 and W_down = 0 a layer is the identity on the residual stream
+    m = _model(7)
+    L = dict(m["layers"][0])
+    L["wo"] = np.zeros_like(L["wo"])
+    L["w_down"] = np.zeros_like(L["w_down"])
+    L["k_cache"] = np.zeros((4, HKV, DH))
+    L["v_cache"] = np.zeros((4, HKV, DH))
+    x = np.random.default_rng(2).standard_normal((1, 1 + 2 * 2, HID))
+    pos = F.row_positions(np.array([0, 4]), 2, 2)
+    y = F.decoder_layer(x, L, np.array([0, 4]), np.array([[2, 2]]), np.array([1]), pos, HQ, HKV,
+                        DH, 2, 2, BASE, EPS)
+    assert np.array_equal(y, x)
+
+
+def test_storage_rounding_is_bf16():
+    # the stored activations are bf16 values: the rounded pass stays within bf16 error
+    # of the exact one, and differs from it
+    m = _model(3)
+    ctx = [1, 2, 3, 4, 5, 6]
+    _, ks, vs = _causal(m, ctx)
+    layers = []
+    for li, L in enumerate(m["layers"]):
+        d = dict(L)
+        d["k_cache"], d["v_cache"] = ks[li], vs[li]
+        layers.append(d)
+    args = (np.array(ctx), np.array([0, 6]), np.array([[[7, 8]]]), np.array([[2]]), np.array([1]),
+            m["embed"], layers, m["final_norm"], m["lm_head"], HQ, HKV, DH, 1, 2)
+    a = F.verify_forward(*args, base=BASE, eps=EPS)
+    b = F.verify_forward(*args, base=BASE, eps=EPS, storage_bf16=False)
+    assert np.all(F.round_bf16(a["h"]) == a["h"])
+    rel = np.abs(a["logits"] - b["logits"]) / (np.abs(b["logits"]) + 1.0)
+    assert 0 < rel.max() < 0.1
