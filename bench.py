@@ -48,6 +48,9 @@ def parse():
                    help="> 0: verify by sampling at this temperature (blocktri_verify_sample + "
                         "accept_sample) instead of greedy")
     p.add_argument("--seed", type=int, default=0x5EED, help="sampling seed (with --temperature)")
+    p.add_argument("--forward", type=int, default=0, metavar="LAYERS",
+                   help="> 0: verify with a full target forward of this many synthetic "
+                        "Llama-3.1-8B layers (ssd_verify_forward) instead of the single-layer share")
     p.add_argument("--calibration", action="store_true",
                    help="time the offline probe calibration pass instead of the decoding step")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -301,6 +304,110 @@ def bench_calibration(a):
     print(json.dumps(line), flush=True)
 
 
+def bench_forward(a):
+    """The copy step with the verification pass as a full target forward: probe ->
+    kgram -> verify_forward (a.forward synthetic Llama-3.1-8B layers) -> accept.
+    The weights are drawn on the GPU by torch's seeded generator (14 GB at 32
+    layers would take minutes on the host); the contexts are the llama8b_b1 ones."""
+    import torch
+    import copy_draft_verification_amd as cdv
+    from workloads import generate, to_torch
+
+    wl = generate("llama8b_b1", with_tensors=False)
+    s = wl.spec
+    inter, nl = 14336, a.forward
+    dev = "cuda:0"
+    up = lambda x: to_torch(x, dev)  # noqa: E731
+    g = torch.Generator(device=dev)
+    g.manual_seed(a.seed)
+    hid, Hq, Hkv, d, V = s.hid, s.Hq, s.Hkv, s.d, s.V
+    N = int(wl.cu_len[-1])
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(torch.bfloat16)
+
+    def norm():
+        return (1.0 + 0.1 * torch.randn(hid, generator=g, device=dev)).to(torch.bfloat16)
+
+    layers = [{"attn_norm": norm(), "wqkv": randn((Hq + 2 * Hkv) * d, hid, std=hid ** -0.5),
+               "wo": randn(hid, Hq * d, std=(Hq * d) ** -0.5), "mlp_norm": norm(),
+               "w_gate": randn(inter, hid, std=hid ** -0.5), "w_up": randn(inter, hid, std=hid ** -0.5),
+               "w_down": randn(hid, inter, std=inter ** -0.5),
+               "k_cache": randn(N, Hkv, d), "v_cache": randn(N, Hkv, d)} for _ in range(nl)]
+    embed, final_norm, lm = randn(V, hid), norm(), randn(V, hid, std=hid ** -0.5)
+    ids, cu, h, w = up(wl.ids), up(wl.cu_len), up(wl.h), up(wl.w)
+    B, R = s.B, 1 + s.W * s.D
+    z = torch.empty(B, dtype=torch.float32, device=dev)
+    fire = torch.empty(B, dtype=torch.uint8, device=dev)
+    kout = {"match_end": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "n_match": torch.empty(B, dtype=torch.int32, device=dev),
+            "cand": torch.empty(B, s.W, s.D, dtype=torch.int32, device=dev),
+            "cand_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev)}
+    am = torch.empty(B, R, dtype=torch.int32, device=dev)
+    ws = torch.empty(cdv.verify_forward_workspace_bytes(B, wl.max_n, s.W, s.D, Hq, Hkv, d, inter, V),
+                     dtype=torch.uint8, device=dev)
+    aout = {"accept_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+            "best_w": torch.empty(B, dtype=torch.int32, device=dev),
+            "best_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "next_token": torch.empty(B, dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        cdv.probe_score(h, w, s.tau, z_out=z, fire_out=fire, stream=stream)
+        cdv.kgram_retrieve(ids, cu, s.kappa, s.W, s.D, fire, out=kout, stream=stream)
+        cdv.verify_forward(ids, cu, wl.max_n, kout["cand"], kout["cand_len"], kout["copy_gate"], embed,
+                           layers, final_norm, lm, s.W, s.D, Hq, Hkv, d, inter, argmax_out=am,
+                           workspace=ws, events=ev, stream=stream)
+        cdv.accept_longest(kout["cand"], kout["cand_len"], kout["copy_gate"], am, s.W, s.D, out=aout,
+                           stream=stream)
+
+    print(f"[bench] forward llama8b_b1 layers={nl} warmup={a.warmup} steps={a.steps}",
+          file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        e1.record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    f_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    gate = kout["copy_gate"].cpu().numpy().astype(bool)
+    cl = kout["cand_len"].cpu().numpy()
+    rows = int(gate.sum()) + int(cl[gate].sum())
+    per_layer = 2 * ((Hq + 2 * Hkv) * d * hid + hid * Hq * d + 3 * inter * hid) + 2 * 2 * N * Hkv * d
+    byts = nl * per_layer + 2 * V * hid + rows * hid * 2 * 2 + 4 * rows
+    achieved = byts / (f_ms * 1e-3) / 1e9
+    print(f"[bench] {ms:.3f} ms/step, forward {f_ms:.3f} ms ({achieved:.0f} GB/s of weights, caches "
+          f"and rows), real rows {rows}", file=sys.stderr, flush=True)
+    line = {
+        "metric": "copy-steps/sec with a full target forward as the verifier (Llama-3.1-8B shape)",
+        "value": round(B / (ms * 1e-3), 2),
+        "unit": "copy-steps/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_b1", "layers": nl, "hid": hid, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "inter": inter, "V": V, "W": s.W, "D": s.D, "n": int(N), "parallelism": "single-gpu"},
+        "verified_cand_tokens_per_s": round(int(cl[gate].sum()) / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "verify_forward (every kernel of the forward)", "kernel_ms": round(f_ms, 4),
+                     "algorithmic_bytes": int(byts)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -313,6 +420,9 @@ def main():
         return
     if a.calibration:
         bench_calibration(a)
+        return
+    if a.forward > 0:
+        bench_forward(a)
         return
     import torch
     import copy_draft_verification_amd as cdv

@@ -44,6 +44,11 @@ _SIGS = {
                                                   _c_p, _c_p, _c_p]),
     "ssd_accept_sample": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
                                          ctypes.c_uint64, _c_p, _c_p, _c_p, _c_p]),
+    "ssd_verify_forward_workspace_bytes": (ctypes.c_size_t, [_i32] * 9),
+    "ssd_verify_forward": (ctypes.c_int, [_c_p, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _i32,
+                                          _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, ctypes.c_float, ctypes.c_float, _c_p, _c_p, _c_p,
+                                          ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ssd_copy_labels_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
     "ssd_copy_labels": (ctypes.c_int, [_c_p, _c_p, _i32, ctypes.c_int64, _i32, _c_p, _c_p,
                                        ctypes.c_size_t, _c_p]),
@@ -375,3 +380,47 @@ def calibrate(z, labels, out=None, workspace=None, stream=None):
                                 _ptr(out["tau"]), _ptr(workspace), workspace.numel(),
                                 _stream(stream)), "calibrate")
     return out
+
+
+LAYER_FIELDS = ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "k_cache", "v_cache")
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in LAYER_FIELDS]
+
+
+def verify_forward_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, inter, V):
+    return load().ssd_verify_forward_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, inter, V)
+
+
+def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers, final_norm,
+                   lm_head, W, D, Hq, Hkv, d, inter, rope_base=500000.0, eps=1e-5,
+                   argmax_out=None, x_out=None, workspace=None, events=None, stream=None):
+    """The verification pass as a full target forward (bf16 weights).  layers: list of
+    dicts with the LAYER_FIELDS tensors.  Returns (argmax [B, R] int32, x_out or None)."""
+    for t, n in ((ids, "ids"), (cu_len, "cu_len"), (cand, "cand"), (cand_len, "cand_len")):
+        _dev(t, n, (torch.int32,))
+    _dev(copy_gate, "copy_gate", (torch.uint8,))
+    for t, n in ((embed, "embed"), (final_norm, "final_norm"), (lm_head, "lm_head")):
+        _dev(t, n, (torch.bfloat16,))
+    arr = (_Layer * max(len(layers), 1))()
+    for i, L in enumerate(layers):
+        for f in LAYER_FIELDS:
+            setattr(arr[i], f, _dev(L[f], f, (torch.bfloat16,)).data_ptr())
+    B = cu_len.numel() - 1
+    R = 1 + W * D
+    V = lm_head.shape[0]
+    dev = cand.device
+    if argmax_out is None:
+        argmax_out = torch.empty(B, R, dtype=torch.int32, device=dev)
+    need = verify_forward_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, inter, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ev0, ev1 = _events(events)
+    _check(load().ssd_verify_forward(
+        _ptr(ids), _ptr(cu_len), int(max_n), _ptr(cand), _ptr(cand_len), _ptr(copy_gate),
+        _ptr(embed), ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(final_norm),
+        _ptr(lm_head), B, W, D, Hq, Hkv, d, inter, V, float(rope_base), float(eps),
+        _ptr(argmax_out), _ptr(x_out), _ptr(workspace), workspace.numel(), ev0, ev1,
+        _stream(stream)), "verify_forward")
+    return argmax_out, x_out

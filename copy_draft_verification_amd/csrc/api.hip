@@ -188,6 +188,58 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
                                             stream));
 }
 
+namespace {
+ssd_status_t check_forward_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
+                                 int32_t Hkv, int32_t d, int32_t inter, int32_t V) {
+  if (B < 1 || max_n < 1 || W < 1 || D < 1 || Hq < 1 || Hkv < 1 || d < 1 || inter < 1 || V < 1)
+    return SSD_ERR_INVALID_ARG;
+  if (W > SSD_MAX_W || D > SSD_MAX_D || Hq % Hkv != 0) return SSD_ERR_INVALID_ARG;
+  const long long hid = static_cast<long long>(Hq) * d;
+  if (static_cast<long long>(B) * (1 + W * D) * (hid > inter ? hid : inter) > (1ll << 34))
+    return SSD_ERR_INVALID_ARG;
+  if (d != 128 || hid % 256 != 0 || inter % 256 != 0 || hid > 8192) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+}  // namespace
+
+size_t ssd_verify_forward_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D,
+                                          int32_t Hq, int32_t Hkv, int32_t d, int32_t inter,
+                                          int32_t V) {
+  if (check_forward_shape(B, max_n, W, D, Hq, Hkv, d, inter, V) != SSD_OK) return 0;
+  return ssd::fwd_layout(B, max_n, W, D, Hq, Hkv, d, inter, V).bytes;
+}
+
+ssd_status_t ssd_verify_forward(const int32_t* ids, const int32_t* cu_len, int32_t max_n,
+                                const int32_t* cand, const int32_t* cand_len,
+                                const uint8_t* copy_gate, const void* embed,
+                                const ssd_layer_t* layers, int32_t n_layers, const void* final_norm,
+                                const void* lm_head, int32_t B, int32_t W, int32_t D, int32_t Hq,
+                                int32_t Hkv, int32_t d, int32_t inter, int32_t V, float rope_base,
+                                float eps, int32_t* argmax_out, float* x_out, void* workspace,
+                                size_t workspace_bytes, hipEvent_t begin, hipEvent_t end,
+                                hipStream_t stream) {
+  if (!ids || !cu_len || !cand || !cand_len || !copy_gate || !embed || !final_norm || !lm_head ||
+      !argmax_out || n_layers < 0 || (n_layers > 0 && !layers))
+    return SSD_ERR_INVALID_ARG;
+  if (!(std::isfinite(rope_base) && rope_base > 1.f) || !(std::isfinite(eps) && eps > 0.f))
+    return SSD_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    const ssd_layer_t& L = layers[l];
+    if (!L.attn_norm || !L.wqkv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up || !L.w_down ||
+        !L.k_cache || !L.v_cache)
+      return SSD_ERR_INVALID_ARG;
+  }
+  const ssd_status_t st = check_forward_shape(B, max_n, W, D, Hq, Hkv, d, inter, V);
+  if (st != SSD_OK) return st;
+  const ssd::FwdLayout L = ssd::fwd_layout(B, max_n, W, D, Hq, Hkv, d, inter, V);
+  if (!workspace || workspace_bytes < L.bytes) return SSD_ERR_WORKSPACE;
+  static_assert(sizeof(ssd_layer_t) == sizeof(ssd::FwdLayer), "layer descriptors match");
+  return from_hip(ssd::launch_forward(ids, cu_len, cand, cand_len, copy_gate, embed,
+                                      reinterpret_cast<const ssd::FwdLayer*>(layers), n_layers,
+                                      final_norm, lm_head, B, W, D, Hq, Hkv, d, inter, V, rope_base,
+                                      eps, L, workspace, argmax_out, x_out, begin, end, stream));
+}
+
 ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
                                 const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
                                 int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,

@@ -54,6 +54,22 @@ struct SampleArgs {
   float* child_logit;         // [B*R][W]
 };
 
+// Epilogues of the bf16 LM-head / GEMM kernel.
+constexpr int kEpiArgmax = 0;   // per (row, tile) best (value, index)
+constexpr int kEpiSample = 1;   // per (row, tile) sampling partials
+constexpr int kEpiPartial = 2;  // split-K partial sums, fp32
+constexpr int kEpiSwiGLU = 3;   // silu(gate) * up, bf16
+
+struct GemmArgs {
+  int kc;                     // hidden elements per split (0: all of K)
+  float* part;                // kEpiPartial: [splits][part_rows][ld], by compact row
+  int part_rows;
+  int ld;                     // leading dimension of part / out (elements)
+  const uint16_t* w2;         // kEpiSwiGLU: the up-projection matrix (A tile 1)
+  uint16_t* out;              // kEpiSwiGLU: [global row][ld]
+  const int32_t* row_list;    // compact row -> global row
+};
+
 // sample == nullptr: greedy partials (value, index); otherwise sampling partials.
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
@@ -98,5 +114,50 @@ size_t calibrate_workspace_bytes(int L, long long N);
 hipError_t launch_calibrate(const float* z, const uint8_t* labels, int L, int N, float* thr_out,
                             int32_t* counts_out, long long* u2_out, float* auc_out,
                             int32_t* best_layer, float* tau, void* ws, hipStream_t s);
+
+// Decoder-layer GEMM on the LM-head kernel's main loop: rows (bf16, gathered
+// through the compact row list in the LM-head workspace `lm_ws_ptr`) times
+// w^T [N][K].  splits must divide K into multiples of 256.  swiglu: w is the gate
+// and w2 the up projection, out[global row][f] = silu(gate) * up (bf16);
+// otherwise part[split][compact row][n] = partial sums (fp32).
+LmPlan gemm_plan(int rows, int N, bool swiglu);
+hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int total_rows, int K,
+                       int N, const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr,
+                       float* part, uint16_t* out, int ld, hipStream_t s);
+
+// The LM-head workspace's compact row list (written by launch_compact_rows).
+struct LmWsView {
+  int32_t* n_rows;
+  int32_t* row_list;
+  int32_t* inv;
+};
+LmWsView lm_ws_view(void* ws, int rows);
+
+// Multi-layer verification forward (embedding, decoder layers, final norm, LM head).
+struct FwdLayer {
+  const void* attn_norm;  // [hid] bf16
+  const void* wqkv;       // [(Hq + 2 Hkv) d][hid] bf16: q heads, then k heads, then v heads
+  const void* wo;         // [hid][Hq d]
+  const void* mlp_norm;   // [hid]
+  const void* w_gate;     // [inter][hid]
+  const void* w_up;       // [inter][hid]
+  const void* w_down;     // [hid][inter]
+  const void* k_cache;    // [sum n][Hkv][d] prefix keys after RoPE
+  const void* v_cache;    // [sum n][Hkv][d]
+};
+struct FwdLayout {
+  AttnPlan attn;
+  LmPlan lm, p_qkv, p_o, p_gu, p_down;
+  int s_qkv, s_o, s_down;  // split-K factors
+  size_t off_lm, off_attn, off_x, off_h, off_q, off_kc, off_vc, off_att, off_a, off_part, bytes;
+};
+FwdLayout fwd_layout(int B, int max_n, int W, int D, int Hq, int Hkv, int d, int inter, int V);
+hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32_t* cand,
+                          const int32_t* cand_len, const uint8_t* copy_gate, const void* embed,
+                          const FwdLayer* layers, int n_layers, const void* final_norm,
+                          const void* lm_head, int B, int W, int D, int Hq, int Hkv, int d,
+                          int inter, int V, float rope_base, float eps, const FwdLayout& L,
+                          void* ws, int32_t* argmax_out, float* x_out, hipEvent_t ev_begin,
+                          hipEvent_t ev_end, hipStream_t s);
 
 }  // namespace ssd

@@ -51,6 +51,7 @@ constexpr int kLmKAlign = kLmKS * kLmSlots;       // the hidden size must be a m
 constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in flight
 constexpr int kLmXcds = 8;                        // XCDs; workgroups are dealt round-robin
 constexpr int kLmXcdSlots = 32;                   // concurrent workgroups per XCD (one per CU)
+constexpr int kPastEnd = -1;                      // iteration index of a load past the K range
 // loads a wave issues per iteration: row blocks, then weight fragments
 constexpr int kLmLoadsPerIter = kLmBlocksPerWave + kLmVA * 4;
 static_assert(kLmBlocks % kLmWaves == 0, "row blocks split evenly over the waves");
@@ -67,6 +68,56 @@ __device__ __forceinline__ void for_each_tile(F& f, std::integer_sequence<int, T
 // logical chunk c sits at position c ^ ((r >> 1) & 7).  Sixteen consecutive rows
 // read at one logical chunk then cover all 64 LDS banks once.
 __device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// GEMM epilogues of the decoder layers (same main loop).  Lane (l32, h) holds,
+// per A tile a and register r, output feature vbase + 32a + 8(r/4) + 4h + r%4 of
+// compact row row0 + 32t + l32 (SwiGLU: feature vbase + 8(r/4) + 4h + r%4, with
+// the gate in A tile 0 and the up projection in A tile 1).
+//  * kEpiPartial: this split's partial sums, fp32, dense by compact row:
+//    part[split][row][feature], four consecutive features per 16-byte store.
+//  * kEpiSwiGLU: silu(gate) * up, bf16, at out[global row][feature].
+template <int kEpi>
+__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows,
+                                              int vbase, int V, int h, int l32, const GemmArgs& ga) {
+#pragma unroll
+  for (int t = 0; t < kLmNT; ++t) {
+    const int row = row0 + t * 32 + l32;
+    if (row >= rows) continue;
+    if constexpr (kEpi == kEpiPartial) {
+      float* pr = ga.part + (static_cast<size_t>(blockIdx.y) * ga.part_rows + row) * ga.ld;
+#pragma unroll
+      for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = vbase + a * 32 + 8 * q + 4 * h;
+          if (v + 3 < V)
+            *reinterpret_cast<float4*>(pr + v) =
+                make_float4(acc[a][t][4 * q], acc[a][t][4 * q + 1], acc[a][t][4 * q + 2], acc[a][t][4 * q + 3]);
+          else
+            for (int i = 0; i < 4; ++i)
+              if (v + i < V) pr[v + i] = acc[a][t][4 * q + i];
+        }
+    } else {
+      uint16_t* orow = ga.out + static_cast<size_t>(ga.row_list[row]) * ga.ld;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = vbase + 8 * q + 4 * h;
+        uint16_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = acc[0][t][4 * q + i], u = acc[1][t][4 * q + i];
+          o[i] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        }
+        if (f + 3 < V)
+          *reinterpret_cast<uint2*>(orow + f) =
+              make_uint2(o[0] | static_cast<uint32_t>(o[1]) << 16, o[2] | static_cast<uint32_t>(o[3]) << 16);
+        else
+          for (int i = 0; i < 4; ++i)
+            if (f + i < V) orow[f + i] = o[i];
+      }
+    }
+  }
+}
 
 // Sampling epilogue (T > 0).  Per row and this workgroup's vocabulary tile:
 // the base-2 log-sum-exp pair (max, sum 2^(t2 - max)) of t2 = log2(e) * logit / T
@@ -197,12 +248,14 @@ __device__ __forceinline__ void sample_epilogue(
   }
 }
 
-template <bool kSample>
+template <int kEpi>
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
     const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
     float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
-    int sm, SampleArgs sa) {
+    int sm, SampleArgs sa, GemmArgs ga) {
+  constexpr bool kSample = kEpi == kEpiSample;
+  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU;
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
@@ -232,20 +285,31 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int h = lane >> 5, l32 = lane & 31;
   const int row0 = mc * kLmMC;
-  const int vbase = vt * kLmVT + wave * kLmVA * 32;
+  // the gate / up GEMM takes its two A tiles from two matrices (the same 32
+  // features of each), so a workgroup covers 128 features instead of 256
+  constexpr int kTileV = kSwiGLU ? kLmVT / kLmVA : kLmVT;
+  const int vbase = kSwiGLU ? vt * kTileV + wave * 32 : vt * kLmVT + wave * kLmVA * 32;
+  // split-K: this workgroup contracts k0 .. k0 + kc of the hidden dimension
+  const int kc = ga.kc > 0 ? ga.kc : K;
+  const int k0 = static_cast<int>(blockIdx.y) * kc;
 
   // Buffer resources: this workgroup's vocabulary tile of the weights and its row
-  // chunk of O.  Reads past either range return zero (vocabulary past V, rows past
-  // `rows`, k past the end of the last row), so the pipeline needs no guards.
-  const int v_in_tile = min(kLmVT, V - vt * kLmVT);
+  // chunk of O.  Reads whose per-lane offset is past either range return zero
+  // (vocabulary past V, rows past `rows`), so the pipeline needs no guards.
+  const int v_in_tile = min(kTileV, V - vt * kTileV);
   const int o_bytes = total_rows * K * 2;
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, v_in_tile * K * 2, kBufFlags);
-  const __amdgpu_buffer_rsrc_t ores =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
+  __amdgpu_buffer_rsrc_t wres[kLmVA];
   int aoff[kLmVA];
 #pragma unroll
-  for (int a = 0; a < kLmVA; ++a) aoff[a] = ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
+  for (int a = 0; a < kLmVA; ++a) {
+    const uint16_t* src = (kSwiGLU && a == 1) ? ga.w2 : Wt;
+    wres[a] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src + static_cast<size_t>(vt) * kTileV * K), 0, v_in_tile * K * 2, kBufFlags);
+    aoff[a] = kSwiGLU ? ((wave * 32 + l32) * K + 8 * h) * 2
+                      : ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
+  }
+  const __amdgpu_buffer_rsrc_t ores =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
   // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
   // fills stage row 8b + i/8 at swizzled position i%8 from O row
   // row_list[row0 + 8b + i/8].  Stage rows past the last real row read past the end
@@ -268,21 +332,32 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
 
   uint4 aw[kLmSlots][kLmVA][4];
+  // The loop issues loads three iterations ahead; the last three issues fall past
+  // this workgroup's K range (it == kPastEnd).  Those take a per-lane offset
+  // beyond every buffer's num_records (the range check covers the per-lane
+  // offset, not the scalar one), so they return zeros without touching memory
+  // instead of fetching the next range's data.
+  constexpr int kOutOfRange = 0x7ffffff0;
   auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
+    const bool past = it == kPastEnd;
+    const int ko = past ? 0 : (k0 + it * kLmKS) * 2;
 #pragma unroll
     for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         dst[a][s] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[a], it * kLmKS * 2 + 32 * s, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wres[a], past ? kOutOfRange : aoff[a],
+                                                          ko + 32 * s, 0));
   };
   auto load_o = [&](uint16_t* stage, int it) {
+    const bool past = it == kPastEnd;
+    const int ko = past ? 0 : (k0 + it * kLmKS) * 2;
 #pragma unroll
     for (int j = 0; j < kLmBlocksPerWave; ++j) {
       const int b = wave * kLmBlocksPerWave + j;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ores, (__attribute__((address_space(3))) void*)(stage + b * 512), 16,
-          ooff[j], it * kLmKS * 2, 0, 0);
+          past ? kOutOfRange : ooff[j], ko, 0, 0);
     }
   };
   // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
@@ -323,15 +398,15 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // wave's rows and weights of iteration it have landed (everything but the two
   // newer iterations' loads), barrier so every wave's row blocks are in LDS and
   // stage (U+3)%4 is no longer read, issue iteration it+3, compute iteration it.
-  const int nit = K / kLmKS;
+  const int nit = kc / kLmKS;
   auto step = [&](auto U_c, int it) {
     constexpr int U = decltype(U_c)::value;
     // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLmLoadsPerIter));
     lds_barrier();
-    load_o(stages[(U + 3) % kLmSlots], it + 3);
+    load_o(stages[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: rows, then weights
-    load_a(aw[(U + 3) % kLmSlots], it + 3);
+    load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
     __builtin_amdgcn_sched_barrier(0);
     compute(aw[U], stages[U]);
   };
@@ -354,6 +429,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if constexpr (kEpi == kEpiPartial || kSwiGLU) {
+    gemm_epilogue<kEpi>(acc, row0, rows, vbase, V, h, l32, ga);
+    return;
+  }
   if constexpr (kSample) {
     sample_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, sa,
                     red_v, red_i, reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_m),
@@ -580,10 +659,28 @@ __global__ __launch_bounds__(256) void sample_reduce_kernel(const float4* __rest
   }
 }
 
-LmPlan lm_plan(int rows, int V, bool bf16) {
+namespace {
+// bf16 tiling of `vtiles` vocabulary (feature) tiles over the row chunks
+LmPlan plan_for(int rows, int vtiles) {
   LmPlan p;
-  p.vtiles = bf16 ? (V + kLmVT - 1) / kLmVT : (V + kLmF32VT - 1) / kLmF32VT;
-  p.mchunks = bf16 ? (rows + kLmMC - 1) / kLmMC : (rows + kLmF32Rows - 1) / kLmF32Rows;
+  p.vtiles = vtiles;
+  p.mchunks = (rows + kLmMC - 1) / kLmMC;
+  p.sm = p.mchunks < 8 ? p.mchunks : 8;
+  p.sv = kLmXcdSlots / p.sm;
+  // narrow matrices: smaller super-tiles, so that every XCD gets some
+  const int spread = (vtiles + kLmXcds - 1) / kLmXcds;
+  if (p.sv > spread) p.sv = spread;
+  const int n_super = ((p.vtiles + p.sv - 1) / p.sv) * ((p.mchunks + p.sm - 1) / p.sm);
+  p.blocks = kLmXcds * ((n_super + kLmXcds - 1) / kLmXcds) * p.sv * p.sm;
+  return p;
+}
+}  // namespace
+
+LmPlan lm_plan(int rows, int V, bool bf16) {
+  if (bf16) return plan_for(rows, (V + kLmVT - 1) / kLmVT);
+  LmPlan p;
+  p.vtiles = (V + kLmF32VT - 1) / kLmF32VT;
+  p.mchunks = (rows + kLmF32Rows - 1) / kLmF32Rows;
   // super-tiles of one XCD's worth of workgroups (bf16 path)
   p.sm = p.mchunks < 8 ? p.mchunks : 8;
   p.sv = kLmXcdSlots / p.sm;
@@ -618,6 +715,11 @@ LmWs lm_ws(void* ws, int rows) {
 
 // The tile partials take 16 bytes per (row, tile): (value, index) at T = 0,
 // (max, sum-exp, best score, best token) when sampling.
+LmWsView lm_ws_view(void* ws, int rows) {
+  const LmWs w = lm_ws(ws, rows);
+  return LmWsView{w.n_rows, w.row_list, w.inv};
+}
+
 size_t lm_workspace_bytes(const LmPlan& p, int rows) {
   return 256 + 2 * al256(sizeof(int32_t) * rows) + static_cast<size_t>(p.vtiles) * rows * sizeof(float4);
 }
@@ -637,15 +739,15 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   const LmWs w = lm_ws(ws, rows);
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (bf16 && sample)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<true>, dim3(plan.blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiSample>, dim3(plan.blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
                        rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
-                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, *sample);
+                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, *sample, GemmArgs{});
   else if (bf16)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<false>, dim3(plan.blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiArgmax>, dim3(plan.blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
                        rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
-                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{});
+                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{}, GemmArgs{});
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
                        static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), hid,
@@ -668,6 +770,41 @@ hipError_t launch_sample_reduce(void* ws, const LmPlan& plan, int rows, float* l
   const LmWs w = lm_ws(ws, rows);
   hipLaunchKernelGGL(sample_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(w.part), plan.vtiles, rows, w.inv, lse, resample);
+  return hipGetLastError();
+}
+
+}  // namespace ssd
+
+namespace ssd {
+
+LmPlan gemm_plan(int rows, int N, bool swiglu) {
+  const int tile = swiglu ? kLmVT / kLmVA : kLmVT;
+  return plan_for(rows, (N + tile - 1) / tile);
+}
+
+hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int total_rows, int K,
+                       int N, const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr,
+                       float* part, uint16_t* out, int ld, hipStream_t s) {
+  const LmWs lw = lm_ws(const_cast<void*>(lm_ws_ptr), total_rows);
+  GemmArgs ga{};
+  ga.kc = K / splits;
+  ga.part = part;
+  ga.part_rows = total_rows;
+  ga.ld = ld;
+  ga.w2 = static_cast<const uint16_t*>(w2);
+  ga.out = out;
+  ga.row_list = lw.row_list;
+  const dim3 grid(plan.blocks, splits);
+  if (swiglu)
+    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiSwiGLU>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
+                       K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
+                       plan.sv, plan.sm, SampleArgs{}, ga);
+  else
+    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPartial>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
+                       K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
+                       plan.sv, plan.sm, SampleArgs{}, ga);
   return hipGetLastError();
 }
 

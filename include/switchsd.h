@@ -57,7 +57,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
   SSD_OK = 0,
@@ -280,6 +280,63 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
                                const uint8_t* copy_gate, int32_t B, int32_t W, int32_t D,
                                uint64_t seed, int32_t* best_w, int32_t* best_len,
                                int32_t* next_token, hipStream_t stream);
+
+/*
+ * Verification pass as a full target forward (bf16).  Paper §3.3 "Parallel
+ * Verification with Block-Triangular Attention": the anchor and all W
+ * candidates go through one target forward, candidate tokens seeing the prefix
+ * and their own earlier tokens.  The layer is the Llama-family pre-norm decoder
+ * layer of the paper's targets (§4.1):
+ *   h = RMSNorm(x) * attn_norm;  q, k, v = W_qkv h;  RoPE(q), RoPE(k);
+ *   x += W_o BlockTriAttention(q, k, v);  h = RMSNorm(x) * mlp_norm;
+ *   x += W_down (silu(W_gate h) * (W_up h));
+ * after the layers h = RMSNorm(x) * final_norm feeds the LM head and argmax.
+ * RMSNorm(x) = x / sqrt(mean(x^2) + eps).  Row tokens: the anchor (the last
+ * context token) at row 0, candidate token j of w at row 1 + w*D + j; their
+ * positions n - 1 and n + j.  RoPE turns the adjacent pair (2i, 2i+1) of every
+ * q and k head by pos * rope_base^(-2i/d).  The prefix caches hold every
+ * context token's key (after RoPE) and value, the anchor's included.  The
+ * residual stream is fp32; the activations between steps (h, q, k, v, the
+ * attention output, the MLP activation) are bf16.  Only real rows are computed.
+ * Weights, all bf16, [out][in] row-major:
+ *   embed [V][hid], lm_head [V][hid], final_norm [hid];
+ *   per layer (ssd_layer_t, an array of n_layers on the host): attn_norm,
+ *   mlp_norm [hid]; wqkv [(Hq + 2 Hkv) d][hid] (q heads, then k heads, then
+ *   v heads); wo [hid][Hq d]; w_gate, w_up [inter][hid]; w_down [hid][inter];
+ *   k_cache, v_cache [cu_len[B]][Hkv][d].
+ *   ids, cu_len, cand [B][W][D], cand_len, copy_gate: as for retrieval / verify.
+ *   argmax_out [B][R] int32: as ssd_blocktri_verify (-1 on rows that are not real)
+ *   x_out [B][R][hid] float or NULL: the final residual stream (0 on rows that
+ *         are not real)
+ *   begin, end: optional events recorded around the whole forward.
+ * hid = Hq*d.  Errors: INVALID_ARG (nulls, sizes < 1, n_layers < 0, Hq % Hkv,
+ *   limits, rope_base <= 1 or eps not finite > 0), UNSUPPORTED (d != 128,
+ *   hid % 256, inter % 256 or hid > 8192), WORKSPACE.
+ */
+typedef struct {
+  const void* attn_norm;
+  const void* wqkv;
+  const void* wo;
+  const void* mlp_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* k_cache;
+  const void* v_cache;
+} ssd_layer_t;
+
+size_t ssd_verify_forward_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D,
+                                          int32_t Hq, int32_t Hkv, int32_t d, int32_t inter,
+                                          int32_t V);
+ssd_status_t ssd_verify_forward(const int32_t* ids, const int32_t* cu_len, int32_t max_n,
+                                const int32_t* cand, const int32_t* cand_len,
+                                const uint8_t* copy_gate, const void* embed,
+                                const ssd_layer_t* layers, int32_t n_layers, const void* final_norm,
+                                const void* lm_head, int32_t B, int32_t W, int32_t D, int32_t Hq,
+                                int32_t Hkv, int32_t d, int32_t inter, int32_t V, float rope_base,
+                                float eps, int32_t* argmax_out, float* x_out, void* workspace,
+                                size_t workspace_bytes, hipEvent_t begin, hipEvent_t end,
+                                hipStream_t stream);
 
 /*
  * Offline probe calibration, step 1: copy-mode labels.  Paper §3.2 "Problem

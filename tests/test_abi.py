@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_status_string", "ssd_commit_accepted", "ssd_copy_labels",
                           "ssd_copy_labels_workspace_bytes", "ssd_probe_logits",
                           "ssd_calibrate", "ssd_calibrate_workspace_bytes",
-                          "ssd_blocktri_verify_sample", "ssd_accept_sample"}
+                          "ssd_blocktri_verify_sample", "ssd_accept_sample",
+                          "ssd_verify_forward", "ssd_verify_forward_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -225,3 +226,29 @@ def test_accept_sample_validation(lib):
         a = list(good)
         a[i] = bad
         assert f(*a) == 1, (i, bad)
+
+
+def test_verify_forward_validation(lib):
+    f = lib.ssd_verify_forward
+    ws = lib.ssd_verify_forward_workspace_bytes
+    assert ws(1, 4096, 10, 20, 32, 8, 128, 14336, 128256) > 0
+    assert ws(1, 4096, 10, 20, 32, 8, 64, 14336, 128256) == 0        # d != 128
+    assert ws(1, 4096, 10, 20, 32, 8, 128, 14335, 128256) == 0       # inter % 256
+    good = dict(ids=FAKE, cu=FAKE, max_n=4096, cand=FAKE, cl=FAKE, gate=FAKE, embed=FAKE,
+                layers=None, n_layers=0, final_norm=FAKE, lm=FAKE, B=1, W=10, D=20, Hq=32, Hkv=8,
+                d=128, inter=14336, V=128256, base=500000.0, eps=1e-5, am=FAKE, x=None, ws=FAKE,
+                wsb=16, ev0=None, ev1=None, stream=None)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return f(*a.values())
+
+    for k in ("ids", "cand", "embed", "final_norm", "lm", "am"):
+        assert call(**{k: None}) == 1, k
+    assert call(n_layers=-1) == 1
+    assert call(n_layers=2) == 1                          # layers missing
+    for k, bad in (("base", 1.0), ("base", float("nan")), ("eps", 0.0), ("Hkv", 5), ("W", 65)):
+        assert call(**{k: bad}) == 1, (k, bad)
+    assert call(d=64) == 2 and call(Hq=72) == 2           # hid = 9216 > 8192
+    assert call() == 3                                    # workspace too small

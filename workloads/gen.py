@@ -473,3 +473,61 @@ def generate_calibration(name, **overrides):
             x[sel] += u
             H[l, r0:r1] = x if s.dtype == "f32" else f32_to_bf16_bits(x)
     return CalibWorkload(s, ids, cu, copy_pos, H, w)
+
+
+# ---------------------------------------------------------------- multi-layer forward
+FWD_CONFIGS = {
+    # parity shape: the small bf16 contexts, hid 512 (4 q heads, 2 kv heads of 128), 2 layers
+    "fwd_small": ("small_bf16", {"V": 3001}, 1024, 2),
+    # Llama-3.1-8B shape (hid 4096, 32 / 8 heads, MLP 14336, vocabulary 128256), batch 1
+    "fwd_llama8b": ("llama8b_b1", {}, 14336, 2),
+}
+
+
+@dataclass
+class FwdWorkload:
+    spec: Spec
+    inter: int
+    ids: np.ndarray
+    cu_len: np.ndarray
+    embed: np.ndarray        # [V, hid] bf16 bits
+    layers: list             # dicts of bf16-bit arrays: attn_norm, wqkv, wo, mlp_norm, w_gate,
+                             # w_up, w_down, k_cache, v_cache
+    final_norm: np.ndarray
+    lm_head: np.ndarray
+
+
+def generate_forward(name, n_layers=None, **overrides):
+    """Contexts of the named copy-step workload and synthetic Llama-family weights:
+    norms 1 + N(0, 0.1^2), projections N(0, 1/fan_in), embeddings N(0, 1), prefix
+    caches N(0, 1), LM head N(0, 1/hid)."""
+    base, over, inter, L = FWD_CONFIGS[name]
+    over = dict(over)
+    over.update(overrides)
+    s = spec(base, **over)
+    L = L if n_layers is None else n_layers
+    wl = generate(s, with_tensors=False)
+    hid, Hq, Hkv, d = s.hid, s.Hq, s.Hkv, s.d
+    N = int(wl.cu_len[-1])
+    seed = s.seed + 7000
+
+    def norm_w(tag, sub):
+        return f32_to_bf16_bits(1.0 + 0.1 * _rng(seed, 40 + tag, sub).standard_normal(hid, dtype=np.float32))
+
+    layers = []
+    for l in range(L):
+        layers.append({
+            "attn_norm": norm_w(1, l),
+            "wqkv": _normal(seed, "q", ((Hq + 2 * Hkv) * d, hid), 1.0 / np.sqrt(hid), "bf16", sub=100 + l),
+            "wo": _normal(seed, "kp", (hid, Hq * d), 1.0 / np.sqrt(Hq * d), "bf16", sub=100 + l),
+            "mlp_norm": norm_w(2, l),
+            "w_gate": _normal(seed, "vp", (inter, hid), 1.0 / np.sqrt(hid), "bf16", sub=100 + l),
+            "w_up": _normal(seed, "kc", (inter, hid), 1.0 / np.sqrt(hid), "bf16", sub=100 + l),
+            "w_down": _normal(seed, "vc", (hid, inter), 1.0 / np.sqrt(inter), "bf16", sub=100 + l),
+            "k_cache": _normal(seed, "kp", (N, Hkv, d), 1.0, "bf16", sub=200 + l),
+            "v_cache": _normal(seed, "vp", (N, Hkv, d), 1.0, "bf16", sub=200 + l),
+        })
+    return FwdWorkload(s, inter, wl.ids, wl.cu_len,
+                       _normal(seed, "lm", (s.V, hid), 1.0, "bf16", sub=1),
+                       layers, norm_w(3, 0),
+                       _normal(seed, "lm", (s.V, hid), 1.0 / np.sqrt(hid), "bf16", sub=2))
