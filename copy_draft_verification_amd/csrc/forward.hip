@@ -174,6 +174,31 @@ __global__ __launch_bounds__(kFwThreads) void fwd_reduce_add_kernel(
   *reinterpret_cast<float4*>(x + static_cast<size_t>(grow) * hid + k) = acc;
 }
 
+// a[grow][f] = silu(sum of the gate partials) * (sum of the up partials), bf16.
+// Grid: (compact row, slice of 1024 features), four features per thread.
+__global__ __launch_bounds__(kFwThreads) void fwd_swiglu_finish_kernel(
+    const float* __restrict__ part, int splits, int part_rows, int inter,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
+    uint16_t* __restrict__ a) {
+  const int ci = blockIdx.x;
+  if (ci >= *n_rows) return;
+  const int f = 4 * (blockIdx.y * kFwThreads + threadIdx.x);
+  if (f >= inter) return;
+  const size_t ld = 2 * static_cast<size_t>(inter), stride = static_cast<size_t>(part_rows) * ld;
+  const float* p0 = part + static_cast<size_t>(ci) * ld + f;
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+  for (int s = 0; s < splits; ++s) {
+    const float4 pg = *reinterpret_cast<const float4*>(p0 + s * stride);
+    const float4 pu = *reinterpret_cast<const float4*>(p0 + s * stride + inter);
+    g.x += pg.x; g.y += pg.y; g.z += pg.z; g.w += pg.w;
+    u.x += pu.x; u.y += pu.y; u.z += pu.z; u.w += pu.w;
+  }
+  auto act = [](float gv, float uv) { return f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv); };
+  *reinterpret_cast<uint2*>(a + static_cast<size_t>(row_list[ci]) * inter + f) =
+      make_uint2(act(g.x, u.x) | static_cast<uint32_t>(act(g.y, u.y)) << 16,
+                 act(g.z, u.z) | static_cast<uint32_t>(act(g.w, u.w)) << 16);
+}
+
 // h[grow] = RMSNorm(x[grow]) g.  One workgroup per compact row.
 __global__ __launch_bounds__(kFwThreads) void fwd_rmsnorm_kernel(
     int hid, const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
@@ -224,9 +249,10 @@ FwdLayout fwd_layout(int B, int max_n, int W, int D, int Hq, int Hkv, int d, int
   L.s_qkv = fwd_splits(L.p_qkv, hid);
   L.s_o = fwd_splits(L.p_o, hid);
   L.s_down = fwd_splits(L.p_down, inter);
+  L.s_gu = fwd_splits(L.p_gu, hid);
   const size_t part = static_cast<size_t>(rows) *
       std::max({static_cast<size_t>(L.s_qkv) * (Hq + 2 * Hkv) * d, static_cast<size_t>(L.s_o) * hid,
-                static_cast<size_t>(L.s_down) * hid});
+                static_cast<size_t>(L.s_down) * hid, static_cast<size_t>(L.s_gu) * 2 * inter});
   size_t o = 0;
   L.off_lm = o;      o += al(lm_workspace_bytes(L.lm, rows));
   L.off_attn = o;    o += al(attn_workspace_bytes(L.attn, B, R, Hq, d));
@@ -305,9 +331,16 @@ hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32
                     s);
     if (e != hipSuccess) return e;
     residual_finish(L.s_o, static_cast<const uint16_t*>(ly.mlp_norm));
-    e = launch_gemm(hb, ly.w_gate, ly.w_up, rows, hid, inter, L.p_gu, 1, true, lmws, nullptr, ab,
-                    inter, s);
-    if (e != hipSuccess) return e;
+    if (L.s_gu > 1) {  // split-K: gate and up partials, then silu(gate) * up
+      e = launch_gemm_pair(hb, ly.w_gate, ly.w_up, rows, hid, inter, L.p_gu, L.s_gu, lmws, part, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(fwd_swiglu_finish_kernel, dim3(rows, (inter / 4 + kFwThreads - 1) / kFwThreads),
+                         dim3(kFwThreads), 0, s, part, L.s_gu, rows, inter, lv.row_list, lv.n_rows, ab);
+    } else {  // enough workgroups without splitting: silu(gate) * up in the epilogue
+      e = launch_gemm(hb, ly.w_gate, ly.w_up, rows, hid, inter, L.p_gu, 1, true, lmws, nullptr, ab,
+                      inter, s);
+      if (e != hipSuccess) return e;
+    }
     e = launch_gemm(ab, ly.w_down, nullptr, rows, inter, hid, L.p_down, L.s_down, false, lmws, part,
                     nullptr, hid, s);
     if (e != hipSuccess) return e;

@@ -59,6 +59,7 @@ constexpr int kEpiArgmax = 0;   // per (row, tile) best (value, index)
 constexpr int kEpiSample = 1;   // per (row, tile) sampling partials
 constexpr int kEpiPartial = 2;  // split-K partial sums, fp32
 constexpr int kEpiSwiGLU = 3;   // silu(gate) * up, bf16
+constexpr int kEpiPair = 4;     // two A matrices (gate, up), split-K partial sums of both
 
 struct GemmArgs {
   int kc;                     // hidden elements per split (0: all of K)
@@ -124,6 +125,11 @@ LmPlan gemm_plan(int rows, int N, bool swiglu);
 hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int total_rows, int K,
                        int N, const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr,
                        float* part, uint16_t* out, int ld, hipStream_t s);
+// The gate / up projection with split-K: part[split][compact row][f] = gate partial,
+// part[split][compact row][N + f] = up partial (ld = 2 N).
+hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate, const void* w_up,
+                            int total_rows, int K, int N, const LmPlan& plan, int splits,
+                            const void* lm_ws_ptr, float* part, hipStream_t s);
 
 // The LM-head workspace's compact row list (written by launch_compact_rows).
 struct LmWsView {
@@ -148,7 +154,7 @@ struct FwdLayer {
 struct FwdLayout {
   AttnPlan attn;
   LmPlan lm, p_qkv, p_o, p_gu, p_down;
-  int s_qkv, s_o, s_down;  // split-K factors
+  int s_qkv, s_o, s_down, s_gu;  // split-K factors
   size_t off_lm, off_attn, off_x, off_h, off_q, off_kc, off_vc, off_att, off_a, off_part, bytes;
 };
 FwdLayout fwd_layout(int B, int max_n, int W, int D, int Hq, int Hkv, int d, int inter, int V);

@@ -76,6 +76,8 @@ __device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7);
 //  * kEpiPartial: this split's partial sums, fp32, dense by compact row:
 //    part[split][row][feature], four consecutive features per 16-byte store.
 //  * kEpiSwiGLU: silu(gate) * up, bf16, at out[global row][feature].
+//  * kEpiPair: the gate and up partial sums of this split, fp32:
+//    part[split][row][feature] and part[split][row][N + feature].
 template <int kEpi>
 __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows,
                                               int vbase, int V, int h, int l32, const GemmArgs& ga) {
@@ -83,7 +85,23 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kLmVA][kLmNT],
   for (int t = 0; t < kLmNT; ++t) {
     const int row = row0 + t * 32 + l32;
     if (row >= rows) continue;
-    if constexpr (kEpi == kEpiPartial) {
+    if constexpr (kEpi == kEpiPair) {
+      // gate partials at [f], up partials at [N + f]
+      float* pr = ga.part + (static_cast<size_t>(blockIdx.y) * ga.part_rows + row) * ga.ld;
+#pragma unroll
+      for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = vbase + 8 * q + 4 * h;
+          float* dst = pr + a * V + f;
+          if (f + 3 < V)
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(acc[a][t][4 * q], acc[a][t][4 * q + 1], acc[a][t][4 * q + 2], acc[a][t][4 * q + 3]);
+          else
+            for (int i = 0; i < 4; ++i)
+              if (f + i < V) dst[i] = acc[a][t][4 * q + i];
+        }
+    } else if constexpr (kEpi == kEpiPartial) {
       float* pr = ga.part + (static_cast<size_t>(blockIdx.y) * ga.part_rows + row) * ga.ld;
 #pragma unroll
       for (int a = 0; a < kLmVA; ++a)
@@ -255,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
     int sm, SampleArgs sa, GemmArgs ga) {
   constexpr bool kSample = kEpi == kEpiSample;
-  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU;
+  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // A tiles from two matrices
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
@@ -805,6 +823,24 @@ hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int t
                        static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
                        K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
                        plan.sv, plan.sm, SampleArgs{}, ga);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate, const void* w_up,
+                            int total_rows, int K, int N, const LmPlan& plan, int splits,
+                            const void* lm_ws_ptr, float* part, hipStream_t s) {
+  const LmWs lw = lm_ws(const_cast<void*>(lm_ws_ptr), total_rows);
+  GemmArgs ga{};
+  ga.kc = K / splits;
+  ga.part = part;
+  ga.part_rows = total_rows;
+  ga.ld = 2 * N;
+  ga.w2 = static_cast<const uint16_t*>(w_up);
+  ga.row_list = lw.row_list;
+  hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPair>, dim3(plan.blocks, splits), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w_gate),
+                     total_rows, K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles,
+                     plan.mchunks, plan.sv, plan.sm, SampleArgs{}, ga);
   return hipGetLastError();
 }
 
