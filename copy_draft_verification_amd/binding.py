@@ -25,6 +25,8 @@ _SIGS = {
                                        _c_p, _c_p]),
     "ssd_kgram_retrieve": (ctypes.c_int, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p,
                                           _c_p, _c_p, _c_p, _c_p]),
+    "ssd_pack_lm_head_bytes": (ctypes.c_size_t, [_i32, _i32]),
+    "ssd_pack_lm_head": (ctypes.c_int, [_c_p, _i32, _i32, _c_p, ctypes.c_size_t, _c_p]),
     "ssd_verify_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      _i32, ctypes.c_int]),
     "ssd_blocktri_verify": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p, _c_p,
@@ -151,6 +153,45 @@ def kgram_retrieve(ids, cu_len, kappa, W, D, fire=None, out=None, stream=None):
     return out
 
 
+class PackedLmHead:
+    """A bf16 LM head [V, K] rearranged by pack_lm_head (device bytes in `data`)."""
+
+    def __init__(self, data, V, K):
+        self.data, self.V, self.K = data, int(V), int(K)
+
+
+def pack_lm_head_bytes(V, K):
+    return int(load().ssd_pack_lm_head_bytes(int(V), int(K)))
+
+
+def pack_lm_head(lm_head, out=None, stream=None):
+    """Rearrange a bf16 LM head [V, K] into the packed layout the bf16 verification
+    calls read.  Returns a PackedLmHead."""
+    _dev(lm_head, "lm_head", (torch.bfloat16,))
+    V, K = lm_head.shape
+    need = pack_lm_head_bytes(V, K)
+    if out is None:
+        out = torch.empty(max(need, 1), dtype=torch.uint8, device=lm_head.device)
+    _check(load().ssd_pack_lm_head(_ptr(lm_head), V, K, _ptr(out), out.numel() * out.element_size(),
+                                   _stream(stream)), "pack_lm_head")
+    return PackedLmHead(out, V, K)
+
+
+def _lm_arg(lm_head, dtype, K):
+    """(tensor, V) of the LM-head argument: packed for bf16, a plain [V, K] fp32 matrix
+    otherwise."""
+    if dtype == torch.bfloat16:
+        if not isinstance(lm_head, PackedLmHead):
+            raise SwitchSDError("a bf16 lm_head must be packed with pack_lm_head first")
+        if lm_head.K != K:
+            raise SwitchSDError(f"packed lm_head has K = {lm_head.K}, the rows have {K}")
+        return lm_head.data, lm_head.V
+    _dev(lm_head, "lm_head", (torch.float32,))
+    if lm_head.shape[1] != K:
+        raise SwitchSDError(f"lm_head has K = {lm_head.shape[1]}, the rows have {K}")
+    return lm_head, lm_head.shape[0]
+
+
 def verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, dtype):
     code = SSD_BF16 if dtype == torch.bfloat16 else SSD_F32
     return int(load().ssd_verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, code))
@@ -160,10 +201,11 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
                     W, D, scale, attn_out=None, argmax_out=None, logits_out=None, workspace=None,
                     events=None, stream=None):
     """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
-    [B, W*D, Hkv, d]; lm_head [V, Hq*d].  Returns (attn_out, argmax_out)."""
+    [B, W*D, Hkv, d]; lm_head [V, Hq*d] (fp32) or a PackedLmHead (bf16).  Returns
+    (attn_out, argmax_out)."""
     dts = (torch.float32, torch.bfloat16)
     for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
-                 (v_cand, "v_cand"), (lm_head, "lm_head")):
+                 (v_cand, "v_cand")):
         _dev(t, n, dts)
         if t.dtype != q.dtype:
             raise SwitchSDError(f"{n} dtype {t.dtype} differs from q dtype {q.dtype}")
@@ -172,7 +214,7 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     B, R, Hq, d = q.shape
     Hkv = k_pre.shape[1]
-    V = lm_head.shape[0]
+    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
     dev = q.device
     if attn_out is None:
         attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
@@ -190,7 +232,7 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
         ev0, ev1 = ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event)
     _check(load().ssd_blocktri_verify(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
-        _ptr(cand_len), _ptr(copy_gate), _ptr(lm_head), B, W, D, Hq, Hkv, d, V, _dt(q),
+        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q),
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)), "blocktri_verify")
     return attn_out, argmax_out
@@ -207,11 +249,12 @@ def _events(events):
 def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand, cand_len,
                            copy_gate, lm_head, W, D, scale, temperature, seed, attn_out=None,
                            rows=None, workspace=None, events=None, stream=None):
-    """Verification pass at temperature > 0 (bf16).  Shapes as blocktri_verify; cand
+    """Verification pass at temperature > 0 (bf16; lm_head a PackedLmHead).  Shapes as
+    blocktri_verify; cand
     [B, W, D] int32.  Returns (attn_out, rows) with rows a dict of n_children [B, R],
     children / child_w [B, R, W], child_logit [B, R, W], lse [B, R], resample [B, R]."""
     for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
-                 (v_cand, "v_cand"), (lm_head, "lm_head")):
+                 (v_cand, "v_cand")):
         _dev(t, n, (torch.bfloat16,))
     _dev(cu_len, "cu_len", (torch.int32,))
     _dev(cand, "cand", (torch.int32,))
@@ -219,7 +262,7 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     B, R, Hq, d = q.shape
     Hkv = k_pre.shape[1]
-    V = lm_head.shape[0]
+    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
     dev = q.device
     if attn_out is None:
         attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
@@ -236,7 +279,7 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
     ev0, ev1 = _events(events)
     _check(load().ssd_blocktri_verify_sample(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
-        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm_head), B, W, D, Hq, Hkv, d, V,
+        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V,
         _dt(q), float(scale), float(temperature), int(seed) & ((1 << 64) - 1), _ptr(attn_out),
         _ptr(rows["n_children"]), _ptr(rows["children"]), _ptr(rows["child_w"]),
         _ptr(rows["child_logit"]), _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(workspace),
@@ -396,20 +439,21 @@ def verify_forward_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, inter, V):
 def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers, final_norm,
                    lm_head, W, D, Hq, Hkv, d, inter, rope_base=500000.0, eps=1e-5,
                    argmax_out=None, x_out=None, workspace=None, events=None, stream=None):
-    """The verification pass as a full target forward (bf16 weights).  layers: list of
-    dicts with the LAYER_FIELDS tensors.  Returns (argmax [B, R] int32, x_out or None)."""
+    """The verification pass as a full target forward (bf16 weights; lm_head a
+    PackedLmHead).  layers: list of dicts with the LAYER_FIELDS tensors.  Returns
+    (argmax [B, R] int32, x_out or None)."""
     for t, n in ((ids, "ids"), (cu_len, "cu_len"), (cand, "cand"), (cand_len, "cand_len")):
         _dev(t, n, (torch.int32,))
     _dev(copy_gate, "copy_gate", (torch.uint8,))
-    for t, n in ((embed, "embed"), (final_norm, "final_norm"), (lm_head, "lm_head")):
+    for t, n in ((embed, "embed"), (final_norm, "final_norm")):
         _dev(t, n, (torch.bfloat16,))
+    lm, V = _lm_arg(lm_head, torch.bfloat16, Hq * d)
     arr = (_Layer * max(len(layers), 1))()
     for i, L in enumerate(layers):
         for f in LAYER_FIELDS:
             setattr(arr[i], f, _dev(L[f], f, (torch.bfloat16,)).data_ptr())
     B = cu_len.numel() - 1
     R = 1 + W * D
-    V = lm_head.shape[0]
     dev = cand.device
     if argmax_out is None:
         argmax_out = torch.empty(B, R, dtype=torch.int32, device=dev)
@@ -420,7 +464,7 @@ def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers,
     _check(load().ssd_verify_forward(
         _ptr(ids), _ptr(cu_len), int(max_n), _ptr(cand), _ptr(cand_len), _ptr(copy_gate),
         _ptr(embed), ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(final_norm),
-        _ptr(lm_head), B, W, D, Hq, Hkv, d, inter, V, float(rope_base), float(eps),
+        _ptr(lm), B, W, D, Hq, Hkv, d, inter, V, float(rope_base), float(eps),
         _ptr(argmax_out), _ptr(x_out), _ptr(workspace), workspace.numel(), ev0, ev1,
         _stream(stream)), "verify_forward")
     return argmax_out, x_out

@@ -14,6 +14,14 @@ bool valid_dtype(ssd_dtype_t t) { return t == SSD_F32 || t == SSD_BF16; }
 
 ssd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// The bf16 kernels address one sequence's keys (with a 64-key block of slack past
+// the last one) and the whole row matrix fed to a GEMM with 32-bit byte offsets.
+bool fits_byte_offsets(long long B, long long max_n, long long R, long long Hkv, long long d,
+                       long long widest) {
+  constexpr long long kLimit = 0x7ffffff0;  // the kernels' out-of-range offset
+  return (max_n + 64) * Hkv * d * 2 < kLimit && B * R * widest * 2 < kLimit;
+}
+
 // shape checks shared by the workspace query and the verify call
 ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
                                 int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dt) {
@@ -24,6 +32,8 @@ ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, 
   if (static_cast<long long>(B) * R * Hq * d > (1ll << 40)) return SSD_ERR_INVALID_ARG;
   if (dt == SSD_BF16) {
     if (d != 128 || (static_cast<long long>(Hq) * d) % 256 != 0) return SSD_ERR_UNSUPPORTED;
+    if (!fits_byte_offsets(B, max_n, R, Hkv, d, static_cast<long long>(Hq) * d))
+      return SSD_ERR_UNSUPPORTED;
   } else {
     if (d != 64 && d != 128) return SSD_ERR_UNSUPPORTED;
   }
@@ -85,6 +95,21 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
     return SSD_ERR_INVALID_ARG;
   return from_hip(ssd::launch_kgram(ids, cu_len, B, kappa, W, D, fire, match_end, n_match, cand,
                                     cand_len, copy_gate, stream));
+}
+
+size_t ssd_pack_lm_head_bytes(int32_t V, int32_t K) {
+  if (V < 1 || K < 1 || K % ssd::lm_k_align() != 0 || K > (1 << 20)) return 0;
+  return ssd::packed_lm_head_bytes(V, K);
+}
+
+ssd_status_t ssd_pack_lm_head(const void* lm_head, int32_t V, int32_t K, void* packed,
+                              size_t packed_bytes, hipStream_t stream) {
+  if (!lm_head || !packed || V < 1 || K < 1) return SSD_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(lm_head) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+    return SSD_ERR_INVALID_ARG;
+  if (K % ssd::lm_k_align() != 0 || K > (1 << 20)) return SSD_ERR_UNSUPPORTED;
+  if (packed_bytes < ssd::packed_lm_head_bytes(V, K)) return SSD_ERR_WORKSPACE;
+  return from_hip(ssd::launch_pack_lm_head(lm_head, V, K, packed, stream));
 }
 
 size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
@@ -198,6 +223,8 @@ ssd_status_t check_forward_shape(int32_t B, int32_t max_n, int32_t W, int32_t D,
   if (static_cast<long long>(B) * (1 + W * D) * (hid > inter ? hid : inter) > (1ll << 34))
     return SSD_ERR_INVALID_ARG;
   if (d != 128 || hid % 256 != 0 || inter % 256 != 0 || hid > 8192) return SSD_ERR_UNSUPPORTED;
+  if (!fits_byte_offsets(B, max_n, 1 + W * D, Hkv, d, hid > inter ? hid : inter))
+    return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
 }  // namespace

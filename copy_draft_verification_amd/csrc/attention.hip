@@ -79,7 +79,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     kp = k_pre + static_cast<size_t>(base) * Hkv * kAttD;
     vp = v_pre + static_cast<size_t>(base) * Hkv * kAttD;
   }
-  // keys of this sequence (or its candidates); reads past the last key return zero
+  // keys of this sequence (or its candidates).  The key index goes into the
+  // per-lane offset, so keys past the last one fall outside the buffer's range:
+  // they read as zero and never touch the memory after it.
   const int key_bytes = Hkv * kAttD * 2;
   const __amdgpu_buffer_rsrc_t kres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, nkeys * key_bytes, kBufFlags);
@@ -125,11 +127,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       kreg[c] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff, (kb + 16 * c) * key_bytes, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff + (kb + 16 * c) * key_bytes, 0, 0));
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       vreg[k] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff, (kb + k) * key_bytes, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff + (kb + k) * key_bytes, 0, 0));
   };
   auto store_block = [&]() {
 #pragma unroll

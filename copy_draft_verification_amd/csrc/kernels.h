@@ -42,6 +42,10 @@ struct LmPlan {
 };
 LmPlan lm_plan(int rows, int V, bool bf16);
 size_t lm_workspace_bytes(const LmPlan& p, int rows);
+// packed bf16 LM-head layout (bytes for V rows of K), its K alignment, and the packing
+size_t packed_lm_head_bytes(int V, int K);
+int lm_k_align();
+hipError_t launch_pack_lm_head(const void* w, int V, int K, void* packed, hipStream_t s);
 
 // Sampling (T > 0) arguments of the LM head's epilogue: 1/T, the Philox key, the
 // trie's children per global row, and where the children's logits / T go.

@@ -52,6 +52,12 @@ constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in
 constexpr int kLmXcds = 8;                        // XCDs; workgroups are dealt round-robin
 constexpr int kLmXcdSlots = 32;                   // concurrent workgroups per XCD (one per CU)
 constexpr int kPastEnd = -1;                      // iteration index of a load past the K range
+// Packed weight layout of the LM head (ssd_pack_lm_head): per (vocabulary tile,
+// k-slab), a 32 KB block; in it, per wave, the 8 KB of A fragments the wave loads
+// for that slab, one 1 KB run per (tile a, k-step s), lane-major.  A wave's
+// weight loads then stream one contiguous 8 KB run per iteration.
+constexpr int kPkWaveBytes = kLmVA * 4 * kWave * 16;       // 8 KB
+constexpr int kPkSlabBytes = kLmWaves * kPkWaveBytes;      // 32 KB
 // loads a wave issues per iteration: row blocks, then weight fragments
 constexpr int kLmLoadsPerIter = kLmBlocksPerWave + kLmVA * 4;
 static_assert(kLmBlocks % kLmWaves == 0, "row blocks split evenly over the waves");
@@ -274,6 +280,9 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     int sm, SampleArgs sa, GemmArgs ga) {
   constexpr bool kSample = kEpi == kEpiSample;
   constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // A tiles from two matrices
+  // the LM head (argmax and sampling epilogues) reads the packed weight layout,
+  // the projections of the forward the plain [N][K] one
+  constexpr bool kPacked = kEpi == kEpiArgmax || kEpi == kEpiSample;
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
@@ -320,11 +329,18 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   int aoff[kLmVA];
 #pragma unroll
   for (int a = 0; a < kLmVA; ++a) {
-    const uint16_t* src = (kSwiGLU && a == 1) ? ga.w2 : Wt;
-    wres[a] = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src + static_cast<size_t>(vt) * kTileV * K), 0, v_in_tile * K * 2, kBufFlags);
-    aoff[a] = kSwiGLU ? ((wave * 32 + l32) * K + 8 * h) * 2
-                      : ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
+    if constexpr (kPacked) {
+      // this tile's blocks: K / 64 slabs of 32 KB, zero-padded past V
+      wres[a] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
+      aoff[a] = wave * kPkWaveBytes + a * 4 * kWave * 16 + lane * 16;
+    } else {
+      const uint16_t* src = (kSwiGLU && a == 1) ? ga.w2 : Wt;
+      wres[a] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(src + static_cast<size_t>(vt) * kTileV * K), 0, v_in_tile * K * 2, kBufFlags);
+      aoff[a] = kSwiGLU ? ((wave * 32 + l32) * K + 8 * h) * 2
+                        : ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
+    }
   }
   const __amdgpu_buffer_rsrc_t ores =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
@@ -350,26 +366,48 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
 
   uint4 aw[kLmSlots][kLmVA][4];
-  // The loop issues loads three iterations ahead; the last three issues fall past
-  // this workgroup's K range (it == kPastEnd).  Those take a per-lane offset
-  // beyond every buffer's num_records (the range check covers the per-lane
-  // offset, not the scalar one), so they return zeros without touching memory
-  // instead of fetching the next range's data.
+  // The loop issues loads ahead of their use; the issues that fall past this
+  // workgroup's K range (it == kPastEnd) take a per-lane offset beyond every
+  // buffer's num_records, so they return zeros without touching memory instead
+  // of fetching the next range's data.
   constexpr int kOutOfRange = 0x7ffffff0;
+  // Iteration it contracts k-slab (it + rot) mod nit: the workgroups resident
+  // together start at different slabs of their tiles, so their streams do not all
+  // hit the same column range of the weight rows (and the same HBM channels) at
+  // once.
+  const int nit = kc / kLmKS;
+  const int rot = vt % nit;
+  auto kbyte = [&](int it) {
+    const int r = it + rot;
+    return (k0 + (r >= nit ? r - nit : r) * kLmKS) * 2;
+  };
   auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
     const bool past = it == kPastEnd;
-    const int ko = past ? 0 : (k0 + it * kLmKS) * 2;
+    if constexpr (kPacked) {
+      // slab block of iteration it; run (a, s) of this wave, 16 B per lane
+      const int r = it + rot;
+      const int so = past ? 0 : (k0 / kLmKS + (r >= nit ? r - nit : r)) * kPkSlabBytes;
 #pragma unroll
-    for (int a = 0; a < kLmVA; ++a)
+      for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dst[a][s] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(wres[a], past ? kOutOfRange : aoff[a],
-                                                          ko + 32 * s, 0));
+        for (int s = 0; s < 4; ++s)
+          dst[a][s] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                         wres[a], past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
+    } else {
+      const int ko = past ? 0 : kbyte(it);
+#pragma unroll
+      for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          dst[a][s] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(wres[a], past ? kOutOfRange : aoff[a],
+                                                            ko + 32 * s, 0));
+    }
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
-    const int ko = past ? 0 : (k0 + it * kLmKS) * 2;
+    const int ko = past ? 0 : kbyte(it);
 #pragma unroll
     for (int j = 0; j < kLmBlocksPerWave; ++j) {
       const int b = wave * kLmBlocksPerWave + j;
@@ -416,7 +454,6 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // wave's rows and weights of iteration it have landed (everything but the two
   // newer iterations' loads), barrier so every wave's row blocks are in LDS and
   // stage (U+3)%4 is no longer read, issue iteration it+3, compute iteration it.
-  const int nit = kc / kLmKS;
   auto step = [&](auto U_c, int it) {
     constexpr int U = decltype(U_c)::value;
     // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
@@ -563,6 +600,33 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
 // Real rows (open gate, row 0 or j < L_w) in row order: row_list[i] = row of the
 // i-th real row, inv[row] = i or -1, n_rows = count.  One workgroup scans all rows.
 constexpr int kCompactThreads = 1024;
+// ----------------------------------------------------------------- weight packing
+// One thread per 16-byte chunk of the packed layout.  Chunk c, decomposed as
+// (tile vt, slab, wave, run a*4 + s, lane = 32h + l32), holds weight row
+// vt*256 + wave*64 + a*32 + l32 at k = slab*64 + 16s + 8h .. +7: the A fragment
+// lane (l32, h) of that wave loads for tile a, k-step s.  Rows past V are zero.
+__global__ __launch_bounds__(256) void pack_lm_head_kernel(const uint16_t* __restrict__ w, int V,
+                                                           int K, uint16_t* __restrict__ packed,
+                                                           size_t n_chunks) {
+  const int nslab = K / kLmKS;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t c = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
+    const int lane = static_cast<int>(c % kWave);
+    size_t t = c / kWave;
+    const int run = static_cast<int>(t % (kLmVA * 4));
+    t /= kLmVA * 4;
+    const int wave = static_cast<int>(t % kLmWaves);
+    t /= kLmWaves;
+    const int slab = static_cast<int>(t % nslab);
+    const size_t vt = t / nslab;
+    const size_t row = vt * kLmVT + wave * kLmVA * 32 + (run / 4) * 32 + (lane & 31);
+    const int k = slab * kLmKS + (run % 4) * 16 + (lane >> 5) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < static_cast<size_t>(V)) v = *reinterpret_cast<const uint4*>(w + row * K + k);
+    *reinterpret_cast<uint4*>(packed + c * 8) = v;
+  }
+}
+
 __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(
     int rows, int R, int W, int D, const int32_t* __restrict__ cand_len,
     const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
@@ -773,6 +837,21 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   return e;
+}
+
+size_t packed_lm_head_bytes(int V, int K) {
+  return static_cast<size_t>((V + kLmVT - 1) / kLmVT) * kLmVT * K * 2;
+}
+
+int lm_k_align() { return kLmKAlign; }
+
+hipError_t launch_pack_lm_head(const void* w, int V, int K, void* packed, hipStream_t s) {
+  const size_t n_chunks = packed_lm_head_bytes(V, K) / 16;
+  const size_t want = (n_chunks + 255) / 256;
+  const int blocks = static_cast<int>(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(pack_lm_head_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w), V, K, static_cast<uint16_t*>(packed), n_chunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,

@@ -14,7 +14,9 @@
  * and, after accept, ssd_commit_accepted copies the accepted tokens' keys and
  * values into the caller's KV cache and lists the tokens that extend the context.
  * At temperature T > 0, ssd_blocktri_verify_sample and ssd_accept_sample take the
- * place of ssd_blocktri_verify and ssd_accept_longest.
+ * place of ssd_blocktri_verify and ssd_accept_longest.  Once, when the model is
+ * loaded, ssd_pack_lm_head rearranges a bf16 LM head into the layout that the
+ * bf16 verification calls read.
  *
  * Offline, before decoding, three calls calibrate the probe (paper §3.2):
  *
@@ -57,7 +59,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum {
   SSD_OK = 0,
@@ -122,6 +124,26 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
                                 int32_t* match_end, int32_t* n_match, int32_t* cand,
                                 int32_t* cand_len, uint8_t* copy_gate, hipStream_t stream);
 
+/*
+ * Packed bf16 LM head.  The projection of the verification pass (paper §3.3: all
+ * candidates are checked in one target pass, ending in the LM head) streams the
+ * whole V x K matrix once per pass; the bf16 kernels read it in a layout where
+ * every wave's weight fragments for one 64-wide k-slab form one contiguous 8 KB
+ * run.  Rearranging is a pure permutation (plus zero rows up to a multiple of
+ * 256), done once per model:
+ *   lm_head [V][K] bf16, row-major, 16-byte aligned (row v = weights of token v)
+ *   packed  ssd_pack_lm_head_bytes(V, K) bytes, 16-byte aligned, caller-owned;
+ *           16-byte chunk c = (((t * K/64 + s) * 4 + w) * 8 + 4a + j) * 64 + 32h + l
+ *           holds row 256t + 64w + 32a + l, columns 64s + 16j + 8h .. +7
+ *           (zeros for rows >= V)
+ * ssd_pack_lm_head_bytes returns 0 for V < 1, K < 1, K % 256 != 0 or K > 2^20.
+ * Errors: INVALID_ARG (nulls, V or K < 1, misaligned pointers), UNSUPPORTED
+ *   (K % 256 != 0 or K > 2^20), WORKSPACE (packed_bytes too small).
+ */
+size_t ssd_pack_lm_head_bytes(int32_t V, int32_t K);
+ssd_status_t ssd_pack_lm_head(const void* lm_head, int32_t V, int32_t K, void* packed,
+                              size_t packed_bytes, hipStream_t stream);
+
 /* Bytes of scratch that ssd_blocktri_verify needs for these sizes (0 on bad sizes). */
 size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
                                   int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype);
@@ -142,20 +164,22 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  *   attn_out [B][R][Hq*d]           head-major concatenation; rows that are not
  *                                   real (gate closed, w >= M, j >= L_w) are zeros
  * LM head + argmax:
- *   lm_head  [V][Hq*d]              transposed projection (row v = weights of token v)
+ *   lm_head  fp32: [V][Hq*d]        transposed projection (row v = weights of token v)
+ *            bf16: that matrix as written by ssd_pack_lm_head
  *   argmax_out [B][R] int32         lowest index among equal maxima; -1 on rows
  *                                   that are not real
  *   logits_out [B][R][V] float or NULL (debug output; written for every row)
  * dtype: SSD_F32 (all float) or SSD_BF16 (all bf16, fp32 accumulation).
- * max_n is a host-side upper bound on the context lengths used to size the
- * launch; results do not depend on it.
+ * max_n: host-side upper bound on the context lengths (every cu_len[b+1] -
+ * cu_len[b] <= max_n), used to size the launch; results do not depend on it.
  * workspace: device scratch of at least ssd_verify_workspace_bytes(...) bytes;
  *   its contents on entry do not matter.
  * lm_begin, lm_end: optional events (may be NULL) recorded on `stream`
  *   immediately before and after the LM-head contraction kernel, for timing.
  * Errors: INVALID_ARG (nulls, sizes < 1, Hq % Hkv != 0, scale not finite > 0,
- *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 256 != 0;
- *   fp32 with d not in {64, 128}), WORKSPACE.
+ *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 256 != 0, or
+ *   beyond the bf16 kernels' 32-bit byte offsets: (max_n + 64)*Hkv*d*2 or
+ *   B*R*Hq*d*2 not below 0x7ffffff0; fp32 with d not in {64, 128}), WORKSPACE.
  */
 ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
                                  const int32_t* cu_len, int32_t max_n, const void* k_cand,
@@ -298,8 +322,9 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
  * context token's key (after RoPE) and value, the anchor's included.  The
  * residual stream is fp32; the activations between steps (h, q, k, v, the
  * attention output, the MLP activation) are bf16.  Only real rows are computed.
- * Weights, all bf16, [out][in] row-major:
- *   embed [V][hid], lm_head [V][hid], final_norm [hid];
+ * Weights, all bf16, [out][in] row-major (the LM head packed):
+ *   embed [V][hid], final_norm [hid], lm_head [V][hid] as written by
+ *   ssd_pack_lm_head;
  *   per layer (ssd_layer_t, an array of n_layers on the host): attn_norm,
  *   mlp_norm [hid]; wqkv [(Hq + 2 Hkv) d][hid] (q heads, then k heads, then
  *   v heads); wo [hid][Hq d]; w_gate, w_up [inter][hid]; w_down [hid][inter];
@@ -311,7 +336,8 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
  *   begin, end: optional events recorded around the whole forward.
  * hid = Hq*d.  Errors: INVALID_ARG (nulls, sizes < 1, n_layers < 0, Hq % Hkv,
  *   limits, rope_base <= 1 or eps not finite > 0), UNSUPPORTED (d != 128,
- *   hid % 256, inter % 256 or hid > 8192), WORKSPACE.
+ *   hid % 256, inter % 256, hid > 8192, or (max_n + 64)*Hkv*d*2 or
+ *   B*R*max(hid, inter)*2 not below 0x7ffffff0), WORKSPACE.
  */
 typedef struct {
   const void* attn_norm;

@@ -51,7 +51,10 @@ class Dev:
         self.h, self.w = up(wl.h), up(wl.w)
         if tensors:
             self.q, self.kp, self.vp = up(wl.q), up(wl.k_pre), up(wl.v_pre)
-            self.kc, self.vc, self.lm = up(wl.k_cand), up(wl.v_cand), up(wl.lm_head)
+            self.kc, self.vc = up(wl.k_cand), up(wl.v_cand)
+            # the bf16 calls read the LM head packed (once, as at model load)
+            lm = up(wl.lm_head)
+            self.lm = cdv.pack_lm_head(lm) if lm.dtype == torch.bfloat16 else lm
 
 
 def check_probe(wl, d):

@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_copy_labels_workspace_bytes", "ssd_probe_logits",
                           "ssd_calibrate", "ssd_calibrate_workspace_bytes",
                           "ssd_blocktri_verify_sample", "ssd_accept_sample",
-                          "ssd_verify_forward", "ssd_verify_forward_workspace_bytes"}
+                          "ssd_verify_forward", "ssd_verify_forward_workspace_bytes",
+                          "ssd_pack_lm_head", "ssd_pack_lm_head_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -59,9 +60,38 @@ def test_workspace_query(lib):
     assert f(1, 512, 10, 20, 1, 1, 64, 1000, 0) > 0                # fp32, d = 64
     small = f(1, 512, 10, 20, 1, 1, 64, 1000, 0)
     assert f(8, 512, 10, 20, 1, 1, 64, 1000, 0) > small
+    # bf16 byte offsets are 32-bit: (max_n + 64) * Hkv * d * 2 and B * R * Hq * d * 2
+    # must stay below 0x7ffffff0
+    assert f(1, 1048511, 10, 20, 32, 8, 128, 1000, 1) > 0           # (n + 64) * 2 KiB
+    assert f(1, 1048512, 10, 20, 32, 8, 128, 1000, 1) == 0
+    assert f(1304, 4096, 10, 20, 32, 8, 128, 1000, 1) > 0           # 1304 * 201 * 8 KiB
+    assert f(1305, 4096, 10, 20, 32, 8, 128, 1000, 1) == 0
+    assert f(1305, 4096, 10, 20, 32, 8, 64, 1000, 0) > 0            # fp32 path: no limit
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def test_pack_lm_head_validation(lib):
+    nb = lib.ssd_pack_lm_head_bytes
+    assert nb(128256, 4096) == 128256 * 4096 * 2                 # 501 full tiles of 256 rows
+    assert nb(1000, 512) == 1024 * 512 * 2                       # last tile zero-padded
+    assert nb(0, 4096) == 0 and nb(10, 0) == 0
+    assert nb(10, 4095) == 0 and nb(10, 4160) == 0               # K % 256
+    assert nb(10, (1 << 20) + 256) == 0
+    f = lib.ssd_pack_lm_head
+    good = [FAKE, 1000, 512, FAKE, 1024 * 512 * 2, None]
+    for i, bad in ((0, None), (3, None), (1, 0), (2, 0), (0, ctypes.c_void_p(0x1008)),
+                   (3, ctypes.c_void_p(0x1004))):
+        a = list(good)
+        a[i] = bad
+        assert f(*a) == 1, (i, bad)
+    a = list(good)
+    a[2] = 320
+    assert f(*a) == 2                                            # K % 256
+    a = list(good)
+    a[4] = 1024 * 512 * 2 - 16
+    assert f(*a) == 3                                            # packed buffer too small
 
 
 def test_probe_validation(lib):
@@ -234,6 +264,8 @@ def test_verify_forward_validation(lib):
     assert ws(1, 4096, 10, 20, 32, 8, 128, 14336, 128256) > 0
     assert ws(1, 4096, 10, 20, 32, 8, 64, 14336, 128256) == 0        # d != 128
     assert ws(1, 4096, 10, 20, 32, 8, 128, 14335, 128256) == 0       # inter % 256
+    assert ws(372, 4096, 10, 20, 32, 8, 128, 14336, 128256) > 0      # 372 * 201 * 28 KiB
+    assert ws(373, 4096, 10, 20, 32, 8, 128, 14336, 128256) == 0
     good = dict(ids=FAKE, cu=FAKE, max_n=4096, cand=FAKE, cl=FAKE, gate=FAKE, embed=FAKE,
                 layers=None, n_layers=0, final_norm=FAKE, lm=FAKE, B=1, W=10, D=20, Hq=32, Hkv=8,
                 d=128, inter=14336, V=128256, base=500000.0, eps=1e-5, am=FAKE, x=None, ws=FAKE,

@@ -70,7 +70,7 @@ def _run(fw, n_layers, kg):
     am, _ = cdv.verify_forward(up(fw.ids), up(fw.cu_len), int(np.diff(fw.cu_len).max()),
                                up(kg["cand"].astype(np.int32)), up(kg["cand_len"].astype(np.int32)),
                                up(kg["copy_gate"].astype(np.uint8)), up(fw.embed), layers,
-                               up(fw.final_norm), up(fw.lm_head), s.W, s.D, s.Hq, s.Hkv, s.d,
+                               up(fw.final_norm), cdv.pack_lm_head(up(fw.lm_head)), s.W, s.D, s.Hq, s.Hkv, s.d,
                                fw.inter, x_out=x)
     torch.cuda.synchronize()
     return host(am), host(x)

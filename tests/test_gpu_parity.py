@@ -111,6 +111,72 @@ def test_all_gates_closed():
     check_accept(wl, g, am)
 
 
+def _pack_host(w, K):
+    """The packed LM-head layout from its definition: 16-byte chunk
+    c = (((t*K/64 + s)*4 + wv)*8 + 4a + j)*64 + 32h + l holds row 256t + 64wv + 32a + l,
+    columns 64s + 16j + 8h .. +7; rows past V are zero."""
+    V = w.shape[0]
+    T = -(-V // 256)
+    wp = np.zeros((T * 256, K), dtype=np.uint16)
+    wp[:V] = w
+    x = wp.reshape(T, 4, 2, 32, K // 64, 4, 2, 8)        # t, wv, a, l | s, j, h, e
+    return x.transpose(0, 4, 1, 2, 5, 6, 3, 7).reshape(-1)
+
+
+@pytest.mark.parametrize("V,K", [(1000, 512), (256, 1024), (513, 256)])
+def test_pack_lm_head_layout_bitwise(V, K):
+    print(f"[case] pack_lm_head V={V} K={K}", flush=True)
+    rng = np.random.default_rng(V + K)
+    bits = rng.integers(0, 1 << 16, (V, K), dtype=np.uint16)
+    w = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    packed = cdv.pack_lm_head(w)
+    torch.cuda.synchronize()
+    got = packed.data.cpu().numpy().view(np.uint16)
+    assert got.size == -(-V // 256) * 256 * K
+    assert np.array_equal(got, _pack_host(bits, K))
+
+
+def test_unpacked_bf16_lm_head_is_refused():
+    wl = generate("small_bf16")
+    d = Dev(wl)
+    g = cdv.kgram_retrieve(d.ids, d.cu, wl.spec.kappa, wl.spec.W, wl.spec.D)
+    with pytest.raises(cdv.SwitchSDError, match="packed"):
+        cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                            g["copy_gate"], up(wl.lm_head), wl.spec.W, wl.spec.D, wl.scale)
+
+
+def _nan_tail(t, extra_rows):
+    """t [rows, ...] copied into the head of a longer buffer whose tail is NaN; returns
+    the view of the head (same shape, same values, NaN right after its end)."""
+    big = torch.full((t.shape[0] + extra_rows, *t.shape[1:]), float("nan"), dtype=t.dtype,
+                     device=t.device)
+    big[: t.shape[0]] = t
+    return big[: t.shape[0]]
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_f32"])
+def test_keys_past_the_end_are_never_read(name):
+    # The last sequence's context and the last candidate block end inside a 64-key
+    # block (n and W*D = 200 are not multiples of 64).  NaN right after the caches
+    # and the candidate keys would reach the output through 0 * NaN if the kernel
+    # read past the last key instead of taking zeros.
+    wl = generate(name, lm_std=1.0)
+    n_last = int(wl.cu_len[-1] - wl.cu_len[-2])
+    print(f"[case] {name} NaN past the caches, n_last={n_last}", flush=True)
+    assert n_last % 64 != 0 and (wl.spec.W * wl.spec.D) % 64 != 0
+    d = Dev(wl)
+    d.kp, d.vp = _nan_tail(d.kp, 128), _nan_tail(d.vp, 128)
+    B, WD = wl.spec.B, wl.spec.W * wl.spec.D
+    d.kc = _nan_tail(d.kc.reshape(B * WD, *d.kc.shape[2:]), 128).reshape(d.kc.shape)
+    d.vc = _nan_tail(d.vc.reshape(B * WD, *d.vc.shape[2:]), 128).reshape(d.vc.shape)
+    fire = torch.ones(B, dtype=torch.uint8, device=DEV)
+    g, ko = check_kgram(wl, d, fire, np.ones(B, dtype=bool))
+    assert bool(ko["copy_gate"][-1])
+    attn, am, st = check_verify(wl, d, g)
+    assert torch.isfinite(attn.float()).all()
+    assert st["att_rows"] > 0
+
+
 @pytest.mark.parametrize("W,D,kappa", [(3, 7, 2), (1, 1, 1), (64, 64, 5), (10, 20, 64)])
 def test_kgram_accept_other_limits(W, D, kappa):
     rng = np.random.default_rng(W * 100 + D)
