@@ -250,6 +250,7 @@ ssd_status_t ssd_verify_forward(const int32_t* ids, const int32_t* cu_len, int32
     return SSD_ERR_INVALID_ARG;
   if (!(std::isfinite(rope_base) && rope_base > 1.f) || !(std::isfinite(eps) && eps > 0.f))
     return SSD_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x_out) % 16 != 0) return SSD_ERR_INVALID_ARG;  // float4 rows
   for (int l = 0; l < n_layers; ++l) {
     const ssd_layer_t& L = layers[l];
     if (!L.attn_norm || !L.wqkv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up || !L.w_down ||
@@ -259,7 +260,8 @@ ssd_status_t ssd_verify_forward(const int32_t* ids, const int32_t* cu_len, int32
   const ssd_status_t st = check_forward_shape(B, max_n, W, D, Hq, Hkv, d, inter, V);
   if (st != SSD_OK) return st;
   const ssd::FwdLayout L = ssd::fwd_layout(B, max_n, W, D, Hq, Hkv, d, inter, V);
-  if (!workspace || workspace_bytes < L.bytes) return SSD_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < L.bytes || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return SSD_ERR_WORKSPACE;
   static_assert(sizeof(ssd_layer_t) == sizeof(ssd::FwdLayer), "layer descriptors match");
   return from_hip(ssd::launch_forward(ids, cu_len, cand, cand_len, copy_gate, embed,
                                       reinterpret_cast<const ssd::FwdLayer*>(layers), n_layers,

@@ -25,6 +25,7 @@ constexpr int kKStride = kAttD + 8; // bf16 per K row in LDS (272 B: conflict-fr
 constexpr int kAttRowsPerBlock = 128;
 constexpr int kXcds = 8;            // workgroups are dealt round-robin over the 8 XCDs
 constexpr float kLazyRescale = 8.f; // the running max moves only when exceeded by 2^8
+constexpr int kAttAhead = 4;        // LDS fragment reads in flight ahead of their MFMA
 
 // V^T in LDS: row d holds the block's 64 keys (128 B, no padding) as sixteen 8-byte
 // units of 4 keys; unit u sits at position u ^ vt_swz(d).  With this swizzle both the
@@ -161,16 +162,32 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     lds_barrier();  // this block is in LDS
     if (kb + kKB < k1) load_block(kb + kKB);  // overlaps the MFMAs below
 
-    // S^T[key][row] for two 32-key subtiles
+    // S^T[key][row] for two 32-key subtiles.  The two accumulation chains alternate
+    // (MFMA i works on subtile i % 2, k-step i / 2), and the K fragments are read
+    // kAttAhead MFMAs ahead of their use, so no MFMA waits on its own LDS read.
     f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+    {
+      auto kfrag = [&](int i) {
+        return *reinterpret_cast<const uint4*>(&k_lds[((i & 1) * 32 + l32) * kKStride + 16 * (i >> 1) + 8 * h]);
+      };
+      uint4 kq[kAttAhead + 1];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 u = *reinterpret_cast<const uint4*>(&k_lds[(kt * 32 + l32) * kKStride + 16 * s + 8 * h]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[s], sacc[kt], 0, 0, 0);
+      for (int i = 0; i < kAttAhead; ++i) kq[i] = kfrag(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + kAttAhead < 16) kq[(i + kAttAhead) % (kAttAhead + 1)] = kfrag(i + kAttAhead);
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, kq[i % (kAttAhead + 1)]), qf[i >> 1], sacc[i & 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kAttAhead, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+        if (i + kAttAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     // Online softmax in the exp2 domain; lanes l and l^32 share a row.  Keys past
@@ -230,21 +247,33 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     // O^T[d][row] += V^T[d][keys] P^T[keys][row]; key order of a P fragment element e
     // for lane half h: kt*32 + 16*s2 + 8*(e/4) + 4*h + e%4 (the S^T output layout),
     // i.e. 4-key units 8kt + 4s2 + h (e < 4) and that + 2 (e >= 4)
+    // MFMA i = (dt, kt, s2) = (i / 4, i / 2 % 2, i % 2); its two 8-byte V^T reads
+    // are issued kAttAhead MFMAs ahead
+    {
+      auto vfrag = [&](int i) {
+        const int d = (i >> 2) * 32 + l32;
+        const uint16_t* vr = &vt_lds[d * kKB];
+        const int sw = vt_swz(d);
+        const int u0 = 8 * ((i >> 1) & 1) + 4 * (i & 1) + h;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * (u0 ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4 * ((u0 + 2) ^ sw));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 vq[kAttAhead + 1];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + l32;
-      const uint16_t* vr = &vt_lds[d * kKB];
-      const int sw = vt_swz(d);
+      for (int i = 0; i < kAttAhead; ++i) vq[i] = vfrag(i);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int i = 0; i < 16; ++i) {
+        if (i + kAttAhead < 16) vq[(i + kAttAhead) % (kAttAhead + 1)] = vfrag(i + kAttAhead);
+        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, vq[i % (kAttAhead + 1)]), pf[(i >> 1) & 1][i & 1], oacc[i >> 2], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAttAhead, 0);  // DS reads
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int u0 = 8 * kt + 4 * s2 + h;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * (u0 ^ sw));
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4 * ((u0 + 2) ^ sw));
-          const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[kt][s2], oacc[dt], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if (i + kAttAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
   }
 

@@ -14,7 +14,7 @@
 // q / k / v, the attention output and the MLP activation are bf16.  The
 // projections run on the LM-head kernel's main loop: split-K partial sums for
 // W_qkv, W_o and W_down (reduced by the kernels below, which also apply RoPE, or
-// the residual add followed by the next RMSNorm), silu(gate) * up fused into the
+// the residual add and the next RMSNorm in one pass), silu(gate) * up fused into the
 // gate / up projection.
 #include <math.h>
 
@@ -28,7 +28,8 @@ namespace ssd {
 
 constexpr int kFwThreads = 256;
 
-// Sum of v over the workgroup (kFwThreads threads); every thread gets it.
+// Sum of v over the workgroup (kThreads threads); every thread gets it.
+template <int kThreads = kFwThreads>
 __device__ __forceinline__ float block_sum(float v, float* s_part) {
   v = wave_sum(v);
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -36,7 +37,7 @@ __device__ __forceinline__ float block_sum(float v, float* s_part) {
   __syncthreads();
   float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < kFwThreads / kWave; ++i) t += s_part[i];
+  for (int i = 0; i < kThreads / kWave; ++i) t += s_part[i];
   __syncthreads();
   return t;
 }
@@ -143,35 +144,63 @@ __global__ __launch_bounds__(kFwThreads) void fwd_qkv_finish_kernel(
   }
 }
 
-// x[grow] += sum of the split partials.  Grid: (compact row, slice of 1024
-// features), four consecutive features per thread, loads of up to eight splits
-// in flight before adding.
-__global__ __launch_bounds__(kFwThreads) void fwd_reduce_add_kernel(
+// x[grow] += the split partials (added in split order), then
+// h[grow] = RMSNorm(x[grow]) g.  One 1024-thread workgroup per compact row;
+// thread t owns features 4t + 4096p (p < 2), and the loads of up to eight splits
+// are in flight before any is added.
+constexpr int kRnThreads = 1024;
+constexpr int kRnPass = 8192 / (4 * kRnThreads);  // hidden <= 8192
+__global__ __launch_bounds__(kRnThreads) void fwd_residual_norm_kernel(
     const float* __restrict__ part, int splits, int part_rows, int hid,
-    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows, float* __restrict__ x) {
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
+    const uint16_t* __restrict__ g, float eps, float* __restrict__ x, uint16_t* __restrict__ hbuf) {
+  __shared__ float s_part[kRnThreads / kWave];
   const int ci = blockIdx.x;
   if (ci >= *n_rows) return;
-  const int k = 4 * (blockIdx.y * kFwThreads + threadIdx.x);
-  if (k >= hid) return;
   const int grow = row_list[ci];
   const size_t stride = static_cast<size_t>(part_rows) * hid;
-  const float* p0 = part + static_cast<size_t>(ci) * hid + k;
-  float4 acc = *reinterpret_cast<const float4*>(x + static_cast<size_t>(grow) * hid + k);
-  for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
-    float4 pv[kSplitBatch];
+  float* const xr = x + static_cast<size_t>(grow) * hid;
+  float4 acc[kRnPass];
+  float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < kSplitBatch; ++u)
-      pv[u] = s0 + u < splits ? *reinterpret_cast<const float4*>(p0 + (s0 + u) * stride)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < kRnPass; ++p) {
+    const int k = 4 * (threadIdx.x + p * kRnThreads);
+    if (k >= hid) continue;
+    const float* p0 = part + static_cast<size_t>(ci) * hid + k;
+    float4 a = *reinterpret_cast<const float4*>(xr + k);
+    for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
+      float4 pv[kSplitBatch];
 #pragma unroll
-    for (int u = 0; u < kSplitBatch; ++u) {
-      acc.x += pv[u].x;
-      acc.y += pv[u].y;
-      acc.z += pv[u].z;
-      acc.w += pv[u].w;
+      for (int u = 0; u < kSplitBatch; ++u)
+        pv[u] = s0 + u < splits ? *reinterpret_cast<const float4*>(p0 + (s0 + u) * stride)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kSplitBatch; ++u) {
+        a.x += pv[u].x;
+        a.y += pv[u].y;
+        a.z += pv[u].z;
+        a.w += pv[u].w;
+      }
     }
+    *reinterpret_cast<float4*>(xr + k) = a;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    acc[p] = a;
   }
-  *reinterpret_cast<float4*>(x + static_cast<size_t>(grow) * hid + k) = acc;
+  const float tot = block_sum<kRnThreads>(ss, s_part);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(hid) + eps);
+  uint16_t* const hr = hbuf + static_cast<size_t>(grow) * hid;
+#pragma unroll
+  for (int p = 0; p < kRnPass; ++p) {
+    const int k = 4 * (threadIdx.x + p * kRnThreads);
+    if (k >= hid) continue;
+    const float4 a = acc[p];
+    // the gain vector carries no alignment promise beyond its element size
+    const uint32_t h0 = f32_to_bf16(a.x * inv * bf16_to_f32(g[k]));
+    const uint32_t h1 = f32_to_bf16(a.y * inv * bf16_to_f32(g[k + 1]));
+    const uint32_t h2 = f32_to_bf16(a.z * inv * bf16_to_f32(g[k + 2]));
+    const uint32_t h3 = f32_to_bf16(a.w * inv * bf16_to_f32(g[k + 3]));
+    *reinterpret_cast<uint2*>(hr + k) = make_uint2(h0 | h1 << 16, h2 | h3 << 16);
+  }
 }
 
 // a[grow][f] = silu(sum of the gate partials) * (sum of the up partials), bf16.
@@ -197,24 +226,6 @@ __global__ __launch_bounds__(kFwThreads) void fwd_swiglu_finish_kernel(
   *reinterpret_cast<uint2*>(a + static_cast<size_t>(row_list[ci]) * inter + f) =
       make_uint2(act(g.x, u.x) | static_cast<uint32_t>(act(g.y, u.y)) << 16,
                  act(g.z, u.z) | static_cast<uint32_t>(act(g.w, u.w)) << 16);
-}
-
-// h[grow] = RMSNorm(x[grow]) g.  One workgroup per compact row.
-__global__ __launch_bounds__(kFwThreads) void fwd_rmsnorm_kernel(
-    int hid, const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
-    const uint16_t* __restrict__ g, float eps, const float* __restrict__ x, uint16_t* __restrict__ hbuf) {
-  __shared__ float s_part[kFwThreads / kWave];
-  const int ci = blockIdx.x;
-  if (ci >= *n_rows) return;
-  const int grow = row_list[ci];
-  const float* xr = x + static_cast<size_t>(grow) * hid;
-  float xv[kFwMaxPer];
-#pragma unroll
-  for (int i = 0; i < kFwMaxPer; ++i) {
-    const int k = threadIdx.x + i * kFwThreads;
-    xv[i] = k < hid ? xr[k] : 0.f;
-  }
-  write_norm<kFwMaxPer>(xv, hid, eps, g, hbuf + static_cast<size_t>(grow) * hid, s_part);
 }
 
 __global__ __launch_bounds__(256) void fwd_zero_kernel(uint32_t* __restrict__ p, size_t n_words) {
@@ -309,10 +320,8 @@ hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32
   const double log2_base = log2(static_cast<double>(rope_base));
   // x += the split partials of the last projection, then h = RMSNorm(x) g
   auto residual_finish = [&](int splits, const uint16_t* g) {
-    hipLaunchKernelGGL(fwd_reduce_add_kernel, dim3(rows, (hid / 4 + kFwThreads - 1) / kFwThreads),
-                       dim3(kFwThreads), 0, s, part, splits, rows, hid, lv.row_list, lv.n_rows, x);
-    hipLaunchKernelGGL(fwd_rmsnorm_kernel, dim3(rows), dim3(kFwThreads), 0, s, hid, lv.row_list,
-                       lv.n_rows, g, eps, x, hb);
+    hipLaunchKernelGGL(fwd_residual_norm_kernel, dim3(rows), dim3(kRnThreads), 0, s, part, splits,
+                       rows, hid, lv.row_list, lv.n_rows, g, eps, x, hb);
   };
   const float scale = 1.0f / sqrtf(static_cast<float>(d));
   for (int l = 0; l < n_layers; ++l) {

@@ -331,11 +331,12 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
  *   k_cache, v_cache [cu_len[B]][Hkv][d].
  *   ids, cu_len, cand [B][W][D], cand_len, copy_gate: as for retrieval / verify.
  *   argmax_out [B][R] int32: as ssd_blocktri_verify (-1 on rows that are not real)
- *   x_out [B][R][hid] float or NULL: the final residual stream (0 on rows that
- *         are not real)
+ *   x_out [B][R][hid] float or NULL, 16-byte aligned: the final residual stream
+ *         (0 on rows that are not real)
+ *   workspace: ssd_verify_forward_workspace_bytes(...) bytes, 16-byte aligned.
  *   begin, end: optional events recorded around the whole forward.
  * hid = Hq*d.  Errors: INVALID_ARG (nulls, sizes < 1, n_layers < 0, Hq % Hkv,
- *   limits, rope_base <= 1 or eps not finite > 0), UNSUPPORTED (d != 128,
+ *   limits, rope_base <= 1 or eps not finite > 0, misaligned x_out), UNSUPPORTED (d != 128,
  *   hid % 256, inter % 256, hid > 8192, or (max_n + 64)*Hkv*d*2 or
  *   B*R*max(hid, inter)*2 not below 0x7ffffff0), WORKSPACE.
  */

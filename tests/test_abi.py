@@ -278,6 +278,7 @@ def test_verify_forward_validation(lib):
 
     for k in ("ids", "cand", "embed", "final_norm", "lm", "am"):
         assert call(**{k: None}) == 1, k
+    assert call(x=ctypes.c_void_p(0x1004)) == 1          # x_out not 16-byte aligned
     assert call(n_layers=-1) == 1
     assert call(n_layers=2) == 1                          # layers missing
     for k, bad in (("base", 1.0), ("base", float("nan")), ("eps", 0.0), ("Hkv", 5), ("W", 65)):
