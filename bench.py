@@ -329,13 +329,17 @@ def bench_forward(a):
     def norm():
         return (1.0 + 0.1 * torch.randn(hid, generator=g, device=dev)).to(torch.bfloat16)
 
-    layers = [{"attn_norm": norm(), "wqkv": randn((Hq + 2 * Hkv) * d, hid, std=hid ** -0.5),
-               "wo": randn(hid, Hq * d, std=(Hq * d) ** -0.5), "mlp_norm": norm(),
-               "w_gate": randn(inter, hid, std=hid ** -0.5), "w_up": randn(inter, hid, std=hid ** -0.5),
-               "w_down": randn(hid, inter, std=inter ** -0.5),
-               "k_cache": randn(N, Hkv, d), "v_cache": randn(N, Hkv, d)} for _ in range(nl)]
+    # each layer's projections are packed as it is drawn (as at model load); the plain
+    # copies are released once packed
+    layers = [cdv.pack_layer({"attn_norm": norm(), "wqkv": randn((Hq + 2 * Hkv) * d, hid, std=hid ** -0.5),
+                              "wo": randn(hid, Hq * d, std=(Hq * d) ** -0.5), "mlp_norm": norm(),
+                              "w_gate": randn(inter, hid, std=hid ** -0.5),
+                              "w_up": randn(inter, hid, std=hid ** -0.5),
+                              "w_down": randn(hid, inter, std=inter ** -0.5),
+                              "k_cache": randn(N, Hkv, d), "v_cache": randn(N, Hkv, d)})
+              for _ in range(nl)]
     embed, final_norm = randn(V, hid), norm()
-    lm = cdv.pack_lm_head(randn(V, hid, std=hid ** -0.5))   # packed once, as at model load
+    lm = cdv.pack_weight(randn(V, hid, std=hid ** -0.5))   # packed once, as at model load
     ids, cu, h, w = up(wl.ids), up(wl.cu_len), up(wl.h), up(wl.w)
     B, R = s.B, 1 + s.W * s.D
     z = torch.empty(B, dtype=torch.float32, device=dev)
@@ -439,7 +443,7 @@ def main():
     B, R = s.B, wl.R
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     if tdt == torch.bfloat16:
-        lm = cdv.pack_lm_head(lm)   # packed once, as at model load (outside the timed region)
+        lm = cdv.pack_weight(lm)   # packed once, as at model load (outside the timed region)
     # every output and the workspace are allocated once, outside the timed region
     z = torch.empty(B, dtype=torch.float32, device=dev)
     fire = torch.empty(B, dtype=torch.uint8, device=dev)

@@ -25,8 +25,10 @@ _SIGS = {
                                        _c_p, _c_p]),
     "ssd_kgram_retrieve": (ctypes.c_int, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p,
                                           _c_p, _c_p, _c_p, _c_p]),
-    "ssd_pack_lm_head_bytes": (ctypes.c_size_t, [_i32, _i32]),
-    "ssd_pack_lm_head": (ctypes.c_int, [_c_p, _i32, _i32, _c_p, ctypes.c_size_t, _c_p]),
+    "ssd_pack_weight_bytes": (ctypes.c_size_t, [_i32, _i32]),
+    "ssd_pack_weight": (ctypes.c_int, [_c_p, _i32, _i32, _c_p, ctypes.c_size_t, _c_p]),
+    "ssd_pack_gate_up_bytes": (ctypes.c_size_t, [_i32, _i32]),
+    "ssd_pack_gate_up": (ctypes.c_int, [_c_p, _c_p, _i32, _i32, _c_p, ctypes.c_size_t, _c_p]),
     "ssd_verify_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      _i32, ctypes.c_int]),
     "ssd_blocktri_verify": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p, _c_p,
@@ -153,39 +155,66 @@ def kgram_retrieve(ids, cu_len, kappa, W, D, fire=None, out=None, stream=None):
     return out
 
 
-class PackedLmHead:
-    """A bf16 LM head [V, K] rearranged by pack_lm_head (device bytes in `data`)."""
+class PackedWeight:
+    """A bf16 weight matrix [rows, K] rearranged by pack_weight, or a gate / up pair
+    [rows, K] each rearranged by pack_gate_up (pair=True); device bytes in `data`."""
 
-    def __init__(self, data, V, K):
-        self.data, self.V, self.K = data, int(V), int(K)
-
-
-def pack_lm_head_bytes(V, K):
-    return int(load().ssd_pack_lm_head_bytes(int(V), int(K)))
+    def __init__(self, data, rows, K, pair=False):
+        self.data, self.rows, self.K, self.pair = data, int(rows), int(K), bool(pair)
 
 
-def pack_lm_head(lm_head, out=None, stream=None):
-    """Rearrange a bf16 LM head [V, K] into the packed layout the bf16 verification
-    calls read.  Returns a PackedLmHead."""
-    _dev(lm_head, "lm_head", (torch.bfloat16,))
-    V, K = lm_head.shape
-    need = pack_lm_head_bytes(V, K)
+def pack_weight_bytes(rows, K):
+    return int(load().ssd_pack_weight_bytes(int(rows), int(K)))
+
+
+def pack_gate_up_bytes(inter, K):
+    return int(load().ssd_pack_gate_up_bytes(int(inter), int(K)))
+
+
+def pack_weight(w, out=None, stream=None):
+    """Rearrange a bf16 weight matrix [rows, K] (an LM head or a projection) into the
+    packed layout the bf16 calls read.  Returns a PackedWeight."""
+    _dev(w, "w", (torch.bfloat16,))
+    rows, K = w.shape
+    need = pack_weight_bytes(rows, K)
     if out is None:
-        out = torch.empty(max(need, 1), dtype=torch.uint8, device=lm_head.device)
-    _check(load().ssd_pack_lm_head(_ptr(lm_head), V, K, _ptr(out), out.numel() * out.element_size(),
-                                   _stream(stream)), "pack_lm_head")
-    return PackedLmHead(out, V, K)
+        out = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    _check(load().ssd_pack_weight(_ptr(w), rows, K, _ptr(out), out.numel() * out.element_size(),
+                                  _stream(stream)), "pack_weight")
+    return PackedWeight(out, rows, K)
+
+
+def pack_gate_up(w_gate, w_up, out=None, stream=None):
+    """Pack an MLP's gate and up projections ([inter, K] bf16 each) into one buffer.
+    Returns a PackedWeight with pair=True."""
+    _dev(w_gate, "w_gate", (torch.bfloat16,))
+    _dev(w_up, "w_up", (torch.bfloat16,))
+    if w_gate.shape != w_up.shape:
+        raise SwitchSDError("w_gate and w_up must have the same shape")
+    inter, K = w_gate.shape
+    need = pack_gate_up_bytes(inter, K)
+    if out is None:
+        out = torch.empty(max(need, 1), dtype=torch.uint8, device=w_gate.device)
+    _check(load().ssd_pack_gate_up(_ptr(w_gate), _ptr(w_up), inter, K, _ptr(out),
+                                   out.numel() * out.element_size(), _stream(stream)), "pack_gate_up")
+    return PackedWeight(out, inter, K, pair=True)
+
+
+def _packed(w, name, rows, K, pair=False):
+    """Device tensor of a PackedWeight argument, checked against the expected shape."""
+    if not isinstance(w, PackedWeight) or w.pair != pair:
+        how = "pack_gate_up" if pair else "pack_weight"
+        raise SwitchSDError(f"{name} must be packed with {how} first")
+    if (rows is not None and w.rows != rows) or w.K != K:
+        raise SwitchSDError(f"{name} is packed as [{w.rows}, {w.K}], expected [{rows}, {K}]")
+    return w.data
 
 
 def _lm_arg(lm_head, dtype, K):
     """(tensor, V) of the LM-head argument: packed for bf16, a plain [V, K] fp32 matrix
     otherwise."""
     if dtype == torch.bfloat16:
-        if not isinstance(lm_head, PackedLmHead):
-            raise SwitchSDError("a bf16 lm_head must be packed with pack_lm_head first")
-        if lm_head.K != K:
-            raise SwitchSDError(f"packed lm_head has K = {lm_head.K}, the rows have {K}")
-        return lm_head.data, lm_head.V
+        return _packed(lm_head, "lm_head", None, K), lm_head.rows
     _dev(lm_head, "lm_head", (torch.float32,))
     if lm_head.shape[1] != K:
         raise SwitchSDError(f"lm_head has K = {lm_head.shape[1]}, the rows have {K}")
@@ -201,7 +230,7 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
                     W, D, scale, attn_out=None, argmax_out=None, logits_out=None, workspace=None,
                     events=None, stream=None):
     """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
-    [B, W*D, Hkv, d]; lm_head [V, Hq*d] (fp32) or a PackedLmHead (bf16).  Returns
+    [B, W*D, Hkv, d]; lm_head [V, Hq*d] (fp32) or a PackedWeight (bf16).  Returns
     (attn_out, argmax_out)."""
     dts = (torch.float32, torch.bfloat16)
     for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
@@ -249,7 +278,7 @@ def _events(events):
 def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand, cand_len,
                            copy_gate, lm_head, W, D, scale, temperature, seed, attn_out=None,
                            rows=None, workspace=None, events=None, stream=None):
-    """Verification pass at temperature > 0 (bf16; lm_head a PackedLmHead).  Shapes as
+    """Verification pass at temperature > 0 (bf16; lm_head a PackedWeight).  Shapes as
     blocktri_verify; cand
     [B, W, D] int32.  Returns (attn_out, rows) with rows a dict of n_children [B, R],
     children / child_w [B, R, W], child_logit [B, R, W], lse [B, R], resample [B, R]."""
@@ -425,7 +454,17 @@ def calibrate(z, labels, out=None, workspace=None, stream=None):
     return out
 
 
-LAYER_FIELDS = ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "k_cache", "v_cache")
+LAYER_FIELDS = ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate_up", "w_down", "k_cache", "v_cache")
+
+
+def pack_layer(layer):
+    """A layer dict with plain bf16 projections (wqkv, wo, w_gate, w_up, w_down) ->
+    the dict verify_forward takes, its projections packed."""
+    out = {k: layer[k] for k in ("attn_norm", "mlp_norm", "k_cache", "v_cache")}
+    out["wqkv"], out["wo"] = pack_weight(layer["wqkv"]), pack_weight(layer["wo"])
+    out["w_gate_up"] = pack_gate_up(layer["w_gate"], layer["w_up"])
+    out["w_down"] = pack_weight(layer["w_down"])
+    return out
 
 
 class _Layer(ctypes.Structure):
@@ -440,18 +479,22 @@ def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers,
                    lm_head, W, D, Hq, Hkv, d, inter, rope_base=500000.0, eps=1e-5,
                    argmax_out=None, x_out=None, workspace=None, events=None, stream=None):
     """The verification pass as a full target forward (bf16 weights; lm_head a
-    PackedLmHead).  layers: list of dicts with the LAYER_FIELDS tensors.  Returns
-    (argmax [B, R] int32, x_out or None)."""
+    PackedWeight).  layers: list of dicts with the LAYER_FIELDS entries, the
+    projections packed (pack_layer).  Returns (argmax [B, R] int32, x_out or None)."""
     for t, n in ((ids, "ids"), (cu_len, "cu_len"), (cand, "cand"), (cand_len, "cand_len")):
         _dev(t, n, (torch.int32,))
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     for t, n in ((embed, "embed"), (final_norm, "final_norm")):
         _dev(t, n, (torch.bfloat16,))
     lm, V = _lm_arg(lm_head, torch.bfloat16, Hq * d)
+    hid = Hq * d
+    shapes = {"wqkv": ((Hq + 2 * Hkv) * d, hid, False), "wo": (hid, hid, False),
+              "w_gate_up": (inter, hid, True), "w_down": (hid, inter, False)}
     arr = (_Layer * max(len(layers), 1))()
     for i, L in enumerate(layers):
         for f in LAYER_FIELDS:
-            setattr(arr[i], f, _dev(L[f], f, (torch.bfloat16,)).data_ptr())
+            t = _packed(L[f], f, *shapes[f]) if f in shapes else _dev(L[f], f, (torch.bfloat16,))
+            setattr(arr[i], f, t.data_ptr())
     B = cu_len.numel() - 1
     R = 1 + W * D
     dev = cand.device

@@ -97,19 +97,38 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
                                     cand_len, copy_gate, stream));
 }
 
-size_t ssd_pack_lm_head_bytes(int32_t V, int32_t K) {
-  if (V < 1 || K < 1 || K % ssd::lm_k_align() != 0 || K > (1 << 20)) return 0;
-  return ssd::packed_lm_head_bytes(V, K);
+size_t ssd_pack_weight_bytes(int32_t rows, int32_t K) {
+  if (rows < 1 || K < 1 || K % ssd::lm_k_align() != 0 || K > (1 << 20)) return 0;
+  return ssd::packed_weight_bytes(rows, K, false);
 }
 
-ssd_status_t ssd_pack_lm_head(const void* lm_head, int32_t V, int32_t K, void* packed,
-                              size_t packed_bytes, hipStream_t stream) {
-  if (!lm_head || !packed || V < 1 || K < 1) return SSD_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(lm_head) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 16 != 0)
-    return SSD_ERR_INVALID_ARG;
+size_t ssd_pack_gate_up_bytes(int32_t inter, int32_t K) {
+  if (inter < 1 || K < 1 || K % ssd::lm_k_align() != 0 || K > (1 << 20)) return 0;
+  return ssd::packed_weight_bytes(inter, K, true);
+}
+
+namespace {
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+ssd_status_t pack(const void* w, const void* w2, int32_t rows, int32_t K, void* packed,
+                  size_t packed_bytes, hipStream_t stream) {
+  if (!w || !packed || rows < 1 || K < 1) return SSD_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(w2) || !aligned16(packed)) return SSD_ERR_INVALID_ARG;
   if (K % ssd::lm_k_align() != 0 || K > (1 << 20)) return SSD_ERR_UNSUPPORTED;
-  if (packed_bytes < ssd::packed_lm_head_bytes(V, K)) return SSD_ERR_WORKSPACE;
-  return from_hip(ssd::launch_pack_lm_head(lm_head, V, K, packed, stream));
+  if (packed_bytes < ssd::packed_weight_bytes(rows, K, w2 != nullptr)) return SSD_ERR_WORKSPACE;
+  return from_hip(ssd::launch_pack_weight(w, w2, rows, K, packed, stream));
+}
+}  // namespace
+
+ssd_status_t ssd_pack_weight(const void* w, int32_t rows, int32_t K, void* packed,
+                             size_t packed_bytes, hipStream_t stream) {
+  return pack(w, nullptr, rows, K, packed, packed_bytes, stream);
+}
+
+ssd_status_t ssd_pack_gate_up(const void* w_gate, const void* w_up, int32_t inter, int32_t K,
+                              void* packed, size_t packed_bytes, hipStream_t stream) {
+  if (!w_up) return SSD_ERR_INVALID_ARG;
+  return pack(w_gate, w_up, inter, K, packed, packed_bytes, stream);
 }
 
 size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
@@ -253,7 +272,7 @@ ssd_status_t ssd_verify_forward(const int32_t* ids, const int32_t* cu_len, int32
   if (reinterpret_cast<uintptr_t>(x_out) % 16 != 0) return SSD_ERR_INVALID_ARG;  // float4 rows
   for (int l = 0; l < n_layers; ++l) {
     const ssd_layer_t& L = layers[l];
-    if (!L.attn_norm || !L.wqkv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up || !L.w_down ||
+    if (!L.attn_norm || !L.wqkv || !L.wo || !L.mlp_norm || !L.w_gate_up || !L.w_down ||
         !L.k_cache || !L.v_cache)
       return SSD_ERR_INVALID_ARG;
   }

@@ -326,8 +326,8 @@ hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32
   const float scale = 1.0f / sqrtf(static_cast<float>(d));
   for (int l = 0; l < n_layers; ++l) {
     const FwdLayer& ly = layers[l];
-    e = launch_gemm(hb, ly.wqkv, nullptr, rows, hid, (Hq + 2 * Hkv) * d, L.p_qkv, L.s_qkv, false,
-                    lmws, part, nullptr, (Hq + 2 * Hkv) * d, s);
+    e = launch_gemm(hb, ly.wqkv, rows, hid, (Hq + 2 * Hkv) * d, L.p_qkv, L.s_qkv, false, lmws, part,
+                    nullptr, (Hq + 2 * Hkv) * d, s);
     if (e != hipSuccess) return e;
     const int nqkv = (Hq + 2 * Hkv) * d;
     hipLaunchKernelGGL(fwd_qkv_finish_kernel, dim3(rows, (nqkv / 2 + kFwThreads - 1) / kFwThreads),
@@ -336,22 +336,20 @@ hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32
     e = launch_attention(qb, ly.k_cache, ly.v_cache, cu_len, kc, vc, cand_len, copy_gate, B, W, D, Hq,
                          Hkv, d, true, scale, L.attn, att, ws_attn, s);
     if (e != hipSuccess) return e;
-    e = launch_gemm(att, ly.wo, nullptr, rows, hid, hid, L.p_o, L.s_o, false, lmws, part, nullptr, hid,
-                    s);
+    e = launch_gemm(att, ly.wo, rows, hid, hid, L.p_o, L.s_o, false, lmws, part, nullptr, hid, s);
     if (e != hipSuccess) return e;
     residual_finish(L.s_o, static_cast<const uint16_t*>(ly.mlp_norm));
     if (L.s_gu > 1) {  // split-K: gate and up partials, then silu(gate) * up
-      e = launch_gemm_pair(hb, ly.w_gate, ly.w_up, rows, hid, inter, L.p_gu, L.s_gu, lmws, part, s);
+      e = launch_gemm_pair(hb, ly.w_gate_up, rows, hid, inter, L.p_gu, L.s_gu, lmws, part, s);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(fwd_swiglu_finish_kernel, dim3(rows, (inter / 4 + kFwThreads - 1) / kFwThreads),
                          dim3(kFwThreads), 0, s, part, L.s_gu, rows, inter, lv.row_list, lv.n_rows, ab);
     } else {  // enough workgroups without splitting: silu(gate) * up in the epilogue
-      e = launch_gemm(hb, ly.w_gate, ly.w_up, rows, hid, inter, L.p_gu, 1, true, lmws, nullptr, ab,
-                      inter, s);
+      e = launch_gemm(hb, ly.w_gate_up, rows, hid, inter, L.p_gu, 1, true, lmws, nullptr, ab, inter, s);
       if (e != hipSuccess) return e;
     }
-    e = launch_gemm(ab, ly.w_down, nullptr, rows, inter, hid, L.p_down, L.s_down, false, lmws, part,
-                    nullptr, hid, s);
+    e = launch_gemm(ab, ly.w_down, rows, inter, hid, L.p_down, L.s_down, false, lmws, part, nullptr,
+                    hid, s);
     if (e != hipSuccess) return e;
     const uint16_t* gn = static_cast<const uint16_t*>(l + 1 < n_layers ? layers[l + 1].attn_norm : final_norm);
     residual_finish(L.s_down, gn);

@@ -42,10 +42,13 @@ struct LmPlan {
 };
 LmPlan lm_plan(int rows, int V, bool bf16);
 size_t lm_workspace_bytes(const LmPlan& p, int rows);
-// packed bf16 LM-head layout (bytes for V rows of K), its K alignment, and the packing
-size_t packed_lm_head_bytes(int V, int K);
+// packed bf16 weight layout of the LM-head / GEMM kernel: bytes for N rows of K (or
+// N features of a gate / up pair), its K alignment, and the packing (w2: the up
+// matrix of a pair, else null)
+size_t packed_weight_bytes(int N, int K, bool pair);
 int lm_k_align();
-hipError_t launch_pack_lm_head(const void* w, int V, int K, void* packed, hipStream_t s);
+hipError_t launch_pack_weight(const void* w, const void* w2, int N, int K, void* packed,
+                              hipStream_t s);
 
 // Sampling (T > 0) arguments of the LM head's epilogue: 1/T, the Philox key, the
 // trie's children per global row, and where the children's logits / T go.
@@ -70,7 +73,6 @@ struct GemmArgs {
   float* part;                // kEpiPartial: [splits][part_rows][ld], by compact row
   int part_rows;
   int ld;                     // leading dimension of part / out (elements)
-  const uint16_t* w2;         // kEpiSwiGLU: the up-projection matrix (A tile 1)
   uint16_t* out;              // kEpiSwiGLU: [global row][ld]
   const int32_t* row_list;    // compact row -> global row
 };
@@ -122,18 +124,18 @@ hipError_t launch_calibrate(const float* z, const uint8_t* labels, int L, int N,
 
 // Decoder-layer GEMM on the LM-head kernel's main loop: rows (bf16, gathered
 // through the compact row list in the LM-head workspace `lm_ws_ptr`) times
-// w^T [N][K].  splits must divide K into multiples of 256.  swiglu: w is the gate
-// and w2 the up projection, out[global row][f] = silu(gate) * up (bf16);
-// otherwise part[split][compact row][n] = partial sums (fp32).
+// w^T [N][K], w packed (launch_pack_weight).  splits must divide K into multiples
+// of 256.  swiglu: w is a packed gate / up pair, out[global row][f] =
+// silu(gate) * up (bf16); otherwise part[split][compact row][n] = partial sums (fp32).
 LmPlan gemm_plan(int rows, int N, bool swiglu);
-hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int total_rows, int K,
-                       int N, const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr,
-                       float* part, uint16_t* out, int ld, hipStream_t s);
-// The gate / up projection with split-K: part[split][compact row][f] = gate partial,
-// part[split][compact row][N + f] = up partial (ld = 2 N).
-hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate, const void* w_up,
-                            int total_rows, int K, int N, const LmPlan& plan, int splits,
-                            const void* lm_ws_ptr, float* part, hipStream_t s);
+hipError_t launch_gemm(const void* rows_in, const void* w, int total_rows, int K, int N,
+                       const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr, float* part,
+                       uint16_t* out, int ld, hipStream_t s);
+// The gate / up projection (a packed pair) with split-K: part[split][compact row][f] =
+// gate partial, part[split][compact row][N + f] = up partial (ld = 2 N).
+hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate_up, int total_rows, int K, int N,
+                            const LmPlan& plan, int splits, const void* lm_ws_ptr, float* part,
+                            hipStream_t s);
 
 // The LM-head workspace's compact row list (written by launch_compact_rows).
 struct LmWsView {
@@ -144,13 +146,13 @@ struct LmWsView {
 LmWsView lm_ws_view(void* ws, int rows);
 
 // Multi-layer verification forward (embedding, decoder layers, final norm, LM head).
+// Projections are packed (launch_pack_weight); norms and caches are plain bf16.
 struct FwdLayer {
   const void* attn_norm;  // [hid] bf16
-  const void* wqkv;       // [(Hq + 2 Hkv) d][hid] bf16: q heads, then k heads, then v heads
+  const void* wqkv;       // [(Hq + 2 Hkv) d][hid]: q heads, then k heads, then v heads
   const void* wo;         // [hid][Hq d]
   const void* mlp_norm;   // [hid]
-  const void* w_gate;     // [inter][hid]
-  const void* w_up;       // [inter][hid]
+  const void* w_gate_up;  // the pair [inter][hid] gate, [inter][hid] up
   const void* w_down;     // [hid][inter]
   const void* k_cache;    // [sum n][Hkv][d] prefix keys after RoPE
   const void* v_cache;    // [sum n][Hkv][d]

@@ -52,10 +52,12 @@ constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in
 constexpr int kLmXcds = 8;                        // XCDs; workgroups are dealt round-robin
 constexpr int kLmXcdSlots = 32;                   // concurrent workgroups per XCD (one per CU)
 constexpr int kPastEnd = -1;                      // iteration index of a load past the K range
-// Packed weight layout of the LM head (ssd_pack_lm_head): per (vocabulary tile,
+// Packed weight layout (ssd_pack_weight, ssd_pack_gate_up): per (256-row tile,
 // k-slab), a 32 KB block; in it, per wave, the 8 KB of A fragments the wave loads
 // for that slab, one 1 KB run per (tile a, k-step s), lane-major.  A wave's
-// weight loads then stream one contiguous 8 KB run per iteration.
+// weight loads then stream one contiguous 8 KB run per iteration.  For the gate /
+// up pair, tile row 64w + 32a + l is feature 128t + 32w + l of the gate (a = 0) or
+// of the up matrix (a = 1).
 constexpr int kPkWaveBytes = kLmVA * 4 * kWave * 16;       // 8 KB
 constexpr int kPkSlabBytes = kLmWaves * kPkWaveBytes;      // 32 KB
 // loads a wave issues per iteration: row blocks, then weight fragments
@@ -279,10 +281,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
     int sm, SampleArgs sa, GemmArgs ga) {
   constexpr bool kSample = kEpi == kEpiSample;
-  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // A tiles from two matrices
-  // the LM head (argmax and sampling epilogues) reads the packed weight layout,
-  // the projections of the forward the plain [N][K] one
-  constexpr bool kPacked = kEpi == kEpiArgmax || kEpi == kEpiSample;
+  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // packed gate / up pair
   __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
@@ -320,28 +319,16 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   const int kc = ga.kc > 0 ? ga.kc : K;
   const int k0 = static_cast<int>(blockIdx.y) * kc;
 
-  // Buffer resources: this workgroup's vocabulary tile of the weights and its row
-  // chunk of O.  Reads whose per-lane offset is past either range return zero
-  // (vocabulary past V, rows past `rows`), so the pipeline needs no guards.
-  const int v_in_tile = min(kTileV, V - vt * kTileV);
+  // Buffer resources: this workgroup's weight tile (K / 64 packed slabs of 32 KB,
+  // zero rows past N) and its row chunk of O.  Reads whose per-lane offset is past
+  // the range return zero (rows past `rows`, prefetches past the K range), so the
+  // pipeline needs no guards.
   const int o_bytes = total_rows * K * 2;
-  __amdgpu_buffer_rsrc_t wres[kLmVA];
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
   int aoff[kLmVA];
 #pragma unroll
-  for (int a = 0; a < kLmVA; ++a) {
-    if constexpr (kPacked) {
-      // this tile's blocks: K / 64 slabs of 32 KB, zero-padded past V
-      wres[a] = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
-      aoff[a] = wave * kPkWaveBytes + a * 4 * kWave * 16 + lane * 16;
-    } else {
-      const uint16_t* src = (kSwiGLU && a == 1) ? ga.w2 : Wt;
-      wres[a] = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(src + static_cast<size_t>(vt) * kTileV * K), 0, v_in_tile * K * 2, kBufFlags);
-      aoff[a] = kSwiGLU ? ((wave * 32 + l32) * K + 8 * h) * 2
-                        : ((wave * kLmVA * 32 + a * 32 + l32) * K + 8 * h) * 2;
-    }
-  }
+  for (int a = 0; a < kLmVA; ++a) aoff[a] = wave * kPkWaveBytes + a * 4 * kWave * 16 + lane * 16;
   const __amdgpu_buffer_rsrc_t ores =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
   // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
@@ -383,27 +370,16 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   };
   auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
     const bool past = it == kPastEnd;
-    if constexpr (kPacked) {
-      // slab block of iteration it; run (a, s) of this wave, 16 B per lane
-      const int r = it + rot;
-      const int so = past ? 0 : (k0 / kLmKS + (r >= nit ? r - nit : r)) * kPkSlabBytes;
+    // slab block of iteration it; run (a, s) of this wave, 16 B per lane
+    const int r = it + rot;
+    const int so = past ? 0 : (k0 / kLmKS + (r >= nit ? r - nit : r)) * kPkSlabBytes;
 #pragma unroll
-      for (int a = 0; a < kLmVA; ++a)
+    for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          dst[a][s] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                         wres[a], past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
-    } else {
-      const int ko = past ? 0 : kbyte(it);
-#pragma unroll
-      for (int a = 0; a < kLmVA; ++a)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          dst[a][s] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(wres[a], past ? kOutOfRange : aoff[a],
-                                                            ko + 32 * s, 0));
-    }
+      for (int s = 0; s < 4; ++s)
+        dst[a][s] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
@@ -602,12 +578,15 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
 constexpr int kCompactThreads = 1024;
 // ----------------------------------------------------------------- weight packing
 // One thread per 16-byte chunk of the packed layout.  Chunk c, decomposed as
-// (tile vt, slab, wave, run a*4 + s, lane = 32h + l32), holds weight row
-// vt*256 + wave*64 + a*32 + l32 at k = slab*64 + 16s + 8h .. +7: the A fragment
-// lane (l32, h) of that wave loads for tile a, k-step s.  Rows past V are zero.
-__global__ __launch_bounds__(256) void pack_lm_head_kernel(const uint16_t* __restrict__ w, int V,
-                                                           int K, uint16_t* __restrict__ packed,
-                                                           size_t n_chunks) {
+// (tile vt, slab, wave, run a*4 + s, lane = 32h + l32), holds tile row
+// 64*wave + 32a + l32 at k = slab*64 + 16s + 8h .. +7: the A fragment lane
+// (l32, h) of that wave loads for tile a, k-step s.  The tile row is weight row
+// 256vt + 64*wave + 32a + l32 of w, or, for a pair (w2 != null), feature
+// 128vt + 32*wave + l32 of w (a = 0) or w2 (a = 1).  Rows past N are zero.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ w2, int N,
+                                                          int K, uint16_t* __restrict__ packed,
+                                                          size_t n_chunks) {
   const int nslab = K / kLmKS;
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   for (size_t c = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
@@ -619,10 +598,13 @@ __global__ __launch_bounds__(256) void pack_lm_head_kernel(const uint16_t* __res
     t /= kLmWaves;
     const int slab = static_cast<int>(t % nslab);
     const size_t vt = t / nslab;
-    const size_t row = vt * kLmVT + wave * kLmVA * 32 + (run / 4) * 32 + (lane & 31);
+    const int a = run / 4;
+    const size_t row = w2 ? vt * (kLmVT / kLmVA) + wave * 32 + (lane & 31)
+                          : vt * kLmVT + wave * kLmVA * 32 + a * 32 + (lane & 31);
+    const uint16_t* src = (w2 && a == 1) ? w2 : w;
     const int k = slab * kLmKS + (run % 4) * 16 + (lane >> 5) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < static_cast<size_t>(V)) v = *reinterpret_cast<const uint4*>(w + row * K + k);
+    if (row < static_cast<size_t>(N)) v = *reinterpret_cast<const uint4*>(src + row * K + k);
     *reinterpret_cast<uint4*>(packed + c * 8) = v;
   }
 }
@@ -839,18 +821,21 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   return e;
 }
 
-size_t packed_lm_head_bytes(int V, int K) {
-  return static_cast<size_t>((V + kLmVT - 1) / kLmVT) * kLmVT * K * 2;
+size_t packed_weight_bytes(int N, int K, bool pair) {
+  const int tile = pair ? kLmVT / kLmVA : kLmVT;   // rows (features) per 256-row packed tile
+  return static_cast<size_t>((N + tile - 1) / tile) * kLmVT * K * 2;
 }
 
 int lm_k_align() { return kLmKAlign; }
 
-hipError_t launch_pack_lm_head(const void* w, int V, int K, void* packed, hipStream_t s) {
-  const size_t n_chunks = packed_lm_head_bytes(V, K) / 16;
+hipError_t launch_pack_weight(const void* w, const void* w2, int N, int K, void* packed,
+                              hipStream_t s) {
+  const size_t n_chunks = packed_weight_bytes(N, K, w2 != nullptr) / 16;
   const size_t want = (n_chunks + 255) / 256;
   const int blocks = static_cast<int>(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(pack_lm_head_kernel, dim3(blocks), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(w), V, K, static_cast<uint16_t*>(packed), n_chunks);
+  hipLaunchKernelGGL(pack_weight_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(w2), N, K,
+                     static_cast<uint16_t*>(packed), n_chunks);
   return hipGetLastError();
 }
 
@@ -879,16 +864,15 @@ LmPlan gemm_plan(int rows, int N, bool swiglu) {
   return plan_for(rows, (N + tile - 1) / tile);
 }
 
-hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int total_rows, int K,
-                       int N, const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr,
-                       float* part, uint16_t* out, int ld, hipStream_t s) {
+hipError_t launch_gemm(const void* rows_in, const void* w, int total_rows, int K, int N,
+                       const LmPlan& plan, int splits, bool swiglu, const void* lm_ws_ptr, float* part,
+                       uint16_t* out, int ld, hipStream_t s) {
   const LmWs lw = lm_ws(const_cast<void*>(lm_ws_ptr), total_rows);
   GemmArgs ga{};
   ga.kc = K / splits;
   ga.part = part;
   ga.part_rows = total_rows;
   ga.ld = ld;
-  ga.w2 = static_cast<const uint16_t*>(w2);
   ga.out = out;
   ga.row_list = lw.row_list;
   const dim3 grid(plan.blocks, splits);
@@ -905,19 +889,18 @@ hipError_t launch_gemm(const void* rows_in, const void* w, const void* w2, int t
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate, const void* w_up,
-                            int total_rows, int K, int N, const LmPlan& plan, int splits,
-                            const void* lm_ws_ptr, float* part, hipStream_t s) {
+hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate_up, int total_rows, int K, int N,
+                            const LmPlan& plan, int splits, const void* lm_ws_ptr, float* part,
+                            hipStream_t s) {
   const LmWs lw = lm_ws(const_cast<void*>(lm_ws_ptr), total_rows);
   GemmArgs ga{};
   ga.kc = K / splits;
   ga.part = part;
   ga.part_rows = total_rows;
   ga.ld = 2 * N;
-  ga.w2 = static_cast<const uint16_t*>(w_up);
   ga.row_list = lw.row_list;
   hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPair>, dim3(plan.blocks, splits), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w_gate),
+                     static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w_gate_up),
                      total_rows, K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles,
                      plan.mchunks, plan.sv, plan.sm, SampleArgs{}, ga);
   return hipGetLastError();

@@ -15,8 +15,8 @@
  * values into the caller's KV cache and lists the tokens that extend the context.
  * At temperature T > 0, ssd_blocktri_verify_sample and ssd_accept_sample take the
  * place of ssd_blocktri_verify and ssd_accept_longest.  Once, when the model is
- * loaded, ssd_pack_lm_head rearranges a bf16 LM head into the layout that the
- * bf16 verification calls read.
+ * loaded, ssd_pack_weight (and ssd_pack_gate_up for an MLP's gate / up pair)
+ * rearranges the bf16 weight matrices into the layout that the bf16 calls read.
  *
  * Offline, before decoding, three calls calibrate the probe (paper §3.2):
  *
@@ -59,7 +59,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 
 typedef enum {
   SSD_OK = 0,
@@ -125,24 +125,33 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
                                 int32_t* cand_len, uint8_t* copy_gate, hipStream_t stream);
 
 /*
- * Packed bf16 LM head.  The projection of the verification pass (paper §3.3: all
+ * Packed bf16 weights.  The projection of the verification pass (paper §3.3: all
  * candidates are checked in one target pass, ending in the LM head) streams the
- * whole V x K matrix once per pass; the bf16 kernels read it in a layout where
- * every wave's weight fragments for one 64-wide k-slab form one contiguous 8 KB
- * run.  Rearranging is a pure permutation (plus zero rows up to a multiple of
- * 256), done once per model:
- *   lm_head [V][K] bf16, row-major, 16-byte aligned (row v = weights of token v)
- *   packed  ssd_pack_lm_head_bytes(V, K) bytes, 16-byte aligned, caller-owned;
+ * whole N x K weight matrix once per pass; the bf16 kernels read it in a layout
+ * where every wave's weight fragments for one 64-wide k-slab form one contiguous
+ * 8 KB run.  Rearranging is a pure permutation (plus zero rows up to a multiple
+ * of 256 tile rows), done once per model:
+ *   w       [rows][K] bf16, row-major, 16-byte aligned (row n = weights of
+ *           output n; for the LM head, token n)
+ *   packed  ssd_pack_weight_bytes(rows, K) bytes, 16-byte aligned, caller-owned;
  *           16-byte chunk c = (((t * K/64 + s) * 4 + w) * 8 + 4a + j) * 64 + 32h + l
- *           holds row 256t + 64w + 32a + l, columns 64s + 16j + 8h .. +7
- *           (zeros for rows >= V)
- * ssd_pack_lm_head_bytes returns 0 for V < 1, K < 1, K % 256 != 0 or K > 2^20.
- * Errors: INVALID_ARG (nulls, V or K < 1, misaligned pointers), UNSUPPORTED
+ *           holds tile row 64w + 32a + l of tile t, columns 64s + 16j + 8h .. +7;
+ *           tile row r of tile t is row 256t + r (zeros for rows past the end)
+ * ssd_pack_gate_up packs the gate and up projections of an MLP, w_gate and w_up
+ * [inter][K] each, into one buffer of ssd_pack_gate_up_bytes(inter, K) bytes with
+ * the same chunk order, where tile row 64w + 32a + l of tile t is feature
+ * 128t + 32w + l of w_gate (a = 0) or of w_up (a = 1): the kernel then finds a
+ * feature's gate and up weights in the same lane.
+ * The _bytes queries return 0 for sizes < 1, K % 256 != 0 or K > 2^20.
+ * Errors: INVALID_ARG (nulls, sizes < 1, misaligned pointers), UNSUPPORTED
  *   (K % 256 != 0 or K > 2^20), WORKSPACE (packed_bytes too small).
  */
-size_t ssd_pack_lm_head_bytes(int32_t V, int32_t K);
-ssd_status_t ssd_pack_lm_head(const void* lm_head, int32_t V, int32_t K, void* packed,
-                              size_t packed_bytes, hipStream_t stream);
+size_t ssd_pack_weight_bytes(int32_t rows, int32_t K);
+ssd_status_t ssd_pack_weight(const void* w, int32_t rows, int32_t K, void* packed,
+                             size_t packed_bytes, hipStream_t stream);
+size_t ssd_pack_gate_up_bytes(int32_t inter, int32_t K);
+ssd_status_t ssd_pack_gate_up(const void* w_gate, const void* w_up, int32_t inter, int32_t K,
+                              void* packed, size_t packed_bytes, hipStream_t stream);
 
 /* Bytes of scratch that ssd_blocktri_verify needs for these sizes (0 on bad sizes). */
 size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
@@ -165,7 +174,7 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  *                                   real (gate closed, w >= M, j >= L_w) are zeros
  * LM head + argmax:
  *   lm_head  fp32: [V][Hq*d]        transposed projection (row v = weights of token v)
- *            bf16: that matrix as written by ssd_pack_lm_head
+ *            bf16: that matrix as written by ssd_pack_weight
  *   argmax_out [B][R] int32         lowest index among equal maxima; -1 on rows
  *                                   that are not real
  *   logits_out [B][R][V] float or NULL (debug output; written for every row)
@@ -322,13 +331,13 @@ ssd_status_t ssd_accept_sample(const int32_t* n_children, const int32_t* child_w
  * context token's key (after RoPE) and value, the anchor's included.  The
  * residual stream is fp32; the activations between steps (h, q, k, v, the
  * attention output, the MLP activation) are bf16.  Only real rows are computed.
- * Weights, all bf16, [out][in] row-major (the LM head packed):
- *   embed [V][hid], final_norm [hid], lm_head [V][hid] as written by
- *   ssd_pack_lm_head;
+ * Weights, all bf16, [out][in] (the projections packed by ssd_pack_weight):
+ *   embed [V][hid] and final_norm [hid] row-major; lm_head [V][hid] packed;
  *   per layer (ssd_layer_t, an array of n_layers on the host): attn_norm,
- *   mlp_norm [hid]; wqkv [(Hq + 2 Hkv) d][hid] (q heads, then k heads, then
- *   v heads); wo [hid][Hq d]; w_gate, w_up [inter][hid]; w_down [hid][inter];
- *   k_cache, v_cache [cu_len[B]][Hkv][d].
+ *   mlp_norm [hid]; wqkv [(Hq + 2 Hkv) d][hid] packed (q heads, then k heads,
+ *   then v heads); wo [hid][Hq d] packed; w_gate_up: the gate and up
+ *   projections [inter][hid] each, packed by ssd_pack_gate_up; w_down
+ *   [hid][inter] packed; k_cache, v_cache [cu_len[B]][Hkv][d] row-major.
  *   ids, cu_len, cand [B][W][D], cand_len, copy_gate: as for retrieval / verify.
  *   argmax_out [B][R] int32: as ssd_blocktri_verify (-1 on rows that are not real)
  *   x_out [B][R][hid] float or NULL, 16-byte aligned: the final residual stream
@@ -345,8 +354,7 @@ typedef struct {
   const void* wqkv;
   const void* wo;
   const void* mlp_norm;
-  const void* w_gate;
-  const void* w_up;
+  const void* w_gate_up;
   const void* w_down;
   const void* k_cache;
   const void* v_cache;

@@ -54,7 +54,7 @@ class Dev:
             self.kc, self.vc = up(wl.k_cand), up(wl.v_cand)
             # the bf16 calls read the LM head packed (once, as at model load)
             lm = up(wl.lm_head)
-            self.lm = cdv.pack_lm_head(lm) if lm.dtype == torch.bfloat16 else lm
+            self.lm = cdv.pack_weight(lm) if lm.dtype == torch.bfloat16 else lm
 
 
 def check_probe(wl, d):

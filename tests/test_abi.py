@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_calibrate", "ssd_calibrate_workspace_bytes",
                           "ssd_blocktri_verify_sample", "ssd_accept_sample",
                           "ssd_verify_forward", "ssd_verify_forward_workspace_bytes",
-                          "ssd_pack_lm_head", "ssd_pack_lm_head_bytes"}
+                          "ssd_pack_weight", "ssd_pack_weight_bytes", "ssd_pack_gate_up",
+                          "ssd_pack_gate_up_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -72,14 +73,18 @@ def test_workspace_query(lib):
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
-def test_pack_lm_head_validation(lib):
-    nb = lib.ssd_pack_lm_head_bytes
+def test_pack_validation(lib):
+    nb = lib.ssd_pack_weight_bytes
     assert nb(128256, 4096) == 128256 * 4096 * 2                 # 501 full tiles of 256 rows
     assert nb(1000, 512) == 1024 * 512 * 2                       # last tile zero-padded
     assert nb(0, 4096) == 0 and nb(10, 0) == 0
     assert nb(10, 4095) == 0 and nb(10, 4160) == 0               # K % 256
     assert nb(10, (1 << 20) + 256) == 0
-    f = lib.ssd_pack_lm_head
+    pb = lib.ssd_pack_gate_up_bytes
+    assert pb(14336, 4096) == 2 * 14336 * 4096 * 2               # 112 tiles of 128 features
+    assert pb(300, 256) == 3 * 256 * 256 * 2                     # 3 tiles, zero-padded
+    assert pb(0, 256) == 0 and pb(128, 100) == 0
+    f = lib.ssd_pack_weight
     good = [FAKE, 1000, 512, FAKE, 1024 * 512 * 2, None]
     for i, bad in ((0, None), (3, None), (1, 0), (2, 0), (0, ctypes.c_void_p(0x1008)),
                    (3, ctypes.c_void_p(0x1004))):
@@ -92,6 +97,15 @@ def test_pack_lm_head_validation(lib):
     a = list(good)
     a[4] = 1024 * 512 * 2 - 16
     assert f(*a) == 3                                            # packed buffer too small
+    fp = lib.ssd_pack_gate_up
+    goodp = [FAKE, FAKE, 300, 256, FAKE, 3 * 256 * 256 * 2, None]
+    for i, bad in ((0, None), (1, None), (4, None), (2, 0), (1, ctypes.c_void_p(0x1002))):
+        a = list(goodp)
+        a[i] = bad
+        assert fp(*a) == 1, (i, bad)
+    a = list(goodp)
+    a[5] = 3 * 256 * 256 * 2 - 16
+    assert fp(*a) == 3
 
 
 def test_probe_validation(lib):

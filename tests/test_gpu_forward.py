@@ -65,12 +65,13 @@ def _f64_layers(fw, n):
 def _run(fw, n_layers, kg):
     s = fw.spec
     R = 1 + s.W * s.D
-    layers = [{k: up(v) for k, v in L.items()} for L in fw.layers[:n_layers]]
+    # projections packed once, as at model load
+    layers = [cdv.pack_layer({k: up(v) for k, v in L.items()}) for L in fw.layers[:n_layers]]
     x = torch.empty(s.B, R, s.hid, dtype=torch.float32, device=DEV)
     am, _ = cdv.verify_forward(up(fw.ids), up(fw.cu_len), int(np.diff(fw.cu_len).max()),
                                up(kg["cand"].astype(np.int32)), up(kg["cand_len"].astype(np.int32)),
                                up(kg["copy_gate"].astype(np.uint8)), up(fw.embed), layers,
-                               up(fw.final_norm), cdv.pack_lm_head(up(fw.lm_head)), s.W, s.D, s.Hq, s.Hkv, s.d,
+                               up(fw.final_norm), cdv.pack_weight(up(fw.lm_head)), s.W, s.D, s.Hq, s.Hkv, s.d,
                                fw.inter, x_out=x)
     torch.cuda.synchronize()
     return host(am), host(x)

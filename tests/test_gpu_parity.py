@@ -112,28 +112,56 @@ def test_all_gates_closed():
 
 
 def _pack_host(w, K):
-    """The packed LM-head layout from its definition: 16-byte chunk
+    """The packed weight layout from its definition: 16-byte chunk
     c = (((t*K/64 + s)*4 + wv)*8 + 4a + j)*64 + 32h + l holds row 256t + 64wv + 32a + l,
-    columns 64s + 16j + 8h .. +7; rows past V are zero."""
-    V = w.shape[0]
-    T = -(-V // 256)
+    columns 64s + 16j + 8h .. +7; rows past the end are zero."""
+    N = w.shape[0]
+    T = -(-N // 256)
     wp = np.zeros((T * 256, K), dtype=np.uint16)
-    wp[:V] = w
+    wp[:N] = w
     x = wp.reshape(T, 4, 2, 32, K // 64, 4, 2, 8)        # t, wv, a, l | s, j, h, e
     return x.transpose(0, 4, 1, 2, 5, 6, 3, 7).reshape(-1)
 
 
-@pytest.mark.parametrize("V,K", [(1000, 512), (256, 1024), (513, 256)])
-def test_pack_lm_head_layout_bitwise(V, K):
-    print(f"[case] pack_lm_head V={V} K={K}", flush=True)
-    rng = np.random.default_rng(V + K)
-    bits = rng.integers(0, 1 << 16, (V, K), dtype=np.uint16)
-    w = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
-    packed = cdv.pack_lm_head(w)
+def _pair_rows_host(gate, up):
+    """The gate / up pair as the rows of one matrix: row 256t + 64wv + 32a + l is
+    feature 128t + 32wv + l of the gate (a = 0) or of the up matrix (a = 1)."""
+    inter, K = gate.shape
+    T = -(-inter // 128)
+    g = np.zeros((T * 128, K), dtype=np.uint16)
+    u = np.zeros((T * 128, K), dtype=np.uint16)
+    g[:inter], u[:inter] = gate, up
+    out = np.stack([g.reshape(T, 4, 32, K), u.reshape(T, 4, 32, K)], axis=2)   # t, wv, a, l
+    return out.reshape(T * 256, K)
+
+
+def _bits(rng, shape):
+    bits = rng.integers(0, 1 << 16, shape, dtype=np.uint16)
+    return bits, torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("N,K", [(1000, 512), (256, 1024), (513, 256)])
+def test_pack_weight_layout_bitwise(N, K):
+    print(f"[case] pack_weight N={N} K={K}", flush=True)
+    bits, w = _bits(np.random.default_rng(N + K), (N, K))
+    packed = cdv.pack_weight(w)
     torch.cuda.synchronize()
     got = packed.data.cpu().numpy().view(np.uint16)
-    assert got.size == -(-V // 256) * 256 * K
+    assert got.size == -(-N // 256) * 256 * K
     assert np.array_equal(got, _pack_host(bits, K))
+
+
+@pytest.mark.parametrize("inter,K", [(1024, 256), (300, 512), (128, 768)])
+def test_pack_gate_up_layout_bitwise(inter, K):
+    print(f"[case] pack_gate_up inter={inter} K={K}", flush=True)
+    rng = np.random.default_rng(inter * 7 + K)
+    gbits, g = _bits(rng, (inter, K))
+    ubits, u = _bits(rng, (inter, K))
+    packed = cdv.pack_gate_up(g, u)
+    torch.cuda.synchronize()
+    got = packed.data.cpu().numpy().view(np.uint16)
+    assert got.size == -(-inter // 128) * 256 * K
+    assert np.array_equal(got, _pack_host(_pair_rows_host(gbits, ubits), K))
 
 
 def test_unpacked_bf16_lm_head_is_refused():
