@@ -2,15 +2,18 @@
 // paper §3.3: one target forward pass verifies all candidates; write-up §3.1:
 // T = 0, so each row's verdict is the argmax of its logits).
 //
-// logits[row][v] = sum_k O[row][k] * lm_head[v][k].  The weight matrix (V x hid,
-// K-contiguous) is the dominant HBM stream, so each workgroup owns a 256-wide
-// vocabulary tile and streams it exactly once while every row of the row chunk
-// (up to 224 rows, the whole verify batch of one sequence) is multiplied
-// against it: the rows are the MFMA N dimension (B operand, staged in LDS),
-// the vocabulary is the M dimension (A operand, loaded straight from HBM into
-// registers one k-step ahead).  The epilogue reduces each row over the tile to
-// a (max, lowest index) pair without writing logits; a second tiny kernel
-// reduces the tiles.  An fp32 variant on the vector ALU serves fp32 inputs.
+// logits[row][v] = sum_k O[row][k] * lm_head[v][k].  The weight matrix (V x hid)
+// is the dominant HBM stream, so each workgroup owns a 256-wide vocabulary tile
+// and streams it exactly once while every row of the row chunk (up to 224 rows,
+// the whole verify batch of one sequence) is multiplied against it: the rows are
+// the MFMA N dimension (B operand, staged in LDS), the vocabulary is the M
+// dimension (A operand, loaded straight from HBM into registers, three k-steps
+// ahead, from the packed layout in which each wave's fragments of a k-step are
+// one contiguous 8 KB run).  The epilogue reduces each row over the tile to a
+// (max, lowest index) pair without writing logits; a second tiny kernel reduces
+// the tiles.  The same main loop, with other epilogues, serves the sampling
+// verification and the projections of the forward.  An fp32 variant on the
+// vector ALU serves fp32 inputs (plain [V][hid] weights).
 #include <limits.h>
 
 #include <type_traits>
@@ -364,15 +367,14 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // once.
   const int nit = kc / kLmKS;
   const int rot = vt % nit;
-  auto kbyte = [&](int it) {
+  auto slab = [&](int it) {   // global k-slab index (k0 is a multiple of 64)
     const int r = it + rot;
-    return (k0 + (r >= nit ? r - nit : r) * kLmKS) * 2;
+    return k0 / kLmKS + (r >= nit ? r - nit : r);
   };
   auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
     const bool past = it == kPastEnd;
     // slab block of iteration it; run (a, s) of this wave, 16 B per lane
-    const int r = it + rot;
-    const int so = past ? 0 : (k0 / kLmKS + (r >= nit ? r - nit : r)) * kPkSlabBytes;
+    const int so = past ? 0 : slab(it) * kPkSlabBytes;
 #pragma unroll
     for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
-    const int ko = past ? 0 : kbyte(it);
+    const int ko = past ? 0 : slab(it) * kLmKS * 2;
 #pragma unroll
     for (int j = 0; j < kLmBlocksPerWave; ++j) {
       const int b = wave * kLmBlocksPerWave + j;
