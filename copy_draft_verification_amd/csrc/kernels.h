@@ -39,6 +39,7 @@ struct LmPlan {
   int mchunks;  // row chunks
   int sv, sm;   // bf16: super-tile of sv vocabulary tiles x sm row chunks per XCD
   int blocks;   // bf16: workgroups launched (super-tiles dealt round-robin to XCDs)
+  int half = 0; // GEMM: tiles are 128-row halves of the packed 256-row tiles
 };
 LmPlan lm_plan(int rows, int V, bool bf16);
 size_t lm_workspace_bytes(const LmPlan& p, int rows);
@@ -67,6 +68,7 @@ constexpr int kEpiSample = 1;   // per (row, tile) sampling partials
 constexpr int kEpiPartial = 2;  // split-K partial sums, fp32
 constexpr int kEpiSwiGLU = 3;   // silu(gate) * up, bf16
 constexpr int kEpiPair = 4;     // two A matrices (gate, up), split-K partial sums of both
+constexpr int kEpiPartialHalf = 5;  // kEpiPartial on one 128-row half of a packed 256-row tile
 
 struct GemmArgs {
   int kc;                     // hidden elements per split (0: all of K)

@@ -86,11 +86,12 @@ __device__ __forceinline__ int lm_swz(int r, int c) { return c ^ ((r >> 1) & 7);
 // the gate in A tile 0 and the up projection in A tile 1).
 //  * kEpiPartial: this split's partial sums, fp32, dense by compact row:
 //    part[split][row][feature], four consecutive features per 16-byte store.
+//    kEpiPartialHalf: the same for one A tile per wave (a 128-row half tile).
 //  * kEpiSwiGLU: silu(gate) * up, bf16, at out[global row][feature].
 //  * kEpiPair: the gate and up partial sums of this split, fp32:
 //    part[split][row][feature] and part[split][row][N + feature].
-template <int kEpi>
-__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows,
+template <int kEpi, int kVA>
+__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kVA][kLmNT], int row0, int rows,
                                               int vbase, int V, int h, int l32, const GemmArgs& ga) {
 #pragma unroll
   for (int t = 0; t < kLmNT; ++t) {
@@ -112,10 +113,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[kLmVA][kLmNT],
             for (int i = 0; i < 4; ++i)
               if (f + i < V) dst[i] = acc[a][t][4 * q + i];
         }
-    } else if constexpr (kEpi == kEpiPartial) {
+    } else if constexpr (kEpi == kEpiPartial || kEpi == kEpiPartialHalf) {
       float* pr = ga.part + (static_cast<size_t>(blockIdx.y) * ga.part_rows + row) * ga.ld;
 #pragma unroll
-      for (int a = 0; a < kLmVA; ++a)
+      for (int a = 0; a < kVA; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int v = vbase + a * 32 + 8 * q + 4 * h;
@@ -277,204 +278,13 @@ __device__ __forceinline__ void sample_epilogue(
   }
 }
 
-template <int kEpi>
-__global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
-    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
-    float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
-    int sm, SampleArgs sa, GemmArgs ga) {
-  constexpr bool kSample = kEpi == kEpiSample;
-  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // packed gate / up pair
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[kLmStage];
-  __shared__ float red_v[kLmWaves][kLmMC];
-  __shared__ int red_i[kLmWaves][kLmMC];
-  __shared__ float red_m[kSample ? kLmWaves : 1][kLmMC];
-  __shared__ float red_s[kSample ? kLmWaves : 1][kLmMC];
-
-  // XCD-aware tile order.  Workgroups are dealt round-robin over the XCDs (block L
-  // runs on XCD L % 8).  Super-tiles of sv vocabulary tiles x sm row chunks (about
-  // one XCD's worth of concurrent workgroups) are dealt to XCDs whole, so the
-  // workgroups resident together on an XCD share their weights and rows in its L2.
-  const int xcd = static_cast<int>(blockIdx.x % kLmXcds), li = static_cast<int>(blockIdx.x / kLmXcds);
-  const int per = sv * sm;
-  const int super = (li / per) * kLmXcds + xcd;
-  const int n_sm = (mchunks + sm - 1) / sm;
-  const int vt = (super / n_sm) * sv + (li % per) / sm;
-  const int mc = (super % n_sm) * sm + (li % per) % sm;
-  if (vt >= vtiles || mc >= mchunks) return;
-  // rows of this chunk are compact indices row0.. into the list of real rows
-  const int rows = *n_rows;
-  if (mc * kLmMC >= rows) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  // wave index in a scalar register: the LDS destination of a buffer-to-LDS load
-  // (M0) must be wave-uniform
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int h = lane >> 5, l32 = lane & 31;
-  const int row0 = mc * kLmMC;
-  // the gate / up GEMM takes its two A tiles from two matrices (the same 32
-  // features of each), so a workgroup covers 128 features instead of 256
-  constexpr int kTileV = kSwiGLU ? kLmVT / kLmVA : kLmVT;
-  const int vbase = kSwiGLU ? vt * kTileV + wave * 32 : vt * kLmVT + wave * kLmVA * 32;
-  // split-K: this workgroup contracts k0 .. k0 + kc of the hidden dimension
-  const int kc = ga.kc > 0 ? ga.kc : K;
-  const int k0 = static_cast<int>(blockIdx.y) * kc;
-
-  // Buffer resources: this workgroup's weight tile (K / 64 packed slabs of 32 KB,
-  // zero rows past N) and its row chunk of O.  Reads whose per-lane offset is past
-  // the range return zero (rows past `rows`, prefetches past the K range), so the
-  // pipeline needs no guards.
-  const int o_bytes = total_rows * K * 2;
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Wt + static_cast<size_t>(vt) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
-  int aoff[kLmVA];
-#pragma unroll
-  for (int a = 0; a < kLmVA; ++a) aoff[a] = wave * kPkWaveBytes + a * 4 * kWave * 16 + lane * 16;
-  const __amdgpu_buffer_rsrc_t ores =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
-  // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
-  // fills stage row 8b + i/8 at swizzled position i%8 from O row
-  // row_list[row0 + 8b + i/8].  Stage rows past the last real row read past the end
-  // of O, which returns zero.
-  int ooff[kLmBlocksPerWave];
-#pragma unroll
-  for (int j = 0; j < kLmBlocksPerWave; ++j) {
-    const int sr = 8 * (wave * kLmBlocksPerWave + j) + (lane >> 3);
-    const int ci = row0 + sr;
-    const int orow = ci < rows ? row_list[ci] : -1;
-    ooff[j] = orow < 0 ? o_bytes : (orow * K + lm_swz(sr, lane & 7) * 8) * 2;
-  }
-
-  f32x16 acc[kLmVA][kLmNT];
-#pragma unroll
-  for (int a = 0; a < kLmVA; ++a)
-#pragma unroll
-    for (int t = 0; t < kLmNT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
-
-  uint4 aw[kLmSlots][kLmVA][4];
-  // The loop issues loads ahead of their use; the issues that fall past this
-  // workgroup's K range (it == kPastEnd) take a per-lane offset beyond every
-  // buffer's num_records, so they return zeros without touching memory instead
-  // of fetching the next range's data.
-  constexpr int kOutOfRange = 0x7ffffff0;
-  // Iteration it contracts k-slab (it + rot) mod nit: the workgroups resident
-  // together start at different slabs of their tiles, so their streams do not all
-  // hit the same column range of the weight rows (and the same HBM channels) at
-  // once.
-  const int nit = kc / kLmKS;
-  const int rot = vt % nit;
-  auto slab = [&](int it) {   // global k-slab index (k0 is a multiple of 64)
-    const int r = it + rot;
-    return k0 / kLmKS + (r >= nit ? r - nit : r);
-  };
-  auto load_a = [&](uint4 (&dst)[kLmVA][4], int it) {
-    const bool past = it == kPastEnd;
-    // slab block of iteration it; run (a, s) of this wave, 16 B per lane
-    const int so = past ? 0 : slab(it) * kPkSlabBytes;
-#pragma unroll
-    for (int a = 0; a < kLmVA; ++a)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dst[a][s] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
-  };
-  auto load_o = [&](uint16_t* stage, int it) {
-    const bool past = it == kPastEnd;
-    const int ko = past ? 0 : slab(it) * kLmKS * 2;
-#pragma unroll
-    for (int j = 0; j < kLmBlocksPerWave; ++j) {
-      const int b = wave * kLmBlocksPerWave + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ores, (__attribute__((address_space(3))) void*)(stage + b * 512), 16,
-          past ? kOutOfRange : ooff[j], ko, 0, 0);
-    }
-  };
-  // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
-  // MFMAs.  The LDS reads run kLmBAhead fragments ahead of their use; the
-  // scheduling groups pin that order (first kLmBAhead reads, then two MFMAs and one
-  // read at a time) so that the compiler does not sink the reads next to their use.
-  auto compute = [&](const uint4 (&w)[kLmVA][4], const uint16_t* stage) {
-    constexpr int NB = 4 * kLmNT;
-    const uint16_t* ob = stage + l32 * kLmKS;
-    const int sw = (l32 >> 1) & 7;
-    auto frag = [&](int j) {
-      const int s = j / kLmNT, t = j % kLmNT;
-      return *reinterpret_cast<const uint4*>(ob + t * 32 * kLmKS + (((2 * s + h) ^ sw) << 3));
-    };
-    uint4 bq[kLmBAhead + 1];
-#pragma unroll
-    for (int i = 0; i < kLmBAhead; ++i) bq[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int s = i / kLmNT, t = i % kLmNT;
-      if (i + kLmBAhead < NB) bq[(i + kLmBAhead) % (kLmBAhead + 1)] = frag(i + kLmBAhead);
-      const bf16x8 bfr = __builtin_bit_cast(bf16x8, bq[i % (kLmBAhead + 1)]);
-#pragma unroll
-      for (int a = 0; a < kLmVA; ++a)
-        acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[a][s]), bfr,
-                                                            acc[a][t], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, kLmBAhead, 0);  // DS reads
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kLmVA, 0);    // MFMAs
-      if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  uint16_t* const stages[kLmSlots] = {st0, st1, st2, st3};
-
-  // Step U of the unrolled loop works on iteration it (it % 4 == U): wait until this
-  // wave's rows and weights of iteration it have landed (everything but the two
-  // newer iterations' loads), barrier so every wave's row blocks are in LDS and
-  // stage (U+3)%4 is no longer read, issue iteration it+3, compute iteration it.
-  auto step = [&](auto U_c, int it) {
-    constexpr int U = decltype(U_c)::value;
-    // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLmLoadsPerIter));
-    lds_barrier();
-    load_o(stages[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
-    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: rows, then weights
-    load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(aw[U], stages[U]);
-  };
-  load_o(st0, 0);
-  load_a(aw[0], 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_o(st1, 1);
-  load_a(aw[1], 1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_o(st2, 2);
-  load_a(aw[2], 2);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int it0 = 0; it0 < nit; it0 += kLmSlots) {
-    step(IntC<0>{}, it0);
-    step(IntC<1>{}, it0 + 1);
-    step(IntC<2>{}, it0 + 2);
-    step(IntC<3>{}, it0 + 3);
-  }
-  // the last three iterations' loads (past the end: zeros) must land before the
-  // workgroup's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  if constexpr (kEpi == kEpiPartial || kSwiGLU) {
-    gemm_epilogue<kEpi>(acc, row0, rows, vbase, V, h, l32, ga);
-    return;
-  }
-  if constexpr (kSample) {
-    sample_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, sa,
-                    red_v, red_i, reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_m),
-                    reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_s), static_cast<float4*>(part_out));
-    return;
-  }
-  int2* const part = static_cast<int2*>(part_out);
-  // epilogue: per row (this lane's column l32 of each row tile), the best
-  // (value, lowest index) over this workgroup's tile
+// Greedy epilogue: per row (this lane's column l32 of each row tile), the best
+// (value, lowest index) over this workgroup's tile, combined over the four waves.
+__device__ __forceinline__ void argmax_epilogue(
+    const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows, int vbase, int V, int vt, int vtiles,
+    int wave, int tid, int l32, int h, const int32_t* __restrict__ row_list,
+    float* __restrict__ logits_out, float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC],
+    int2* __restrict__ part) {
 #pragma unroll
   for (int t = 0; t < kLmNT; ++t) {
     const int row = row0 + t * 32 + l32;
@@ -509,6 +319,209 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     part[static_cast<size_t>(row) * vtiles + vt] = make_int2(__float_as_int(bv), bi);
   }
 }
+
+template <int kEpi>
+__global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
+    float* __restrict__ logits_out, void* __restrict__ part_out, int vtiles, int mchunks, int sv,
+    int sm, SampleArgs sa, GemmArgs ga) {
+  constexpr bool kSample = kEpi == kEpiSample;
+  constexpr bool kSwiGLU = kEpi == kEpiSwiGLU || kEpi == kEpiPair;   // packed gate / up pair
+  // A tiles per wave: one for a half tile (rows 64w + 32 hh .. + 31 of a packed tile)
+  constexpr int kVA = kEpi == kEpiPartialHalf ? 1 : kLmVA;
+  constexpr int kLoadsPerIter = kLmBlocksPerWave + kVA * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[kLmStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[kLmStage];
+  __shared__ float red_v[kLmWaves][kLmMC];
+  __shared__ int red_i[kLmWaves][kLmMC];
+  __shared__ float red_m[kSample ? kLmWaves : 1][kLmMC];
+  __shared__ float red_s[kSample ? kLmWaves : 1][kLmMC];
+
+  // XCD-aware tile order.  Workgroups are dealt round-robin over the XCDs (block L
+  // runs on XCD L % 8).  Super-tiles of sv vocabulary tiles x sm row chunks (about
+  // one XCD's worth of concurrent workgroups) are dealt to XCDs whole, so the
+  // workgroups resident together on an XCD share their weights and rows in its L2.
+  const int xcd = static_cast<int>(blockIdx.x % kLmXcds), li = static_cast<int>(blockIdx.x / kLmXcds);
+  const int per = sv * sm;
+  const int super = (li / per) * kLmXcds + xcd;
+  const int n_sm = (mchunks + sm - 1) / sm;
+  const int vt = (super / n_sm) * sv + (li % per) / sm;
+  const int mc = (super % n_sm) * sm + (li % per) % sm;
+  if (vt >= vtiles || mc >= mchunks) return;
+  // rows of this chunk are compact indices row0.. into the list of real rows
+  const int rows = *n_rows;
+  if (mc * kLmMC >= rows) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // wave index in a scalar register: the LDS destination of a buffer-to-LDS load
+  // (M0) must be wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int row0 = mc * kLmMC;
+  // the gate / up GEMM takes its two A tiles from two matrices (the same 32
+  // features of each), so a workgroup covers 128 features instead of 256; a
+  // half-tile workgroup covers rows 64w + 32hh .. + 31 of packed tile vt / 2
+  const int ptile = kVA == 1 ? vt >> 1 : vt, hh = kVA == 1 ? vt & 1 : 0;
+  const int vbase = kSwiGLU ? vt * (kLmVT / kLmVA) + wave * 32
+                            : ptile * kLmVT + wave * kLmVA * 32 + hh * 32;
+  // split-K: this workgroup contracts k0 .. k0 + kc of the hidden dimension
+  const int kc = ga.kc > 0 ? ga.kc : K;
+  const int k0 = static_cast<int>(blockIdx.y) * kc;
+
+  // Buffer resources: this workgroup's weight tile (K / 64 packed slabs of 32 KB,
+  // zero rows past N) and its row chunk of O.  Reads whose per-lane offset is past
+  // the range return zero (rows past `rows`, prefetches past the K range), so the
+  // pipeline needs no guards.
+  const int o_bytes = total_rows * K * 2;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Wt + static_cast<size_t>(ptile) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
+  int aoff[kVA];
+#pragma unroll
+  for (int a = 0; a < kVA; ++a) aoff[a] = wave * kPkWaveBytes + (a + hh) * 4 * kWave * 16 + lane * 16;
+  const __amdgpu_buffer_rsrc_t ores =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
+  // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
+  // fills stage row 8b + i/8 at swizzled position i%8 from O row
+  // row_list[row0 + 8b + i/8].  Stage rows past the last real row read past the end
+  // of O, which returns zero.
+  int ooff[kLmBlocksPerWave];
+#pragma unroll
+  for (int j = 0; j < kLmBlocksPerWave; ++j) {
+    const int sr = 8 * (wave * kLmBlocksPerWave + j) + (lane >> 3);
+    const int ci = row0 + sr;
+    const int orow = ci < rows ? row_list[ci] : -1;
+    ooff[j] = orow < 0 ? o_bytes : (orow * K + lm_swz(sr, lane & 7) * 8) * 2;
+  }
+
+  f32x16 acc[kVA][kLmNT];
+#pragma unroll
+  for (int a = 0; a < kVA; ++a)
+#pragma unroll
+    for (int t = 0; t < kLmNT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][t][r] = 0.f;
+
+  uint4 aw[kLmSlots][kVA][4];
+  // The loop issues loads ahead of their use; the issues that fall past this
+  // workgroup's K range (it == kPastEnd) take a per-lane offset beyond every
+  // buffer's num_records, so they return zeros without touching memory instead
+  // of fetching the next range's data.
+  constexpr int kOutOfRange = 0x7ffffff0;
+  // Iteration it contracts k-slab (it + rot) mod nit: the workgroups resident
+  // together start at different slabs of their tiles, so their streams do not all
+  // hit the same column range of the weight rows (and the same HBM channels) at
+  // once.
+  const int nit = kc / kLmKS;
+  const int rot = vt % nit;
+  auto slab = [&](int it) {   // global k-slab index (k0 is a multiple of 64)
+    const int r = it + rot;
+    return k0 / kLmKS + (r >= nit ? r - nit : r);
+  };
+  auto load_a = [&](uint4 (&dst)[kVA][4], int it) {
+    const bool past = it == kPastEnd;
+    // slab block of iteration it; run (a, s) of this wave, 16 B per lane
+    const int so = past ? 0 : slab(it) * kPkSlabBytes;
+#pragma unroll
+    for (int a = 0; a < kVA; ++a)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dst[a][s] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
+  };
+  auto load_o = [&](uint16_t* stage, int it) {
+    const bool past = it == kPastEnd;
+    const int ko = past ? 0 : slab(it) * kLmKS * 2;
+#pragma unroll
+    for (int j = 0; j < kLmBlocksPerWave; ++j) {
+      const int b = wave * kLmBlocksPerWave + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ores, (__attribute__((address_space(3))) void*)(stage + b * 512), 16,
+          past ? kOutOfRange : ooff[j], ko, 0, 0);
+    }
+  };
+  // 28 B fragments per iteration (k-step s major, row tile t minor), each feeding two
+  // MFMAs.  The LDS reads run kLmBAhead fragments ahead of their use; the
+  // scheduling groups pin that order (first kLmBAhead reads, then two MFMAs and one
+  // read at a time) so that the compiler does not sink the reads next to their use.
+  auto compute = [&](const uint4 (&w)[kVA][4], const uint16_t* stage) {
+    constexpr int NB = 4 * kLmNT;
+    const uint16_t* ob = stage + l32 * kLmKS;
+    const int sw = (l32 >> 1) & 7;
+    auto frag = [&](int j) {
+      const int s = j / kLmNT, t = j % kLmNT;
+      return *reinterpret_cast<const uint4*>(ob + t * 32 * kLmKS + (((2 * s + h) ^ sw) << 3));
+    };
+    uint4 bq[kLmBAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kLmBAhead; ++i) bq[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = i / kLmNT, t = i % kLmNT;
+      if (i + kLmBAhead < NB) bq[(i + kLmBAhead) % (kLmBAhead + 1)] = frag(i + kLmBAhead);
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, bq[i % (kLmBAhead + 1)]);
+#pragma unroll
+      for (int a = 0; a < kVA; ++a)
+        acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[a][s]), bfr,
+                                                            acc[a][t], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kLmBAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kVA, 0);      // MFMAs
+      if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  uint16_t* const stages[kLmSlots] = {st0, st1, st2, st3};
+
+  // Step U of the unrolled loop works on iteration it (it % 4 == U): wait until this
+  // wave's rows and weights of iteration it have landed (everything but the two
+  // newer iterations' loads), barrier so every wave's row blocks are in LDS and
+  // stage (U+3)%4 is no longer read, issue iteration it+3, compute iteration it.
+  auto step = [&](auto U_c, int it) {
+    constexpr int U = decltype(U_c)::value;
+    // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerIter));
+    lds_barrier();
+    load_o(stages[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: rows, then weights
+    load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(aw[U], stages[U]);
+  };
+  load_o(st0, 0);
+  load_a(aw[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_o(st1, 1);
+  load_a(aw[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_o(st2, 2);
+  load_a(aw[2], 2);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int it0 = 0; it0 < nit; it0 += kLmSlots) {
+    step(IntC<0>{}, it0);
+    step(IntC<1>{}, it0 + 1);
+    step(IntC<2>{}, it0 + 2);
+    step(IntC<3>{}, it0 + 3);
+  }
+  // the last three iterations' loads (past the end: zeros) must land before the
+  // workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if constexpr (kEpi == kEpiPartial || kEpi == kEpiPartialHalf || kSwiGLU) {
+    gemm_epilogue<kEpi, kVA>(acc, row0, rows, vbase, V, h, l32, ga);
+  } else if constexpr (kSample) {
+    sample_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, sa,
+                    red_v, red_i, reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_m),
+                    reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_s), static_cast<float4*>(part_out));
+  } else {
+    argmax_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, logits_out,
+                    red_v, red_i, static_cast<int2*>(part_out));
+  }
+}
+
 
 // fp32: thread per vocabulary column, 32 rows per workgroup, O staged in LDS.
 constexpr int kLmF32Rows = 32;
@@ -862,8 +875,17 @@ hipError_t launch_sample_reduce(void* ws, const LmPlan& plan, int rows, float* l
 namespace ssd {
 
 LmPlan gemm_plan(int rows, int N, bool swiglu) {
-  const int tile = swiglu ? kLmVT / kLmVA : kLmVT;
-  return plan_for(rows, (N + tile - 1) / tile);
+  if (swiglu) return plan_for(rows, (N + kLmVT / kLmVA - 1) / (kLmVT / kLmVA));
+  // A projection whose 256-row tiles fill fewer than half the CUs needs many
+  // K splits to keep every CU streaming, and each split writes a full tile of
+  // fp32 partial sums.  Half tiles (one A tile per wave) give twice the tiles,
+  // so half the splits and half the partial sums.
+  const int full = (N + kLmVT - 1) / kLmVT;
+  const int mchunks = (rows + kLmMC - 1) / kLmMC;
+  const bool half = full * mchunks < 128;
+  LmPlan p = plan_for(rows, half ? 2 * full : full);
+  p.half = half ? 1 : 0;
+  return p;
 }
 
 hipError_t launch_gemm(const void* rows_in, const void* w, int total_rows, int K, int N,
@@ -880,6 +902,11 @@ hipError_t launch_gemm(const void* rows_in, const void* w, int total_rows, int K
   const dim3 grid(plan.blocks, splits);
   if (swiglu)
     hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiSwiGLU>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
+                       K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
+                       plan.sv, plan.sm, SampleArgs{}, ga);
+  else if (plan.half)
+    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPartialHalf>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
                        K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
                        plan.sv, plan.sm, SampleArgs{}, ga);
