@@ -98,6 +98,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
   // candidate mask of this row: keys cw*D .. cw*D + cj (none for the anchor row)
   const int cw = r_row > 0 ? (r_row - 1) / D : -1;
   const int cj = r_row > 0 ? (r_row - 1) - cw * D : -1;
+  // Keys this row may see in this slot: [vis_lo, vis_hi] and below k1.  In the
+  // candidate slot that is its own candidate's keys cw*D .. cw*D + cj (an empty
+  // range for the anchor row); in a prefix slot, every key.
+  const int vis_lo = !cand ? 0 : (cw >= 0 ? cw * D : 1);
+  const int vis_hi = !cand ? INT_MAX : (cw >= 0 ? cw * D + cj : 0);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16s + 8h .. +7]
   bf16x8 qf[8];
@@ -205,12 +210,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          bool vis = key < k1;
-          if (cand) {
-            const int kw = key / D;
-            vis = vis && kw == cw && key - kw * D <= cj;
-          }
-          if (!vis) sacc[kt][r] = -INFINITY;
+          const bool vis = key < k1 && key >= vis_lo && key <= vis_hi;
+          sacc[kt][r] = vis ? sacc[kt][r] : -INFINITY;
           smax = fmaxf(smax, sacc[kt][r]);
         }
     }
