@@ -17,6 +17,11 @@ timed region) and the CPU oracle timed on the host on a bounded sample.
 measures the offline probe calibration instead: one pass is copy labels, probe
 logits at every position of every layer, and the per-layer F1 / AUC sweep with the
 layer choice, over a 32-layer, 4096-position, 4096-wide bf16 set.
+
+    python bench.py --scan [--steps K] [--warmup W]
+
+times kappa-gram retrieval alone over 2^24, 2^26 and 2^28 Zipf ids in contexts of
+16384 (every context scanned to its start unless W matches stop it earlier).
 """
 import argparse
 import json
@@ -53,6 +58,9 @@ def parse():
                         "Llama-3.1-8B layers (ssd_verify_forward) instead of the single-layer share")
     p.add_argument("--calibration", action="store_true",
                    help="time the offline probe calibration pass instead of the decoding step")
+    p.add_argument("--scan", action="store_true",
+                   help="time kappa-gram retrieval alone on large id arrays (2^24, 2^26, 2^28 ids "
+                        "in contexts of 16384) instead of the decoding step")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference point that scales the "
                         "HBM byte counters) and exit")
@@ -65,6 +73,8 @@ SAMPLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_bf16_kernel_sample.
 LM_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "lmhead.hip")
 CAL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probe_logits_kernel.calib_llama8b.traffic.txt")
 CAL_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "calib.hip")
+SCAN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kgram_kernel.scan_2e28.traffic.txt")
+SCAN_SOURCE = os.path.join(ROOT, "copy_draft_verification_amd", "csrc", "kgram.hip")
 
 
 def calibrate_copy():
@@ -304,6 +314,120 @@ def bench_calibration(a):
     print(json.dumps(line), flush=True)
 
 
+def scan_algorithmic(n, kappa, W, D, n_match, last_end, cand_len):
+    """Bytes the retrieval itself must move: each context's ids from the anchor back
+    to the start of the W-th match (all n when fewer than W matches exist), the
+    offsets, the gathered candidate ids, and the outputs."""
+    n = np.asarray(n, dtype=np.int64)
+    full = n_match >= W
+    scanned = np.where(full, n - last_end + kappa - 1, n)
+    B = len(n)
+    out = B * (4 * W + 4 + 4 * W * D + 4 * W + 1)
+    return int(4 * scanned.sum() + 4 * (B + 1) + 4 * int(cand_len.sum()) + out)
+
+
+def bench_scan(a):
+    """kappa-gram retrieval over many long contexts (the step's retrieval call alone,
+    every probe fired).  Each launch is timed with HIP events; between launches a
+    1 GiB buffer is overwritten (outside the timed launches) so that the ids come
+    from HBM, not from the 256 MB last-level cache."""
+    import torch
+    import copy_draft_verification_amd as cdv
+    import oracle
+    from workloads import SCAN_N, SCAN_SIZES, scan_ids_device
+
+    kappa, W, D = 5, 10, 20
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    rows = []
+    for total in SCAN_SIZES:
+        ids, cu = scan_ids_device(total, device=dev)
+        B = cu.numel() - 1
+        out = {"match_end": torch.empty(B, W, dtype=torch.int32, device=dev),
+               "n_match": torch.empty(B, dtype=torch.int32, device=dev),
+               "cand": torch.empty(B, W, D, dtype=torch.int32, device=dev),
+               "cand_len": torch.empty(B, W, dtype=torch.int32, device=dev),
+               "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev)}
+        print(f"[bench] scan total={total} B={B} n={SCAN_N} warmup={a.warmup} steps={a.steps}",
+              file=sys.stderr, flush=True)
+        for _ in range(a.warmup):
+            cdv.kgram_retrieve(ids, cu, kappa, W, D, out=out)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.steps)]
+        for e0, e1 in evs:
+            flush.zero_()
+            e0.record(stream)
+            cdv.kgram_retrieve(ids, cu, kappa, W, D, out=out)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+        nm = out["n_match"].cpu().numpy()
+        last = out["match_end"][:, W - 1].cpu().numpy().astype(np.int64)
+        byts = scan_algorithmic(np.full(B, SCAN_N), kappa, W, D, nm, last, out["cand_len"].cpu().numpy())
+        k_ms = float(ms.mean())
+        gbs = byts / (k_ms * 1e-3) / 1e9
+        rows.append({"ids": total, "contexts": B, "kernel_ms": round(k_ms, 4),
+                     "kernel_ms_median": round(float(np.median(ms)), 4),
+                     "algorithmic_bytes": byts, "GB/s": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "contexts_with_match": int((nm > 0).sum())})
+        print(f"[bench] scan total={total}: {k_ms:.4f} ms ({gbs:.0f} GB/s, "
+              f"{gbs / HBM_PEAK_GBS:.1%} of HBM), contexts with a match {int((nm > 0).sum())}",
+              file=sys.stderr, flush=True)
+        last_ids, last_cu, last_out = ids, cu, out
+        if total != SCAN_SIZES[-1]:
+            del ids, cu, out
+            torch.cuda.empty_cache()
+    top = rows[-1]
+    cpu = None
+    if not a.no_cpu_baseline:
+        # the oracle on whole contexts of the largest launch, as many as fit the budget
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        B = last_cu.numel() - 1
+        done, t_cpu = 0, 0.0
+        one = np.array([0, SCAN_N], dtype=np.int32)
+        while t_cpu < min(a.cpu_budget_s, 10.0) and done < B:
+            x = last_ids[done * SCAN_N:(done + 1) * SCAN_N].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.kgram_retrieve(x, one, kappa, W, D)
+            t_cpu += time.perf_counter() - t0
+            done += 1
+        per_launch = t_cpu / done * B
+        cpu = {"value": round(top["ids"] / per_launch / 1e9, 6), "unit": "Gids/s", "cores": 1,
+               "kind": "oracle",
+               "sample": (f"kappa-gram retrieval of {done} of the {B} contexts of {SCAN_N} ids "
+                          f"({t_cpu:.2f}s), scaled to the whole launch: {per_launch:.1f}s"),
+               "measured_s": round(t_cpu, 2)}
+    roof = {"bound": "hbm", "achieved": top["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": top["frac"],
+            "traffic": measured_traffic(f"scan_{top['ids']}", SCAN_TRAFFIC_FILE, SCAN_SOURCE),
+            "kernel": "kgram_kernel", "kernel_ms": top["kernel_ms"],
+            "algorithmic_bytes": top["algorithmic_bytes"]}
+    line = {
+        "metric": "kappa-gram retrieval: context ids scanned/sec (large-array sweep)",
+        "value": round(top["ids"] / (top["kernel_ms"] * 1e-3) / 1e9, 3),
+        "unit": "Gids/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": top["kernel_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": f"scan_{top['ids']}", "contexts": top["contexts"], "n": SCAN_N,
+                   "V": 128256, "zipf": 1.1, "kappa": kappa, "W": W, "D": D,
+                   "parallelism": "single-gpu"},
+        "sweep": rows,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_forward(a):
     """The copy step with the verification pass as a full target forward: probe ->
     kgram -> verify_forward (a.forward synthetic Llama-3.1-8B layers) -> accept.
@@ -425,6 +549,9 @@ def main():
         return
     if a.calibration:
         bench_calibration(a)
+        return
+    if a.scan:
+        bench_scan(a)
         return
     if a.forward > 0:
         bench_forward(a)

@@ -164,8 +164,10 @@ __device__ __forceinline__ bool real_row(int r, int D, const int32_t* cand_len_b
 
 // Exclusive prefix sum of v over a workgroup of NT threads (NT / 64 waves), in
 // thread order; `total` receives the sum.  s_wave holds NT / 64 ints of LDS.
-// Contains two __syncthreads(): every thread of the workgroup must call it.
-template <int NT>
+// Contains two workgroup barriers: every thread of the workgroup must call it.
+// With kLdsOnly the barriers order LDS only (lds_barrier), so global loads the
+// caller has in flight stay in flight across the scan.
+template <int NT, bool kLdsOnly = false>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int incl = v;
@@ -175,14 +177,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
     if (lane >= o) incl += t;
   }
   if (lane == kWave - 1) s_wave[wv] = incl;
-  __syncthreads();
+  if constexpr (kLdsOnly) lds_barrier(); else __syncthreads();
   int woff = 0, tot = 0;
   for (int i = 0; i < NT / kWave; ++i) {
     const int c = s_wave[i];
     if (i < wv) woff += c;
     tot += c;
   }
-  __syncthreads();
+  if constexpr (kLdsOnly) lds_barrier(); else __syncthreads();
   total = tot;
   return woff + incl - v;
 }

@@ -6,11 +6,15 @@
 //
 // One 1024-lane workgroup per sequence scans end positions from the newest
 // (n-2) backwards in chunks of 8192.  A chunk of ids (plus a kappa-1 halo) is
-// staged in LDS with coalesced loads; lane t tests positions top-8t .. top-8t-7,
-// so lane order equals recency order.  Matches are compacted in that order by a
-// workgroup prefix sum over per-lane counts, and the scan stops as soon as W
-// matches are known.  The candidate gather then copies L_w = min(D, n-1-p_w)
-// ids after each match.
+// copied from HBM straight into LDS by buffer-to-LDS loads, which hold no
+// registers while in flight; two LDS stages let the next chunk's loads run
+// while the current chunk is tested, and a context of up to two chunks is
+// entirely in flight at once.  The barriers of the loop order LDS only, which
+// leaves those loads outstanding.  Lane t tests positions top-8t .. top-8t-7
+// from its eight ids (two 16-byte LDS reads), so lane order equals recency
+// order.  Matches are compacted in that order by a workgroup prefix sum over
+// per-lane counts, and the scan stops as soon as W matches are known.  The
+// candidate gather then copies L_w = min(D, n-1-p_w) ids after each match.
 #include "common.h"
 #include "kernels.h"
 #include "switchsd.h"
@@ -18,58 +22,103 @@
 namespace ssd {
 
 constexpr int kKgThreads = 1024;
-constexpr int kKgPer = 8;
-constexpr int kKgChunk = kKgThreads * kKgPer;
+constexpr int kKgPer = 8;                              // end positions per lane and chunk
+constexpr int kKgChunk = kKgThreads * kKgPer;          // end positions per chunk
+// Staged ids per chunk: the chunk's end positions, the kappa-1 ids before the
+// oldest of them, and up to 3 more below those, so that the staged range starts
+// at a position congruent to top-7 (mod 4) and every lane's eight ids
+// (top-8t-7 .. top-8t) sit on a 16-byte boundary of LDS.
+constexpr int kKgStage = kKgChunk + (SSD_MAX_KAPPA - 1) + 3;
+constexpr int kKgLoads = (kKgStage + kKgThreads - 1) / kKgThreads;  // loads per lane and chunk (9)
+constexpr int kKgPad = 8;  // LDS slots before the staged ids (the lowest lane reads from 1 below)
+constexpr int kKgSlots = kKgPad + kKgLoads * kKgThreads;           // ints per LDS stage
+static_assert(kKgPad % 4 == 0 && kKgPad >= kKgPer - 1, "pad keeps 16-byte reads in the array");
+static_assert(kKgLoads <= 31, "vmcnt holds two chunks' loads");
 
-__global__ __launch_bounds__(kKgThreads) void kgram_kernel(
+// Two workgroups per CU (8 waves per SIMD, 2 x 72 KB of LDS): while one
+// compares, the other's loads are in flight.
+__global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_len, int kappa, int W, int D,
     const uint8_t* __restrict__ fire, int32_t* __restrict__ match_end, int32_t* __restrict__ n_match,
     int32_t* __restrict__ cand, int32_t* __restrict__ cand_len, uint8_t* __restrict__ copy_gate) {
-  __shared__ int s_ids[kKgChunk + SSD_MAX_KAPPA];
+  // two stages as two arrays: the compiler then knows which LDS a pending
+  // buffer-to-LDS load writes, and reads of the other stage need not wait for it
   __shared__ int s_suffix[SSD_MAX_KAPPA];
   __shared__ int s_list[SSD_MAX_W];
   __shared__ int s_wave[kKgThreads / kWave];
+  __shared__ __attribute__((aligned(16))) int st0[kKgSlots];
+  __shared__ __attribute__((aligned(16))) int st1[kKgSlots];
   const int b = blockIdx.x, t = threadIdx.x;
   const int base = cu_len[b];
   const int n = cu_len[b + 1] - base;
   const bool active = (fire == nullptr || fire[b] != 0) && n >= kappa + 1;
   int found = 0;
   if (active) {
-    if (t < kappa) s_suffix[t] = ids[base + n - kappa + t];
     const int lo = kappa - 1;
-    for (int top = n - 2; top >= lo && found < W; top -= kKgChunk) {
+    // the LDS destination of a buffer-to-LDS load (M0) must be wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    if (t < kappa) s_suffix[t] = ids[base + n - kappa + t];
+    // first staged position of the chunk whose newest end position is top
+    auto stage_lo = [&](int top) {
+      const int lbase = max(lo, top - kKgChunk + 1) - (kappa - 1);
+      return lbase - ((lbase - (top - (kKgPer - 1))) & 3);
+    };
+    // The sequence's ids as a buffer: loads past its last id return zero.  A
+    // staged position below 0 (at most 3 of them, lanes 0..2 of the first load)
+    // reads id 0 instead; positions below the halo are never compared.  Staged
+    // index i lands in stage slot kKgPad + i; every lane issues kKgLoads loads
+    // per chunk, so the wave's load count per chunk is fixed.
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(ids + base), 0, n * 4, kBufFlags);
+    // Loads of a chunk that does not exist (top < lo) are still issued, with an
+    // offset past the buffer: they return zeros without touching memory, and every
+    // chunk is followed by exactly kKgLoads loads of this wave, so one fixed wait
+    // count serves every chunk.
+    constexpr int kOutOfRange = 0x7ffffff0;
+    auto issue = [&](int* stage, int top) {
+      const bool past = top < lo;
+      const int i0 = past ? 0 : stage_lo(top) + t;
+#pragma unroll
+      for (int u = 0; u < kKgLoads; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            res, (__attribute__((address_space(3))) void*)(stage + kKgPad + u * kKgThreads + wave * kWave),
+            4, past ? kOutOfRange : u == 0 ? max(i0, 0) * 4 : (i0 + u * kKgThreads) * 4, 0, 0, 0);
+    };
+    // Test the chunk whose newest end position is top, staged in `stage`; false
+    // when the scan is over.  On return the stage may be reloaded (the scan ends
+    // with a barrier that follows every read of it).
+    auto chunk = [&](int* stage, int top) -> bool {
+      // this wave's loads of the chunk have landed (the next chunk's may not)...
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKgLoads));
+      // ...and every wave's
+      lds_barrier();
       const int cbeg = max(lo, top - kKgChunk + 1);
-      const int lbase = cbeg - kappa + 1;
-      const int cnt = top - lbase + 1;
-      // stage the chunk: every thread issues all of its loads before storing any
-      int tmp[kKgPer + 1];
-#pragma unroll
-      for (int u = 0; u <= kKgPer; ++u) {
-        const int i = t + u * kKgThreads;
-        tmp[u] = i < cnt ? ids[base + lbase + i] : 0;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u <= kKgPer; ++u) {
-        const int i = t + u * kKgThreads;
-        if (i < cnt) s_ids[i] = tmp[u];
-      }
-      __syncthreads();
+      const int abase = stage_lo(top);
+      const int s_last = s_suffix[kappa - 1];
+      const int s_prev = kappa >= 2 ? s_suffix[kappa - 2] : 0;
       unsigned mask = 0;
       const int p0 = top - t * kKgPer;
+      if (p0 >= cbeg) {
+        // ids of positions p0-7 .. p0; positions below cbeg are never matched
+        const int s0 = kKgPad + p0 - (kKgPer - 1) - abase;
+        const int4 ra = *reinterpret_cast<const int4*>(&stage[s0]);
+        const int4 rb = *reinterpret_cast<const int4*>(&stage[s0 + 4]);
+        const int v[kKgPer] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-      for (int i = 0; i < kKgPer; ++i) {
-        const int p = p0 - i;
-        if (p >= cbeg) {
-          bool m = true;
-          for (int qq = 0; qq < kappa; ++qq) {
-            if (s_ids[p - qq - lbase] != s_suffix[kappa - 1 - qq]) { m = false; break; }
+        for (int i = 0; i < kKgPer; ++i) {
+          const int p = p0 - i;  // its id is v[7 - i]
+          bool m = p >= cbeg && v[kKgPer - 1 - i] == s_last;
+          // the id before it is still in registers, except for the lane's oldest position
+          if (i < kKgPer - 1 && kappa >= 2) m = m && v[kKgPer - 2 - i] == s_prev;
+          if (m) {
+            for (int qq = i < kKgPer - 1 ? 2 : 1; qq < kappa; ++qq)
+              if (stage[kKgPad + p - qq - abase] != s_suffix[kappa - 1 - qq]) { m = false; break; }
           }
           if (m) mask |= 1u << i;
         }
       }
       int total;
-      int rank = found + block_excl_scan<kKgThreads>(__popc(mask), s_wave, total);
+      int rank = found + block_excl_scan<kKgThreads, true>(__popc(mask), s_wave, total);
       while (mask) {
         const int i = __ffs(mask) - 1;
         mask &= mask - 1;
@@ -77,7 +126,23 @@ __global__ __launch_bounds__(kKgThreads) void kgram_kernel(
         ++rank;
       }
       found += total;
+      const int nt = top - kKgChunk;
+      if (nt < lo || found >= W) return false;
+      issue(stage, nt - kKgChunk);
+      return true;
+    };
+    int top = n - 2;
+    issue(st0, top);
+    issue(st1, top - kKgChunk);
+    for (;;) {
+      if (!chunk(st0, top)) break;
+      top -= kKgChunk;
+      if (!chunk(st1, top)) break;
+      top -= kKgChunk;
     }
+    // a scan that stopped early may still have the next chunk's loads in
+    // flight: they must land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
   const int M = min(found, W);

@@ -13,10 +13,12 @@ the write-up's CopyDiversity table (§2.2: 10.6 / 11.7 / 77.7 %) and the copy
 trigger rates of its Table 1 set the planted-repeat densities; no dataset item
 of any benchmark is used.
 """
-from .gen import (CALIB_CONFIGS, CONFIGS, FWD_CONFIGS, CalibWorkload, FwdWorkload, Workload,
-                  f32_to_bf16_bits, generate, generate_calibration, generate_forward,
-                  generate_with_ids, spec, to_torch)
+from .gen import (CALIB_CONFIGS, CONFIGS, FWD_CONFIGS, SCAN_N, SCAN_SIZES, CalibWorkload,
+                  FwdWorkload, Workload, f32_to_bf16_bits, generate, generate_calibration,
+                  generate_forward, generate_with_ids, scan_ids_device, scan_ids_planted, spec,
+                  to_torch)
 
 __all__ = ["CALIB_CONFIGS", "CONFIGS", "FWD_CONFIGS", "CalibWorkload", "FwdWorkload", "Workload",
            "f32_to_bf16_bits", "generate", "generate_calibration", "generate_forward",
-           "generate_with_ids", "spec", "to_torch"]
+           "generate_with_ids", "SCAN_N", "SCAN_SIZES", "scan_ids_device", "scan_ids_planted",
+           "spec", "to_torch"]

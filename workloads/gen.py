@@ -531,3 +531,68 @@ def generate_forward(name, n_layers=None, **overrides):
                        _normal(seed, "lm", (s.V, hid), 1.0, "bf16", sub=1),
                        layers, norm_w(3, 0),
                        _normal(seed, "lm", (s.V, hid), 1.0 / np.sqrt(hid), "bf16", sub=2))
+
+
+# ---------------------------------------------------------------- large-array kappa-gram scan
+# Many long contexts of Zipf ids, scanned whole: the retrieval step's throughput
+# regime.  The contexts have no planted repeats, so the anchor's kappa-gram almost
+# never occurs earlier and every scan reads its whole context (the case in which
+# the probe fires but the dual gate closes).
+SCAN_SIZES = (1 << 24, 1 << 26, 1 << 28)   # ids per launch
+SCAN_N = 16384                             # ids per context
+SCAN_V, SCAN_ZIPF, SCAN_SEED = 128256, 1.1, 4001
+
+
+def _zipf_cdf(V, zipf):
+    ranks = np.arange(1, V + 1, dtype=np.float64)
+    cdf = np.cumsum(ranks ** (-zipf))
+    return cdf / cdf[-1]
+
+
+def scan_ids_device(total, n=SCAN_N, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, device="cuda"):
+    """`total` Zipf(zipf) ids over V ranks, drawn on `device` by torch's seeded
+    generator (inverse CDF, as in the host generator), as total / n contexts of
+    n ids.  Returns (ids int32 [total], cu_len int32 [total / n + 1])."""
+    import torch
+    assert total % n == 0
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    cdf = torch.from_numpy(_zipf_cdf(V, zipf).astype(np.float32)).to(device)
+    ids = torch.empty(total, dtype=torch.int32, device=device)
+    step = 1 << 26
+    for s0 in range(0, total, step):
+        e = min(total, s0 + step)
+        u = torch.rand(e - s0, generator=g, device=device, dtype=torch.float32)
+        ids[s0:e] = torch.searchsorted(cdf, u, right=True, out_int32=True).clamp_(max=V - 1)
+    B = total // n
+    cu = torch.arange(0, B + 1, dtype=torch.int32, device=device) * n
+    return ids, cu
+
+
+def scan_ids_planted(ns, kappa=KAPPA, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, max_occ=14):
+    """Host contexts for scan parity: one context of Zipf ids per length in `ns`,
+    in which the anchor's kappa-gram is copied to 0..max_occ earlier end
+    positions, spread over the whole context, some placed right at or across
+    multiples of 8192 (powers of two are natural chunk boundaries for a scan).
+    Returns (ids int32 [sum(ns)], cu_len int32 [len(ns) + 1])."""
+    cdf = _zipf_cdf(V, zipf)
+    out = []
+    for b, n in enumerate(ns):
+        rng = _rng(seed, 13, b)
+        x = np.minimum(np.searchsorted(cdf, rng.random(n), side="right"), V - 1).astype(np.int32)
+        suffix = x[n - kappa:].copy()
+        occ = int(rng.integers(0, max_occ + 1)) if n >= 2 * kappa + 2 else 0
+        ends = set()
+        for _ in range(occ):
+            if rng.random() < 0.3:   # near a power-of-two boundary
+                p = int(rng.integers(1, max(2, n // 8192 + 1))) * 8192 + int(rng.integers(-kappa, kappa + 1))
+            else:
+                p = int(rng.integers(kappa - 1, n - 1))
+            if kappa - 1 <= p <= n - 2 - kappa:   # keep the suffix itself intact
+                ends.add(p)
+        for p in sorted(ends):
+            x[p - kappa + 1:p + 1] = suffix
+        out.append(x)
+    cu = np.zeros(len(ns) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(ns)
+    return np.concatenate(out), cu
