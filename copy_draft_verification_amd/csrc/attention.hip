@@ -46,9 +46,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
     const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
-    const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int Hkv, int W, int D,
-    int nsplit, int chunk, int qtiles, float scale_log2, float* __restrict__ ws_m,
-    float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ cand_len, int B, int R,
+    int Hq, int Hkv, int W, int D, int nsplit, int chunk, int qtiles, float scale_log2,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kAttD * kKB];
 
@@ -95,6 +95,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
   const int i_row = qtile * kAttRowsPerBlock + wave * 32 + l32;  // this lane's query row (B operand column)
   const bool row_ok = i_row < G;
   const int r_row = row_ok ? i_row / g : 0, hh = row_ok ? i_row - (i_row / g) * g : 0;
+  // A tile whose rows are all padding (candidates past M, tokens past L_w) has
+  // nothing to contribute: the merge reads partials of real rows only.
+  if (!__syncthreads_or(row_ok && real_row(r_row, D, cand_len + static_cast<size_t>(b) * W, true)))
+    return;
   // candidate mask of this row: keys cw*D .. cw*D + cj (none for the anchor row)
   const int cw = r_row > 0 ? (r_row - 1) / D : -1;
   const int cj = r_row > 0 ? (r_row - 1) - cw * D : -1;
@@ -506,7 +510,7 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pre),
                        static_cast<const uint16_t*>(v_pre), cu_len,
                        static_cast<const uint16_t*>(k_cand), static_cast<const uint16_t*>(v_cand),
-                       copy_gate, B, R, Hq, Hkv, W, D, plan.nsplit, plan.chunk, plan.qtiles,
+                       copy_gate, cand_len, B, R, Hq, Hkv, W, D, plan.nsplit, plan.chunk, plan.qtiles,
                        scale_log2, ws_m, ws_l, ws_o);
     hipLaunchKernelGGL(attn_merge_bf16_kernel, mgrid, dim3(256), 0, s, cu_len, cand_len, copy_gate,
                        B, R, Hq, W, D, plan.nsplit, plan.chunk, ws_m, ws_l, ws_o,
