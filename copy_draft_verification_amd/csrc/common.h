@@ -132,6 +132,10 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float om, float o
 // swizzle, offset addressing): loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;
 
+// Cache-policy operand of the buffer load builtins: the nontemporal bit, for data
+// streamed once from HBM.
+constexpr int kNonTemporal = 2;
+
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
 // operations of this wave are outstanding; the other counters are not waited on.
 constexpr int waitcnt_vm(int n) {

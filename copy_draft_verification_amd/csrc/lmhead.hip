@@ -320,7 +320,11 @@ __device__ __forceinline__ void argmax_epilogue(
   }
 }
 
-template <int kEpi>
+// kOnce: every weight of the launch is read by one workgroup only (a single row
+// chunk), so the weight loads carry the nontemporal hint, which streams faster
+// from HBM; with several row chunks the chunks of one tile share it through L2,
+// and the default policy keeps it there.
+template <int kEpi, bool kOnce>
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
     const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       for (int s = 0; s < 4; ++s)
         dst[a][s] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, 0));
+                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, kOnce ? kNonTemporal : 0));
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
@@ -803,6 +807,16 @@ size_t lm_workspace_bytes(const LmPlan& p, int rows) {
   return 256 + 2 * al256(sizeof(int32_t) * rows) + static_cast<size_t>(p.vtiles) * rows * sizeof(float4);
 }
 
+// Launch the bf16 kernel with epilogue kEpi; the nontemporal weight loads when the
+// launch has one row chunk.
+template <int kEpi, typename... Args>
+static void launch_bf16(const LmPlan& plan, dim3 grid, hipStream_t s, Args... args) {
+  if (plan.mchunks == 1)
+    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, true>), grid, dim3(256), 0, s, args...);
+  else
+    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, false>), grid, dim3(256), 0, s, args...);
+}
+
 hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
                                const uint8_t* copy_gate, hipStream_t s) {
   const LmWs w = lm_ws(ws, rows);
@@ -818,12 +832,12 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   const LmWs w = lm_ws(ws, rows);
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (bf16 && sample)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiSample>, dim3(plan.blocks), dim3(256), 0, s,
+    launch_bf16<kEpiSample>(plan, dim3(plan.blocks), s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
                        rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
                        plan.vtiles, plan.mchunks, plan.sv, plan.sm, *sample, GemmArgs{});
   else if (bf16)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiArgmax>, dim3(plan.blocks), dim3(256), 0, s,
+    launch_bf16<kEpiArgmax>(plan, dim3(plan.blocks), s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
                        rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
                        plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{}, GemmArgs{});
@@ -901,17 +915,17 @@ hipError_t launch_gemm(const void* rows_in, const void* w, int total_rows, int K
   ga.row_list = lw.row_list;
   const dim3 grid(plan.blocks, splits);
   if (swiglu)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiSwiGLU>, grid, dim3(256), 0, s,
+    launch_bf16<kEpiSwiGLU>(plan, grid, s,
                        static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
                        K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
                        plan.sv, plan.sm, SampleArgs{}, ga);
   else if (plan.half)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPartialHalf>, grid, dim3(256), 0, s,
+    launch_bf16<kEpiPartialHalf>(plan, grid, s,
                        static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
                        K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
                        plan.sv, plan.sm, SampleArgs{}, ga);
   else
-    hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPartial>, grid, dim3(256), 0, s,
+    launch_bf16<kEpiPartial>(plan, grid, s,
                        static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w), total_rows,
                        K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles, plan.mchunks,
                        plan.sv, plan.sm, SampleArgs{}, ga);
@@ -928,7 +942,7 @@ hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate_up, int tota
   ga.part_rows = total_rows;
   ga.ld = 2 * N;
   ga.row_list = lw.row_list;
-  hipLaunchKernelGGL(lmhead_bf16_kernel<kEpiPair>, dim3(plan.blocks, splits), dim3(256), 0, s,
+  launch_bf16<kEpiPair>(plan, dim3(plan.blocks, splits), s,
                      static_cast<const uint16_t*>(rows_in), static_cast<const uint16_t*>(w_gate_up),
                      total_rows, K, N, lw.row_list, lw.n_rows, nullptr, nullptr, plan.vtiles,
                      plan.mchunks, plan.sv, plan.sm, SampleArgs{}, ga);
