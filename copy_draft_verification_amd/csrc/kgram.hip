@@ -35,6 +35,25 @@ constexpr int kKgSlots = kKgPad + kKgLoads * kKgThreads;           // ints per L
 static_assert(kKgPad % 4 == 0 && kKgPad >= kKgPer - 1, "pad keeps 16-byte reads in the array");
 static_assert(kKgLoads <= 31, "vmcnt holds two chunks' loads");
 
+// LDS reads of the stages, written as asm that waits for its own result.  The
+// compiler cannot tell which LDS a pending buffer-to-LDS copy writes, so before a
+// plain read of one stage it would wait for every copy in flight, the other
+// stage's included; the stage being read has already been waited for (fixed
+// wait count + barrier).
+using i32x4 = __attribute__((ext_vector_type(4))) int;
+__device__ __forceinline__ uint32_t lds_addr(const int* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) int*)p));
+}
+__device__ __forceinline__ int lds_ld(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_ld8(const int* p, i32x4& a, i32x4& b) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(a), "=v"(b) : "v"(lds_addr(p)) : "memory");
+}
+
 // Two workgroups per CU (8 waves per SIMD, 2 x 72 KB of LDS): while one
 // compares, the other's loads are in flight.
 __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
@@ -78,14 +97,18 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     // chunk is followed by exactly kKgLoads loads of this wave, so one fixed wait
     // count serves every chunk.
     constexpr int kOutOfRange = 0x7ffffff0;
+    // Slots past the chunk's staged count (ids above top, which the previous chunk
+    // already read) take the out-of-range offset too: no memory is touched.
     auto issue = [&](int* stage, int top) {
       const bool past = top < lo;
-      const int i0 = past ? 0 : stage_lo(top) + t;
+      const int abase = past ? 0 : stage_lo(top);
+      const int i0 = abase + t, room = past ? 0 : top - abase + 1 - t;
 #pragma unroll
       for (int u = 0; u < kKgLoads; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             res, (__attribute__((address_space(3))) void*)(stage + kKgPad + u * kKgThreads + wave * kWave),
-            4, past ? kOutOfRange : u == 0 ? max(i0, 0) * 4 : (i0 + u * kKgThreads) * 4, 0, 0, kNonTemporal);
+            4, u * kKgThreads >= room ? kOutOfRange : u == 0 ? max(i0, 0) * 4 : (i0 + u * kKgThreads) * 4,
+            0, 0, kNonTemporal);
     };
     // Test the chunk whose newest end position is top, staged in `stage`; false
     // when the scan is over.  On return the stage may be reloaded (the scan ends
@@ -104,8 +127,8 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
       if (p0 >= cbeg) {
         // ids of positions p0-7 .. p0; positions below cbeg are never matched
         const int s0 = kKgPad + p0 - (kKgPer - 1) - abase;
-        const int4 ra = *reinterpret_cast<const int4*>(&stage[s0]);
-        const int4 rb = *reinterpret_cast<const int4*>(&stage[s0 + 4]);
+        i32x4 ra, rb;
+        lds_ld8(stage + s0, ra, rb);
         const int v[kKgPer] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
         for (int i = 0; i < kKgPer; ++i) {
@@ -115,7 +138,7 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
           if (i < kKgPer - 1 && kappa >= 2) m = m && v[kKgPer - 2 - i] == s_prev;
           if (m) {
             for (int qq = i < kKgPer - 1 ? 2 : 1; qq < kappa; ++qq)
-              if (stage[kKgPad + p - qq - abase] != s_suffix[kappa - 1 - qq]) { m = false; break; }
+              if (lds_ld(stage + kKgPad + p - qq - abase) != s_suffix[kappa - 1 - qq]) { m = false; break; }
           }
           if (m) mask |= 1u << i;
         }
