@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--workload", default="llama8b_b1")
     p.add_argument("--anchor", default=None, choices=("full", "natural"),
                    help="anchor mode of the synthetic contexts (default: the workload's own)")
+    p.add_argument("--W", type=int, default=None, help="candidates per sequence (default: the workload's)")
+    p.add_argument("--D", type=int, default=None, help="tokens per candidate (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--temperature", type=float, default=0.0,
@@ -560,7 +562,8 @@ def main():
     import copy_draft_verification_amd as cdv
     from workloads import generate, to_torch
 
-    wl = generate(a.workload, **({"anchor": a.anchor} if a.anchor else {}))
+    over = {k: v for k, v in (("anchor", a.anchor), ("W", a.W), ("D", a.D)) if v is not None}
+    wl = generate(a.workload, **over)
     s = wl.spec
     dev = "cuda:0"
     up = lambda x: to_torch(x, dev)  # noqa: E731
