@@ -60,8 +60,7 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_len, int kappa, int W, int D,
     const uint8_t* __restrict__ fire, int32_t* __restrict__ match_end, int32_t* __restrict__ n_match,
     int32_t* __restrict__ cand, int32_t* __restrict__ cand_len, uint8_t* __restrict__ copy_gate) {
-  // two stages as two arrays: the compiler then knows which LDS a pending
-  // buffer-to-LDS load writes, and reads of the other stage need not wait for it
+  // the two stages, read through the asm helpers above
   __shared__ int s_suffix[SSD_MAX_KAPPA];
   __shared__ int s_list[SSD_MAX_W];
   __shared__ int s_wave[kKgThreads / kWave];
