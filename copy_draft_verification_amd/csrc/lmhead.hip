@@ -456,10 +456,11 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // MFMA stream: one load after each MFMA pair from pair kLmIssueAt on, so that the
   // first MFMAs after the barrier wait only on their own B fragments, and the loads'
   // issue slots fall under MFMAs already in the matrix pipeline.  That makes the
-  // greedy LM head 7-9% faster (batch 1 and batch 32).  The sampling epilogue is
-  // 3-4% slower with it, and the projections of the forward (8 to 32 iterations per
-  // workgroup) up to 1.5% slower, so they issue their loads before the MFMAs.
-  constexpr bool kInterleave = kEpi == kEpiArgmax;
+  // greedy LM head 7-9% faster (batch 1 and batch 32) and the gate / up projection
+  // 8% faster.  The sampling epilogue is 3-4% slower with it, and the split-K
+  // projections on half tiles are slower too, so they issue their loads before the
+  // MFMAs.
+  constexpr bool kInterleave = kEpi == kEpiArgmax || kEpi == kEpiPair;
   auto compute = [&](const uint4 (&w)[kVA][4], const uint16_t* stage, auto&& issue_next) {
     constexpr int NB = 4 * kLmNT;
     static_assert(kLmIssueAt + kLoadsPerIter <= NB, "the loads fit between the MFMA pairs");
