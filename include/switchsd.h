@@ -118,6 +118,9 @@ ssd_status_t ssd_probe_score(const void* h, ssd_dtype_t h_dtype, const float* w,
  *   copy_gate [B] uint8 = fired && M > 0
  * Errors: INVALID_ARG for null pointers (fire excepted), B < 1,
  *   kappa not in [1, SSD_MAX_KAPPA], W not in [1, SSD_MAX_W], D not in [1, SSD_MAX_D].
+ * Data contract (device-side, not checked): cu_len is non-decreasing and every
+ *   context holds fewer than 2^29 - 2^14 ids (byte offsets inside a context are
+ *   32-bit).
  */
 ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32_t B,
                                 int32_t kappa, int32_t W, int32_t D, const uint8_t* fire,
