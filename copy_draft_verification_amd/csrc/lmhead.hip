@@ -52,7 +52,7 @@ constexpr int kLmBlocksPerWave = kLmBlocks / kLmWaves;  // 7
 constexpr int kLmSlots = 4;                       // weight register slots = LDS stages
 constexpr int kLmKAlign = kLmKS * kLmSlots;       // the hidden size must be a multiple of this
 constexpr int kLmBAhead = 4;                      // LDS reads of B fragments in flight
-constexpr int kLmIssueAt = 4;                     // MFMA pair after which the next loads start
+constexpr int kLmIssueAt = 4;                     // MFMA pair after which the next loads start (full tiles)
 constexpr int kLmXcds = 8;                        // XCDs; workgroups are dealt round-robin
 constexpr int kLmXcdSlots = 32;                   // concurrent workgroups per XCD (one per CU)
 constexpr int kPastEnd = -1;                      // iteration index of a load past the K range
@@ -456,14 +456,16 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // MFMA stream: one load after each MFMA pair from pair kLmIssueAt on, so that the
   // first MFMAs after the barrier wait only on their own B fragments, and the loads'
   // issue slots fall under MFMAs already in the matrix pipeline.  That makes the
-  // greedy LM head 7-9% faster (batch 1 and batch 32) and the gate / up projection
-  // 8% faster.  The sampling epilogue is 3-4% slower with it, and the split-K
-  // projections on half tiles are slower too, so they issue their loads before the
-  // MFMAs.
-  constexpr bool kInterleave = kEpi == kEpiArgmax || kEpi == kEpiPair;
+  // greedy LM head 7-9% faster (batch 1 and batch 32), the gate / up projection 8%
+  // and the split-K projections on half tiles 3-4% faster, the latter with the
+  // loads starting after pair 10 (their 11 loads per iteration against 14 MFMA
+  // pairs; after pair 4 they were slower).  The sampling epilogue is 3-4% slower
+  // with it, so it issues its loads before the MFMAs.
+  constexpr bool kInterleave = kEpi == kEpiArgmax || kEpi == kEpiPair || kEpi == kEpiPartialHalf;
+  constexpr int kIssueAt = kEpi == kEpiPartialHalf ? 10 : kLmIssueAt;
   auto compute = [&](const uint4 (&w)[kVA][4], const uint16_t* stage, auto&& issue_next) {
     constexpr int NB = 4 * kLmNT;
-    static_assert(kLmIssueAt + kLoadsPerIter <= NB, "the loads fit between the MFMA pairs");
+    static_assert(kIssueAt + kLoadsPerIter <= NB, "the loads fit between the MFMA pairs");
     const uint16_t* ob = stage + l32 * kLmKS;
     const int sw = (l32 >> 1) & 7;
     auto frag = [&](int j) {
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s = i / kLmNT, t = i % kLmNT;
-      if (kInterleave && i == kLmIssueAt) issue_next();
+      if (kInterleave && i == kIssueAt) issue_next();
       if (i + kLmBAhead < NB) bq[(i + kLmBAhead) % (kLmBAhead + 1)] = frag(i + kLmBAhead);
       const bf16x8 bfr = __builtin_bit_cast(bf16x8, bq[i % (kLmBAhead + 1)]);
 #pragma unroll
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     for (int i = 0; i < NB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, kVA, 0);      // MFMAs
       if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kInterleave && i >= kLmIssueAt && i < kLmIssueAt + kLoadsPerIter)
+      if (kInterleave && i >= kIssueAt && i < kIssueAt + kLoadsPerIter)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // a global load
     }
   };
