@@ -116,9 +116,10 @@ def measured_traffic(workload, path=TRAFFIC_FILE, source=LM_SOURCE):
 
 def lm_algorithmic(s, R_tot):
     """LM-head work the method itself needs: the weights once, the real rows in,
-    one int per row out; 2 flops per weight per real row."""
+    one int per row out; 2 flops per weight per real row.  With no real row (every
+    gate closed) there is nothing to contract and nothing to read."""
     elt = 2 if s.dtype == "bf16" else 4
-    byts = s.V * s.hid * elt + R_tot * s.hid * elt + 4 * R_tot
+    byts = (s.V * s.hid * elt + R_tot * s.hid * elt + 4 * R_tot) if R_tot > 0 else 0
     flops = 2.0 * R_tot * s.hid * s.V
     return byts, flops
 
@@ -662,7 +663,12 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(tflops / mfma_peak, 4)}
-    roof.update({"traffic": measured_traffic(s.name, SAMPLE_TRAFFIC_FILE if T > 0 else TRAFFIC_FILE),
+    # the committed counters were taken on the workload's own full anchors and W, D
+    from workloads import spec as base_spec
+    b0 = base_spec(s.name)
+    same = (s.anchor, s.W, s.D) == (b0.anchor, b0.W, b0.D)
+    roof.update({"traffic": measured_traffic(s.name, SAMPLE_TRAFFIC_FILE if T > 0 else TRAFFIC_FILE)
+                 if same else None,
                  "kernel": ("lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel") +
                            ("<sample>" if T > 0 else ""),
                  "kernel_ms": round(lm_ms, 4), "algorithmic_bytes": int(lm_bytes),
