@@ -176,6 +176,7 @@ constexpr int kPlThreads = 512;
 constexpr int kPlRowsPerWave = 16;
 constexpr int kPlRows = kPlRowsPerWave * (kPlThreads / kWave);   // rows per workgroup
 constexpr int kPlUnroll = 8;                                     // 16-byte loads in flight per lane
+constexpr int kPlFastHid = kWave * kPlUnroll * 8;                // widest row of one round of loads
 
 template <typename T>
 __global__ __launch_bounds__(kPlThreads) void probe_logits_kernel(const T* __restrict__ h,
@@ -185,10 +186,71 @@ __global__ __launch_bounds__(kPlThreads) void probe_logits_kernel(const T* __res
   extern __shared__ __align__(16) float s_w[];
   const int l = blockIdx.y;
   const float* wl = w + static_cast<size_t>(l) * hid;
-  for (int k = threadIdx.x; k < hid; k += kPlThreads) s_w[k] = wl[k];
+  // zero past hid up to kPlFastHid, so that the lanes of the fast path that load
+  // past a row (zeros) add exactly 0
+  for (int k = threadIdx.x; k < max(hid, kPlFastHid); k += kPlThreads) s_w[k] = k < hid ? wl[k] : 0.f;
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const T* hl = h + static_cast<size_t>(l) * N * hid;
+  if ((hid & 7) == 0 && hid <= kPlFastHid) {
+    // A row is one round of loads: the next row's loads are issued before this
+    // row's FMAs, so each wave keeps a row in flight while it computes.  Each row
+    // is read as a buffer of hid elements: every lane issues all kPlUnroll loads,
+    // those past the row return zeros, and no load sits behind a lane-dependent
+    // branch (which would make the compiler wait for every load in flight
+    // before any FMA).
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto row_u = [&](int m) {
+      return static_cast<long long>(blockIdx.x) * kPlRows + m * (kPlThreads / kWave) + wvu;
+    };
+    // Row r >= N (there is no next row) is issued too, as a buffer of size 0:
+    // its loads return zeros without touching memory, and every row is followed
+    // by the same number of loads, so the compiler's wait before the FMAs
+    // leaves the next row's loads in flight.
+    auto load_row = [&](Chunk8<T> (&dst)[kPlUnroll], long long r) {
+      const bool ok = r < N;
+      const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<T*>(hl + (ok ? static_cast<size_t>(r) * hid : 0)), 0,
+          ok ? hid * static_cast<int>(sizeof(T)) : 0, kBufFlags);
+#pragma unroll
+      for (int u = 0; u < kPlUnroll; ++u)
+        dst[u].template load_buf<kNonTemporal>(res, (u * kWave + lane) * 8 * static_cast<int>(sizeof(T)));
+    };
+    // Row m computes from one buffer while row m+1 loads into the other; the
+    // loop is unrolled by two so that the buffers swap roles without a copy (a
+    // register copy would wait for the loads in flight).
+    auto row = [&](int m, const Chunk8<T> (&cur)[kPlUnroll], Chunk8<T> (&nxt)[kPlUnroll]) -> bool {
+      const long long r = row_u(m);
+      if (r >= N) return false;
+      load_row(nxt, m + 1 < kPlRowsPerWave ? row_u(m + 1) : N);
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < kPlUnroll; ++u) {
+        const int c = u * kWave + lane;
+        const float4 w0 = reinterpret_cast<const float4*>(s_w)[2 * c];
+        const float4 w1 = reinterpret_cast<const float4*>(s_w)[2 * c + 1];
+        acc = fmaf(w0.x, cur[u].at(0), acc);
+        acc = fmaf(w0.y, cur[u].at(1), acc);
+        acc = fmaf(w0.z, cur[u].at(2), acc);
+        acc = fmaf(w0.w, cur[u].at(3), acc);
+        acc = fmaf(w1.x, cur[u].at(4), acc);
+        acc = fmaf(w1.y, cur[u].at(5), acc);
+        acc = fmaf(w1.z, cur[u].at(6), acc);
+        acc = fmaf(w1.w, cur[u].at(7), acc);
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) z[static_cast<size_t>(l) * N + r] = acc;
+      return true;
+    };
+    static_assert(kPlRowsPerWave % 2 == 0, "rows come in pairs");
+    Chunk8<T> b0[kPlUnroll], b1[kPlUnroll];
+    load_row(b0, row_u(0));
+    for (int m = 0; m < kPlRowsPerWave; m += 2) {
+      if (!row(m, b0, b1)) break;
+      if (!row(m + 1, b1, b0)) break;
+    }
+    return;
+  }
   for (int m = 0; m < kPlRowsPerWave; ++m) {
     const long long r = static_cast<long long>(blockIdx.x) * kPlRows + m * (kPlThreads / kWave) + wv;
     if (r >= N) break;
@@ -231,7 +293,7 @@ __global__ __launch_bounds__(kPlThreads) void probe_logits_kernel(const T* __res
 hipError_t launch_probe_logits(const void* h, bool bf16, const float* w, int L, long long N,
                                int hid, float* z, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((N + kPlRows - 1) / kPlRows), L);
-  const size_t lds = static_cast<size_t>(hid) * sizeof(float);
+  const size_t lds = static_cast<size_t>(std::max(hid, kPlFastHid)) * sizeof(float);
   if (bf16)
     hipLaunchKernelGGL(probe_logits_kernel<uint16_t>, grid, dim3(kPlThreads), lds, s,
                        static_cast<const uint16_t*>(h), w, N, hid, z);

@@ -60,6 +60,11 @@ template <> struct Chunk8<uint16_t> {
     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     v = make_uint4(t.x, t.y, t.z, t.w);
   }
+  // Buffer load: an offset past the buffer's size returns zeros.
+  template <int kPolicy>
+  __device__ void load_buf(__amdgpu_buffer_rsrc_t res, int off) {
+    v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, off, 0, kPolicy));
+  }
   __device__ float at(int e) const {
     const uint32_t w = (&v.x)[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -76,6 +81,11 @@ template <> struct Chunk8<float> {
     const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
     a = make_float4(x[0], x[1], x[2], x[3]);
     b = make_float4(y[0], y[1], y[2], y[3]);
+  }
+  template <int kPolicy>
+  __device__ void load_buf(__amdgpu_buffer_rsrc_t res, int off) {
+    a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(res, off, 0, kPolicy));
+    b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(res, off + 16, 0, kPolicy));
   }
   __device__ float at(int e) const { return e < 4 ? (&a.x)[e] : (&b.x)[e - 4]; }
 };

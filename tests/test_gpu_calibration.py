@@ -3,10 +3,11 @@ threshold / AUC sweep and layer choice) against the float64 oracle.
 
 Bars:
 * labels: bit-exact.
-* probe logits: |z_gpu - z| <= (ceil(hid / 64) + 8) * 2^-24 * sum_k |w_k h_k|.  Each lane
-  runs one fused multiply-add chain over hid / 64 products, then six shuffle adds: a
-  recursive sum of at most hid / 64 + 7 rounded steps, whose error is bounded by that
-  many unit roundoffs times the sum of magnitudes.
+* probe logits: |z_gpu - z| <= (c + 7) * 2^-24 * sum_k |w_k h_k|.  Each lane runs one
+  fused multiply-add chain over c products, then six shuffle adds: a recursive sum of at
+  most c + 7 rounded steps, whose error is bounded by that many unit roundoffs times the
+  sum of magnitudes.  A lane takes every 64th element (c = ceil(hid / 64)), or, when
+  hid % 8 == 0, every 64th group of eight (c = 8 * ceil(hid / 512), e.g. 16 at hid = 520).
 * sweep: run on the GPU's own fp32 scores, the oracle (float64, exact on those values)
   must give the same threshold, TP / FP / FN / P and 2U exactly, the same layer; AUC and
   tau within the rounding of a double to float.
@@ -117,7 +118,8 @@ def _logit_bound(H, w, dtype):
     Hd = oracle.bf16_bits_to_f64(H) if dtype == "bf16" else np.asarray(H, np.float64)
     mag = np.einsum("lnk,lk->ln", np.abs(Hd), np.abs(np.asarray(w, np.float64)))
     hid = H.shape[-1]
-    return (math.ceil(hid / 64) + 8) * 2.0 ** -24 * mag
+    chain = 8 * math.ceil(hid / 512) if hid % 8 == 0 else math.ceil(hid / 64)
+    return (chain + 7) * 2.0 ** -24 * mag
 
 
 def _check_logits(H, w, dtype, z_gpu):
@@ -137,9 +139,11 @@ def test_probe_logits_small(name):
     print(f"[ok] max err/tol {r:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("hid", [1, 7, 13, 520, 16384])
+@pytest.mark.parametrize("hid", [1, 7, 13, 8, 520, 1000, 4096, 4104, 16384])
 def test_probe_logits_odd_hidden(hid):
-    # hid % 8 != 0 takes the per-element path; 16384 fills the LDS copy of w
+    # hid % 8 != 0 takes the per-element path; hid % 8 == 0 up to 4096 the one-round,
+    # next-row-prefetch path (rows shorter than a round read zeros past their end);
+    # 4104 and 16384 the multi-round path; 16384 fills the LDS copy of w
     c = generate_calibration("calib_small_f32", hid=hid, L=2, B=1, n=(97, 97))
     _case(f"logits hid={hid} H={c.H.shape}")
     _check_logits(c.H, c.w, "f32", host(cdv.probe_logits(up(c.H), up(c.w))))
