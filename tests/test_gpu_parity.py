@@ -62,6 +62,14 @@ def test_bf16_chain_other_candidate_shapes(W, D):
     assert st["att_rows"] > 0
 
 
+def test_bf16_chain_many_key_splits():
+    # one sequence whose rows fit one tile of one KV head: the 12000-token context is
+    # cut into 23 key splits (21 of them hold keys), more slots than the merge loads
+    # at once, so its running (max, sum, output) is carried across load groups
+    st = _chain(generate("small_bf16", B=1, n=(12000, 12000), W=1, D=20, lm_std=1.0, q_scale=4.0))
+    assert st["att_rows"] > 0
+
+
 @pytest.mark.parametrize("W,D", [(3, 7), (64, 1)])
 def test_f32_chain_other_candidate_shapes(W, D):
     _chain(generate("small_f32", W=W, D=D, lm_std=1.0))
@@ -307,7 +315,9 @@ def test_max_n_only_sizes_the_launch():
     d = Dev(wl)
     g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, None)
     outs = []
-    for mn in (wl.max_n, 64, 4 * wl.max_n):
+    # 32 * max_n gives 22 key splits, most of them past every context: the candidate
+    # slot then sits in the merge's second load group
+    for mn in (wl.max_n, 64, 4 * wl.max_n, 32 * wl.max_n):
         a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, mn, d.kc, d.vc, g["cand_len"],
                                    g["copy_gate"], d.lm, s.W, s.D, wl.scale)
         torch.cuda.synchronize()
