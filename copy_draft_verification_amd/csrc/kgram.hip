@@ -49,9 +49,13 @@ __device__ __forceinline__ int lds_ld(const int* p) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return v;
 }
+// The outputs are early-clobber: the first read's destination must not share a
+// register with the address, which the second read takes when it issues, and LDS
+// data can land before that (nothing orders a register read after an LDS load
+// still in flight to the same register).
 __device__ __forceinline__ void lds_ld8(const int* p, i32x4& a, i32x4& b) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(a), "=v"(b) : "v"(lds_addr(p)) : "memory");
+               : "=&v"(a), "=&v"(b) : "v"(lds_addr(p)) : "memory");
 }
 
 // Two workgroups per CU (8 waves per SIMD, 2 x 72 KB of LDS): while one
