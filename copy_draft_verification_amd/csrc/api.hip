@@ -159,12 +159,16 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
   float* ws_attn = static_cast<float*>(workspace);
   void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
   const int R = 1 + W * D;
+  // bf16: the row compaction runs as one more workgroup of the attention launch
+  const ssd::LmWsView cv = ssd::lm_ws_view(ws_lm, B * R);
   hipError_t e = ssd::launch_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
                                        B, W, D, Hq, Hkv, d, bf16, scale, L.attn, attn_out, ws_attn,
-                                       stream);
+                                       stream, bf16 ? &cv : nullptr);
   if (e != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (!bf16) {
+    e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+  }
   e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
                          lm_begin, lm_end, stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
@@ -195,11 +199,10 @@ ssd_status_t ssd_blocktri_verify_sample(
   float* ws_attn = static_cast<float*>(workspace);
   void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
   const int R = 1 + W * D;
+  const ssd::LmWsView cv = ssd::lm_ws_view(ws_lm, B * R);  // compaction beside the attention
   hipError_t e = ssd::launch_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
                                        B, W, D, Hq, Hkv, d, true, scale, L.attn, attn_out, ws_attn,
-                                       stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
+                                       stream, &cv);
   if (e != hipSuccess) return SSD_ERR_HIP;
   e = ssd::launch_trie(cand, cand_len, copy_gate, B, W, D, n_children, children, child_w,
                        child_logit, stream);

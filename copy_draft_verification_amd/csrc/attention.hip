@@ -42,16 +42,24 @@ __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 15
 // the workspace, in the exp2 domain; the merge kernel combines them.
 //
 // Grid: the (sequence, kv head, slot) groups are dealt to XCDs so that all row
-// tiles of a group share one XCD's L2 (they read the same keys).
+// tiles of a group share one XCD's L2 (they read the same keys).  With
+// compact.row_list set, the grid has one more workgroup, the last, which writes
+// the compact list of real rows for the LM head while the others attend.
 __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
     const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
     const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ cand_len, int B, int R,
     int Hq, int Hkv, int W, int D, int nsplit, int chunk, int qtiles, float scale_log2,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, LmWsView compact) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kAttD * kKB];
+  if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
+    __shared__ int s_cwave[256 / kWave];
+    compact_rows_body<256>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
+                           compact.n_rows, s_cwave);
+    return;
+  }
 
   // XCD-aware decode: block L runs on XCD L % 8; groups g with g % 8 == x run there
   const int nslots = nsplit + 1;
@@ -507,7 +515,9 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                             const int32_t* cu_len, const void* k_cand, const void* v_cand,
                             const int32_t* cand_len, const uint8_t* copy_gate, int B, int W,
                             int D, int Hq, int Hkv, int d, bool bf16, float scale,
-                            const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s) {
+                            const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s,
+                            const LmWsView* compact) {
+  if (compact != nullptr && !bf16) return hipErrorInvalidValue;
   const int R = 1 + W * D;
   const size_t rows = static_cast<size_t>(plan.nslots) * B * R * Hq;
   float* ws_m = ws;
@@ -519,12 +529,14 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   if (bf16) {
     const int groups = B * Hkv * plan.nslots;
     const int per_xcd = (groups + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(attn_prefix_bf16_kernel, dim3(kXcds * per_xcd * plan.qtiles), dim3(256), 0, s,
+    const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr};
+    hipLaunchKernelGGL(attn_prefix_bf16_kernel,
+                       dim3(kXcds * per_xcd * plan.qtiles + (compact != nullptr ? 1 : 0)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pre),
                        static_cast<const uint16_t*>(v_pre), cu_len,
                        static_cast<const uint16_t*>(k_cand), static_cast<const uint16_t*>(v_cand),
                        copy_gate, cand_len, B, R, Hq, Hkv, W, D, plan.nsplit, plan.chunk, plan.qtiles,
-                       scale_log2, ws_m, ws_l, ws_o);
+                       scale_log2, ws_m, ws_l, ws_o, cv);
     hipLaunchKernelGGL(attn_merge_bf16_kernel, mgrid, dim3(256), 0, s, cu_len, cand_len, copy_gate,
                        B, R, Hq, W, D, plan.nsplit, plan.chunk, ws_m, ws_l, ws_o,
                        static_cast<uint16_t*>(attn_out));

@@ -203,4 +203,31 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
   return woff + incl - v;
 }
 
+// Compact list of the real verification rows of B*R rows (R per sequence), in row
+// order: row_list[k] = k-th real row, inv[row] = its position or -1, *n_rows = the
+// count.  Run by every thread of one workgroup of NT threads; s_wave holds NT / 64
+// ints of LDS.
+template <int NT>
+__device__ void compact_rows_body(int rows, int R, int W, int D, const int32_t* __restrict__ cand_len,
+                                  const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
+                                  int32_t* __restrict__ inv, int32_t* __restrict__ n_rows, int* s_wave) {
+  int base = 0;
+  for (int r0 = 0; r0 < rows; r0 += NT) {
+    const int row = r0 + static_cast<int>(threadIdx.x);
+    bool real = false;
+    if (row < rows) {
+      const int b = row / R;
+      real = real_row(row - b * R, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0);
+    }
+    int total;
+    const int pos = base + block_excl_scan<NT>(real ? 1 : 0, s_wave, total);
+    if (row < rows) {
+      inv[row] = real ? pos : -1;
+      if (real) row_list[pos] = row;
+    }
+    base += total;
+  }
+  if (threadIdx.x == 0) *n_rows = base;
+}
+
 }  // namespace ssd

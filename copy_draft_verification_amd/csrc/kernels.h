@@ -28,11 +28,23 @@ struct AttnPlan {
 AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16);
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int R, int Hq, int d);
 
+// The LM-head workspace's compact row list (written by launch_compact_rows, or by
+// launch_attention when it is given one).
+struct LmWsView {
+  int32_t* n_rows;
+  int32_t* row_list;
+  int32_t* inv;
+};
+
+// With `compact` (bf16 only), one more workgroup of the prefix launch writes the
+// compact list of the B*(1+W*D) rows, as launch_compact_rows would, beside the
+// attention instead of after it.
 hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                             const int32_t* cu_len, const void* k_cand, const void* v_cand,
                             const int32_t* cand_len, const uint8_t* copy_gate, int B, int W,
                             int D, int Hq, int Hkv, int d, bool bf16, float scale,
-                            const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s);
+                            const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s,
+                            const LmWsView* compact = nullptr);
 
 struct LmPlan {
   int vtiles;   // vocabulary tiles (one workgroup column each)
@@ -139,12 +151,6 @@ hipError_t launch_gemm_pair(const void* rows_in, const void* w_gate_up, int tota
                             const LmPlan& plan, int splits, const void* lm_ws_ptr, float* part,
                             hipStream_t s);
 
-// The LM-head workspace's compact row list (written by launch_compact_rows).
-struct LmWsView {
-  int32_t* n_rows;
-  int32_t* row_list;
-  int32_t* inv;
-};
 LmWsView lm_ws_view(void* ws, int rows);
 
 // Multi-layer verification forward (embedding, decoder layers, final norm, LM head).

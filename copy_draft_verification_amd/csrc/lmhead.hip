@@ -662,23 +662,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(
     const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
     int32_t* __restrict__ inv, int32_t* __restrict__ n_rows) {
   __shared__ int s_wave[kCompactThreads / kWave];
-  int base = 0;
-  for (int r0 = 0; r0 < rows; r0 += kCompactThreads) {
-    const int row = r0 + static_cast<int>(threadIdx.x);
-    bool real = false;
-    if (row < rows) {
-      const int b = row / R;
-      real = real_row(row - b * R, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0);
-    }
-    int total;
-    const int pos = base + block_excl_scan<kCompactThreads>(real ? 1 : 0, s_wave, total);
-    if (row < rows) {
-      inv[row] = real ? pos : -1;
-      if (real) row_list[pos] = row;
-    }
-    base += total;
-  }
-  if (threadIdx.x == 0) *n_rows = base;
+  compact_rows_body<kCompactThreads>(rows, R, W, D, cand_len, copy_gate, row_list, inv, n_rows, s_wave);
 }
 
 // One wave per row: the row's tile partials are contiguous ([row][vtile]), each
