@@ -104,9 +104,53 @@ def _dev(t, name, dtypes=None):
     return t
 
 
-def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise SwitchSDError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    return t
+
+
+def _out(t, name, dtype, shape, device):
+    """A caller-supplied output: a contiguous tensor of exactly this dtype and shape on
+    the device of the inputs (the kernels write every element of it)."""
+    _dev(t, name, (dtype,))
+    _shape(t, name, shape)
+    if t.device != device:
+        raise SwitchSDError(f"{name} is on {t.device}, the inputs on {device}")
+    return t
+
+
+def _same_device(device, *named):
+    for t, n in named:
+        if t is not None and t.device != device:
+            raise SwitchSDError(f"{n} is on {t.device}, expected {device}")
+
+
+def _torch_stream(stream, device):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _torch_stream_handle(ts):
+    return ctypes.c_void_p(ts.cuda_stream)
+
+
+def _alloc(stream, shape, dtype, device):
+    """torch.empty on the stream the library's kernels will use: the caching allocator
+    then ties the block to that stream, so it is not handed to other work before the
+    kernels queued there are done with it."""
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(workspace, need, stream, device):
+    if workspace is None:
+        return _alloc(stream, (max(need, 1),), torch.uint8, device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    if workspace.device != device:
+        raise SwitchSDError(f"workspace is on {workspace.device}, expected {device}")
+    if workspace.numel() < need:
+        raise SwitchSDError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    return workspace
 
 
 def _dt(t):
@@ -121,13 +165,21 @@ def probe_score(h, w, tau, z_out=None, fire_out=None, stream=None):
     """Probe decision per sequence.  h [B, hid] (fp32 | bf16), w [hid] fp32."""
     _dev(h, "h", (torch.float32, torch.bfloat16))
     _dev(w, "w", (torch.float32,))
+    if h.dim() != 2:
+        raise SwitchSDError("h must be [B, hid]")
     B, hid = h.shape
+    _shape(w, "w", (hid,))
+    dev = h.device
+    _same_device(dev, (w, "w"))
+    ts = _torch_stream(stream, dev)
     if z_out is None:
-        z_out = torch.empty(B, dtype=torch.float32, device=h.device)
+        z_out = _alloc(ts, (B,), torch.float32, dev)
     if fire_out is None:
-        fire_out = torch.empty(B, dtype=torch.uint8, device=h.device)
+        fire_out = _alloc(ts, (B,), torch.uint8, dev)
+    _out(z_out, "z_out", torch.float32, (B,), dev)
+    _out(fire_out, "fire_out", torch.uint8, (B,), dev)
     _check(load().ssd_probe_score(_ptr(h), _dt(h), _ptr(w), B, hid, float(tau), _ptr(z_out),
-                                  _ptr(fire_out), _stream(stream)), "probe_score")
+                                  _ptr(fire_out), _torch_stream_handle(ts)), "probe_score")
     return z_out, fire_out
 
 
@@ -136,21 +188,24 @@ def kgram_retrieve(ids, cu_len, kappa, W, D, fire=None, out=None, stream=None):
     cand_len, copy_gate (device tensors)."""
     _dev(ids, "ids", (torch.int32,))
     _dev(cu_len, "cu_len", (torch.int32,))
-    if fire is not None:
-        _dev(fire, "fire", (torch.uint8,))
     B = cu_len.numel() - 1
     dev = ids.device
+    _same_device(dev, (cu_len, "cu_len"), (fire, "fire"))
+    if fire is not None:
+        _dev(fire, "fire", (torch.uint8,))
+        _shape(fire, "fire", (B,))
+    ts = _torch_stream(stream, dev)
+    shapes = {"match_end": ((B, W), torch.int32), "n_match": ((B,), torch.int32),
+              "cand": ((B, W, D), torch.int32), "cand_len": ((B, W), torch.int32),
+              "copy_gate": ((B,), torch.uint8)}
     if out is None:
-        out = {
-            "match_end": torch.empty(B, W, dtype=torch.int32, device=dev),
-            "n_match": torch.empty(B, dtype=torch.int32, device=dev),
-            "cand": torch.empty(B, W, D, dtype=torch.int32, device=dev),
-            "cand_len": torch.empty(B, W, dtype=torch.int32, device=dev),
-            "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev),
-        }
+        out = {k: _alloc(ts, sh, dt, dev) for k, (sh, dt) in shapes.items()}
+    for k, (sh, dt) in shapes.items():
+        _out(out[k], f"out[{k!r}]", dt, sh, dev)
     _check(load().ssd_kgram_retrieve(_ptr(ids), _ptr(cu_len), B, kappa, W, D, _ptr(fire),
                                      _ptr(out["match_end"]), _ptr(out["n_match"]), _ptr(out["cand"]),
-                                     _ptr(out["cand_len"]), _ptr(out["copy_gate"]), _stream(stream)),
+                                     _ptr(out["cand_len"]), _ptr(out["copy_gate"]),
+                                     _torch_stream_handle(ts)),
            "kgram_retrieve")
     return out
 
@@ -175,12 +230,17 @@ def pack_weight(w, out=None, stream=None):
     """Rearrange a bf16 weight matrix [rows, K] (an LM head or a projection) into the
     packed layout the bf16 calls read.  Returns a PackedWeight."""
     _dev(w, "w", (torch.bfloat16,))
+    if w.dim() != 2:
+        raise SwitchSDError("w must be [rows, K]")
     rows, K = w.shape
     need = pack_weight_bytes(rows, K)
+    ts = _torch_stream(stream, w.device)
     if out is None:
-        out = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+        out = _alloc(ts, (max(need, 1),), torch.uint8, w.device)
+    _dev(out, "out", (torch.uint8,))
+    _same_device(w.device, (out, "out"))
     _check(load().ssd_pack_weight(_ptr(w), rows, K, _ptr(out), out.numel() * out.element_size(),
-                                  _stream(stream)), "pack_weight")
+                                  _torch_stream_handle(ts)), "pack_weight")
     return PackedWeight(out, rows, K)
 
 
@@ -191,12 +251,20 @@ def pack_gate_up(w_gate, w_up, out=None, stream=None):
     _dev(w_up, "w_up", (torch.bfloat16,))
     if w_gate.shape != w_up.shape:
         raise SwitchSDError("w_gate and w_up must have the same shape")
+    if w_gate.dim() != 2:
+        raise SwitchSDError("w_gate must be [inter, K]")
     inter, K = w_gate.shape
     need = pack_gate_up_bytes(inter, K)
+    dev = w_gate.device
+    _same_device(dev, (w_up, "w_up"))
+    ts = _torch_stream(stream, dev)
     if out is None:
-        out = torch.empty(max(need, 1), dtype=torch.uint8, device=w_gate.device)
+        out = _alloc(ts, (max(need, 1),), torch.uint8, dev)
+    _dev(out, "out", (torch.uint8,))
+    _same_device(dev, (out, "out"))
     _check(load().ssd_pack_gate_up(_ptr(w_gate), _ptr(w_up), inter, K, _ptr(out),
-                                   out.numel() * out.element_size(), _stream(stream)), "pack_gate_up")
+                                   out.numel() * out.element_size(), _torch_stream_handle(ts)),
+           "pack_gate_up")
     return PackedWeight(out, inter, K, pair=True)
 
 
@@ -226,44 +294,66 @@ def verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, dtype):
     return int(load().ssd_verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, code))
 
 
-def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
-                    W, D, scale, attn_out=None, argmax_out=None, logits_out=None, workspace=None,
-                    events=None, stream=None):
-    """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
-    [B, W*D, Hkv, d]; lm_head [V, Hq*d] (fp32) or a PackedWeight (bf16).  Returns
-    (attn_out, argmax_out)."""
-    dts = (torch.float32, torch.bfloat16)
+def _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate, W, D, dtypes):
+    """Checks shared by the verification calls; returns (B, R, Hq, Hkv, d)."""
     for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
                  (v_cand, "v_cand")):
-        _dev(t, n, dts)
+        _dev(t, n, dtypes)
         if t.dtype != q.dtype:
             raise SwitchSDError(f"{n} dtype {t.dtype} differs from q dtype {q.dtype}")
     _dev(cu_len, "cu_len", (torch.int32,))
     _dev(cand_len, "cand_len", (torch.int32,))
     _dev(copy_gate, "copy_gate", (torch.uint8,))
+    if q.dim() != 4 or k_pre.dim() != 3:
+        raise SwitchSDError("q must be [B, R, Hq, d] and k_pre [N, Hkv, d]")
     B, R, Hq, d = q.shape
     Hkv = k_pre.shape[1]
+    if R != 1 + W * D:
+        raise SwitchSDError(f"q has {R} rows per sequence, 1 + W*D = {1 + W * D}")
+    _shape(k_pre, "k_pre", (k_pre.shape[0], Hkv, d))
+    _shape(v_pre, "v_pre", k_pre.shape)
+    _shape(k_cand, "k_cand", (B, W * D, Hkv, d))
+    _shape(v_cand, "v_cand", (B, W * D, Hkv, d))
+    _shape(cand_len, "cand_len", (B, W))
+    _shape(cu_len, "cu_len", (B + 1,))
+    _shape(copy_gate, "copy_gate", (B,))
+    _same_device(q.device, (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
+                 (v_cand, "v_cand"), (cu_len, "cu_len"), (cand_len, "cand_len"),
+                 (copy_gate, "copy_gate"))
+    return B, R, Hq, Hkv, d
+
+
+def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
+                    W, D, scale, attn_out=None, argmax_out=None, logits_out=None, workspace=None,
+                    events=None, stream=None):
+    """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
+    [B, W*D, Hkv, d]; cand_len [B, W]; cu_len [B+1]; copy_gate [B]; lm_head [V, Hq*d]
+    (fp32) or a PackedWeight (bf16).  Outputs, when given: attn_out [B, R, Hq*d] of
+    q's dtype, argmax_out [B, R] int32, logits_out [B, R, V] float32; workspace uint8
+    of at least verify_workspace_bytes.  cu_len[B] <= N is the caller's to keep (it
+    lives on the device).  Returns (attn_out, argmax_out)."""
+    B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
+                                      copy_gate, W, D, (torch.float32, torch.bfloat16))
     lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
     dev = q.device
+    ts = _torch_stream(stream, dev)
     if attn_out is None:
-        attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
+        attn_out = _alloc(ts, (B, R, Hq * d), q.dtype, dev)
+    _out(attn_out, "attn_out", q.dtype, (B, R, Hq * d), dev)
     if argmax_out is None:
-        argmax_out = torch.empty(B, R, dtype=torch.int32, device=dev)
+        argmax_out = _alloc(ts, (B, R), torch.int32, dev)
+    _out(argmax_out, "argmax_out", torch.int32, (B, R), dev)
+    if logits_out is not None:
+        _out(logits_out, "logits_out", torch.float32, (B, R, V), dev)
     need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    ev0 = ev1 = None
-    if events is not None:
-        # torch creates an event on its first record(); a handle of 0 would make the
-        # library skip the record silently, so refuse it here
-        if not events[0].cuda_event or not events[1].cuda_event:
-            raise SwitchSDError("events must be created (recorded once) before they are passed")
-        ev0, ev1 = ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event)
+    workspace = _workspace(workspace, need, ts, dev)
+    ev0, ev1 = _events(events)
     _check(load().ssd_blocktri_verify(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
         _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q),
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)), "blocktri_verify")
+        workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
+        "blocktri_verify")
     return attn_out, argmax_out
 
 
@@ -282,29 +372,25 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
     blocktri_verify; cand
     [B, W, D] int32.  Returns (attn_out, rows) with rows a dict of n_children [B, R],
     children / child_w [B, R, W], child_logit [B, R, W], lse [B, R], resample [B, R]."""
-    for t, n in ((q, "q"), (k_pre, "k_pre"), (v_pre, "v_pre"), (k_cand, "k_cand"),
-                 (v_cand, "v_cand")):
-        _dev(t, n, (torch.bfloat16,))
-    _dev(cu_len, "cu_len", (torch.int32,))
+    B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
+                                      copy_gate, W, D, (torch.bfloat16,))
     _dev(cand, "cand", (torch.int32,))
-    _dev(cand_len, "cand_len", (torch.int32,))
-    _dev(copy_gate, "copy_gate", (torch.uint8,))
-    B, R, Hq, d = q.shape
-    Hkv = k_pre.shape[1]
+    _shape(cand, "cand", (B, W, D))
     lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
     dev = q.device
+    ts = _torch_stream(stream, dev)
     if attn_out is None:
-        attn_out = torch.empty(B, R, Hq * d, dtype=q.dtype, device=dev)
+        attn_out = _alloc(ts, (B, R, Hq * d), q.dtype, dev)
+    _out(attn_out, "attn_out", q.dtype, (B, R, Hq * d), dev)
+    shapes = {"n_children": ((B, R), torch.int32), "children": ((B, R, W), torch.int32),
+              "child_w": ((B, R, W), torch.int32), "child_logit": ((B, R, W), torch.float32),
+              "lse": ((B, R), torch.float32), "resample": ((B, R), torch.int32)}
     if rows is None:
-        rows = {"n_children": torch.empty(B, R, dtype=torch.int32, device=dev),
-                "children": torch.empty(B, R, W, dtype=torch.int32, device=dev),
-                "child_w": torch.empty(B, R, W, dtype=torch.int32, device=dev),
-                "child_logit": torch.empty(B, R, W, dtype=torch.float32, device=dev),
-                "lse": torch.empty(B, R, dtype=torch.float32, device=dev),
-                "resample": torch.empty(B, R, dtype=torch.int32, device=dev)}
+        rows = {k: _alloc(ts, sh, dt, dev) for k, (sh, dt) in shapes.items()}
+    for k, (sh, dt) in shapes.items():
+        _out(rows[k], f"rows[{k!r}]", dt, sh, dev)
     need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, ts, dev)
     ev0, ev1 = _events(events)
     _check(load().ssd_blocktri_verify_sample(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
@@ -312,7 +398,7 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
         _dt(q), float(scale), float(temperature), int(seed) & ((1 << 64) - 1), _ptr(attn_out),
         _ptr(rows["n_children"]), _ptr(rows["children"]), _ptr(rows["child_w"]),
         _ptr(rows["child_logit"]), _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), ev0, ev1, _stream(stream)),
+        workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
         "blocktri_verify_sample")
     return attn_out, rows
 
@@ -323,14 +409,22 @@ def accept_sample(rows, copy_gate, W, D, seed, out=None, stream=None):
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     B = copy_gate.numel()
     dev = copy_gate.device
+    R = 1 + W * D
+    shapes = {"n_children": ((B, R), torch.int32), "child_w": ((B, R, W), torch.int32),
+              "child_logit": ((B, R, W), torch.float32), "lse": ((B, R), torch.float32),
+              "resample": ((B, R), torch.int32)}
+    for k, (sh, dt) in shapes.items():
+        _out(rows[k], f"rows[{k!r}]", dt, sh, dev)
+    ts = _torch_stream(stream, dev)
     if out is None:
-        out = {k: torch.empty(B, dtype=torch.int32, device=dev)
-               for k in ("best_w", "best_len", "next_token")}
+        out = {k: _alloc(ts, (B,), torch.int32, dev) for k in ("best_w", "best_len", "next_token")}
+    for k in ("best_w", "best_len", "next_token"):
+        _out(out[k], f"out[{k!r}]", torch.int32, (B,), dev)
     _check(load().ssd_accept_sample(
         _ptr(rows["n_children"]), _ptr(rows["child_w"]), _ptr(rows["child_logit"]),
         _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(copy_gate), B, W, D,
         int(seed) & ((1 << 64) - 1), _ptr(out["best_w"]), _ptr(out["best_len"]),
-        _ptr(out["next_token"]), _stream(stream)), "accept_sample")
+        _ptr(out["next_token"]), _torch_stream_handle(ts)), "accept_sample")
     return out
 
 
@@ -341,16 +435,20 @@ def accept_longest(cand, cand_len, copy_gate, argmax, W, D, out=None, stream=Non
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     B = copy_gate.numel()
     dev = cand.device
+    _shape(cand, "cand", (B, W, D))
+    _shape(cand_len, "cand_len", (B, W))
+    _shape(argmax, "argmax", (B, 1 + W * D))
+    _same_device(dev, (cand_len, "cand_len"), (argmax, "argmax"), (copy_gate, "copy_gate"))
+    ts = _torch_stream(stream, dev)
+    shapes = {"accept_len": (B, W), "best_w": (B,), "best_len": (B,), "next_token": (B,)}
     if out is None:
-        out = {
-            "accept_len": torch.empty(B, W, dtype=torch.int32, device=dev),
-            "best_w": torch.empty(B, dtype=torch.int32, device=dev),
-            "best_len": torch.empty(B, dtype=torch.int32, device=dev),
-            "next_token": torch.empty(B, dtype=torch.int32, device=dev),
-        }
+        out = {k: _alloc(ts, sh, torch.int32, dev) for k, sh in shapes.items()}
+    for k, sh in shapes.items():
+        _out(out[k], f"out[{k!r}]", torch.int32, sh, dev)
     _check(load().ssd_accept_longest(_ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(argmax), B, W,
                                      D, _ptr(out["accept_len"]), _ptr(out["best_w"]),
-                                     _ptr(out["best_len"]), _ptr(out["next_token"]), _stream(stream)),
+                                     _ptr(out["best_len"]), _ptr(out["next_token"]),
+                                     _torch_stream_handle(ts)),
            "accept_longest")
     return out
 
@@ -369,17 +467,31 @@ def commit_accepted(k_cand, v_cand, cand, best_w, best_len, next_token, W, D, k_
                  (next_token, "next_token")):
         _dev(t, n, (torch.int32,))
     _dev(cache_off, "cache_off", (torch.int64,))
+    if k_cand.dim() != 4:
+        raise SwitchSDError("k_cand must be [B, W*D, Hkv, d]")
     B, _, Hkv, d = k_cand.shape
+    _shape(k_cand, "k_cand", (B, W * D, Hkv, d))
+    _shape(v_cand, "v_cand", k_cand.shape)
+    _shape(cand, "cand", (B, W, D))
+    for t, n in ((best_w, "best_w"), (best_len, "best_len"), (next_token, "next_token"),
+                 (cache_off, "cache_off")):
+        _shape(t, n, (B,))
     if k_cache.shape[1:] != k_cand.shape[2:] or v_cache.shape != k_cache.shape:
         raise SwitchSDError("k_cache / v_cache must be [rows, Hkv, d] matching k_cand")
     dev = k_cand.device
+    _same_device(dev, (v_cand, "v_cand"), (cand, "cand"), (best_w, "best_w"),
+                 (best_len, "best_len"), (next_token, "next_token"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache"), (cache_off, "cache_off"))
+    ts = _torch_stream(stream, dev)
     if out is None:
-        out = {"tokens": torch.empty(B, D + 1, dtype=torch.int32, device=dev),
-               "n_tokens": torch.empty(B, dtype=torch.int32, device=dev)}
+        out = {"tokens": _alloc(ts, (B, D + 1), torch.int32, dev),
+               "n_tokens": _alloc(ts, (B,), torch.int32, dev)}
+    _out(out["tokens"], "out['tokens']", torch.int32, (B, D + 1), dev)
+    _out(out["n_tokens"], "out['n_tokens']", torch.int32, (B,), dev)
     _check(load().ssd_commit_accepted(
         _ptr(k_cand), _ptr(v_cand), _ptr(cand), _ptr(best_w), _ptr(best_len), _ptr(next_token),
         B, W, D, Hkv, d, _dt(k_cand), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
-        _ptr(cache_off), _ptr(out["tokens"]), _ptr(out["n_tokens"]), _stream(stream)),
+        _ptr(cache_off), _ptr(out["tokens"]), _ptr(out["n_tokens"]), _torch_stream_handle(ts)),
         "commit_accepted")
     return out
 
@@ -394,15 +506,15 @@ def copy_labels(ids, cu_len, n_train=5, labels=None, workspace=None, stream=None
     _dev(ids, "ids", (torch.int32,))
     _dev(cu_len, "cu_len", (torch.int32,))
     n, B = ids.numel(), cu_len.numel() - 1
+    dev = ids.device
+    _same_device(dev, (cu_len, "cu_len"))
+    ts = _torch_stream(stream, dev)
     if labels is None:
-        labels = torch.empty(n, dtype=torch.uint8, device=ids.device)
-    _dev(labels, "labels", (torch.uint8,))
-    need = copy_labels_workspace_bytes(n)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
-    _dev(workspace, "workspace", (torch.uint8,))
+        labels = _alloc(ts, (n,), torch.uint8, dev)
+    _out(labels, "labels", torch.uint8, (n,), dev)
+    workspace = _workspace(workspace, copy_labels_workspace_bytes(n), ts, dev)
     _check(load().ssd_copy_labels(_ptr(ids), _ptr(cu_len), B, n, n_train, _ptr(labels),
-                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+                                  _ptr(workspace), workspace.numel(), _torch_stream_handle(ts)),
            "copy_labels")
     return labels
 
@@ -411,14 +523,19 @@ def probe_logits(h, w, z_out=None, stream=None):
     """z[l][i] = w[l] . h[l][i].  h [L, N, hid] (fp32 | bf16), w [L, hid] fp32 -> z [L, N] fp32."""
     _dev(h, "h", (torch.float32, torch.bfloat16))
     _dev(w, "w", (torch.float32,))
+    if h.dim() != 3:
+        raise SwitchSDError("h must be [L, N, hid]")
     L, N, hid = h.shape
     if tuple(w.shape) != (L, hid):
         raise SwitchSDError(f"w must be [{L}, {hid}], got {tuple(w.shape)}")
+    dev = h.device
+    _same_device(dev, (w, "w"))
+    ts = _torch_stream(stream, dev)
     if z_out is None:
-        z_out = torch.empty(L, N, dtype=torch.float32, device=h.device)
-    _dev(z_out, "z_out", (torch.float32,))
+        z_out = _alloc(ts, (L, N), torch.float32, dev)
+    _out(z_out, "z_out", torch.float32, (L, N), dev)
     _check(load().ssd_probe_logits(_ptr(h), _dt(h), _ptr(w), L, N, hid, _ptr(z_out),
-                                   _stream(stream)), "probe_logits")
+                                   _torch_stream_handle(ts)), "probe_logits")
     return z_out
 
 
@@ -436,21 +553,20 @@ def calibrate(z, labels, out=None, workspace=None, stream=None):
     if labels.numel() != N:
         raise SwitchSDError(f"labels must hold {N} entries, got {labels.numel()}")
     dev = z.device
+    _same_device(dev, (labels, "labels"))
+    ts = _torch_stream(stream, dev)
+    shapes = {"thr": ((L,), torch.float32), "counts": ((L, 4), torch.int32),
+              "u2": ((L,), torch.int64), "auc": ((L,), torch.float32),
+              "best_layer": ((1,), torch.int32), "tau": ((1,), torch.float32)}
     if out is None:
-        out = {"thr": torch.empty(L, dtype=torch.float32, device=dev),
-               "counts": torch.empty(L, 4, dtype=torch.int32, device=dev),
-               "u2": torch.empty(L, dtype=torch.int64, device=dev),
-               "auc": torch.empty(L, dtype=torch.float32, device=dev),
-               "best_layer": torch.empty(1, dtype=torch.int32, device=dev),
-               "tau": torch.empty(1, dtype=torch.float32, device=dev)}
-    need = calibrate_workspace_bytes(L, N)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _dev(workspace, "workspace", (torch.uint8,))
+        out = {k: _alloc(ts, sh, dt, dev) for k, (sh, dt) in shapes.items()}
+    for k, (sh, dt) in shapes.items():
+        _out(out[k], f"out[{k!r}]", dt, sh, dev)
+    workspace = _workspace(workspace, calibrate_workspace_bytes(L, N), ts, dev)
     _check(load().ssd_calibrate(_ptr(z), _ptr(labels), L, N, _ptr(out["thr"]), _ptr(out["counts"]),
                                 _ptr(out["u2"]), _ptr(out["auc"]), _ptr(out["best_layer"]),
                                 _ptr(out["tau"]), _ptr(workspace), workspace.numel(),
-                                _stream(stream)), "calibrate")
+                                _torch_stream_handle(ts)), "calibrate")
     return out
 
 
@@ -498,16 +614,33 @@ def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers,
     B = cu_len.numel() - 1
     R = 1 + W * D
     dev = cand.device
+    _shape(cand, "cand", (B, W, D))
+    _shape(cand_len, "cand_len", (B, W))
+    _shape(copy_gate, "copy_gate", (B,))
+    _shape(final_norm, "final_norm", (hid,))
+    if embed.dim() != 2 or embed.shape[1] != hid:
+        raise SwitchSDError(f"embed must be [vocab, {hid}], got {list(embed.shape)}")
+    for i, L in enumerate(layers):
+        for f in ("attn_norm", "mlp_norm"):
+            _shape(L[f], f"layers[{i}][{f!r}]", (hid,))
+        for f in ("k_cache", "v_cache"):
+            if L[f].dim() != 3 or tuple(L[f].shape[1:]) != (Hkv, d):
+                raise SwitchSDError(f"layers[{i}][{f!r}] must be [N, {Hkv}, {d}]")
+    _same_device(dev, (ids, "ids"), (cu_len, "cu_len"), (cand_len, "cand_len"),
+                 (copy_gate, "copy_gate"), (embed, "embed"), (final_norm, "final_norm"))
+    ts = _torch_stream(stream, dev)
     if argmax_out is None:
-        argmax_out = torch.empty(B, R, dtype=torch.int32, device=dev)
+        argmax_out = _alloc(ts, (B, R), torch.int32, dev)
+    _out(argmax_out, "argmax_out", torch.int32, (B, R), dev)
+    if x_out is not None:
+        _out(x_out, "x_out", torch.float32, (B, R, hid), dev)
     need = verify_forward_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, inter, V)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, ts, dev)
     ev0, ev1 = _events(events)
     _check(load().ssd_verify_forward(
         _ptr(ids), _ptr(cu_len), int(max_n), _ptr(cand), _ptr(cand_len), _ptr(copy_gate),
         _ptr(embed), ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(final_norm),
         _ptr(lm), B, W, D, Hq, Hkv, d, inter, V, float(rope_base), float(eps),
         _ptr(argmax_out), _ptr(x_out), _ptr(workspace), workspace.numel(), ev0, ev1,
-        _stream(stream)), "verify_forward")
+        _torch_stream_handle(ts)), "verify_forward")
     return argmax_out, x_out

@@ -36,7 +36,7 @@ in ``tests/test_oracle_*.py``; no function here is "parity unpinned".
 from .bf16 import bf16_bits_to_f64
 from .probe import probe_score, logit
 from .kgram import kgram_matches, kgram_retrieve
-from .attention import allowed_keys, attention_row, blocktri_attention
+from .attention import allowed_keys, blocktri_attention
 from .lmhead import lm_logits, argmax_with_margin, lmhead_argmax
 from .accept import accept_longest
 from .commit import commit_accepted
@@ -46,7 +46,7 @@ from .forward import decoder_layer, verify_forward
 
 __all__ = [
     "bf16_bits_to_f64", "probe_score", "logit", "kgram_matches", "kgram_retrieve",
-    "allowed_keys", "attention_row", "blocktri_attention", "lm_logits",
+    "allowed_keys", "blocktri_attention", "lm_logits",
     "argmax_with_margin", "lmhead_argmax", "accept_longest", "commit_accepted", "copy_labels",
     "probe_logits", "threshold_sweep", "calibrate", "candidate_trie", "philox", "sample_step",
     "sample_verify", "decoder_layer", "verify_forward",

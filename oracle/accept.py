@@ -1,12 +1,13 @@
 """Longest accepted continuation at T = 0 (oracle; test infrastructure only).
 
 SwitchSD paper §3.3 "Parallel Verification": after the single verification pass
-the framework keeps the longest validated continuation; write-up §2.6 says the
-same ("选最长验证通过的延续").  Greedy verification checks a drafted token
+the framework keeps the candidate whose verified continuation is longest; the
+write-up's §2.6 states the same rule.  Greedy verification checks a drafted token
 against the target's own choice after the tokens before it and stops at the
-first disagreement — the prefix-acceptance rule that the VIA-SD page states for
-the draft-verify paradigm ("Draft–Verify and Lossy Acceptance": decoding stops
-at the first rejection; "VIA-SD Inference" step 4: longest accepted prefix).
+first disagreement, the prefix-acceptance rule of the draft-verify paradigm as
+the VIA-SD page states it ("Draft–Verify and Lossy Acceptance": decoding halts
+at the first rejected token; "VIA-SD Inference" step 4: the accepted prefix is
+the longest one).
 
 Readings:
 * pred(w, -1) is the anchor row's choice (row 0); pred(w, j) is the choice at

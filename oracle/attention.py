@@ -55,16 +55,6 @@ def real_rows(cand_len_b, gate_b, W, D):
     return rows
 
 
-def attention_row(q_h, K, V, vis, scale):
-    """softmax(scale * K q over visible keys) . V for one query vector, float64."""
-    s = (K @ q_h) * scale
-    s_vis = s[vis]
-    m = s_vis.max()
-    e = np.exp(s_vis - m)
-    p = e / e.sum()
-    return p @ V[vis]
-
-
 def blocktri_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
                        Hq, Hkv, d, W, D, scale=None, rows=None):
     """Block-triangular attention output for real rows.

@@ -23,10 +23,16 @@ Readings:
 * The anchor's own key and value are prefix entry n - 1 (the caller's cache), so
   the anchor row contributes only its query; candidate rows contribute their
   keys and values to the candidate blocks.
-* Storage: activations passed between steps are bfloat16 (the normalised states,
-  q / k / v after RoPE, the attention output, the MLP activation); the residual
-  stream x stays wide.  Arithmetic is float64 and values are rounded to bf16 at
-  those points, as the kernels store them.
+* Storage, the rule of a bf16 Llama layer: every tensor that one operation hands
+  to the next as an operand of a bf16 matrix product or of attention is held in
+  bf16.  Those are the RMSNorm outputs that feed the q/k/v and the gate/up
+  projections, q and k after RoPE and v (so the KV cache holds bf16 keys and
+  values), the attention output that feeds W_o, the SwiGLU activation
+  silu(gate) * up that feeds W_down, and the final RMSNorm output that feeds the
+  LM head.  Each is computed wide, held as the float32 an accumulator would
+  hold, and rounded to bf16, to nearest even.  The
+  residual stream x, into which W_o and W_down add their outputs, stays wide, and
+  so do the logits.  storage_bf16=False keeps every tensor wide.
 """
 import numpy as np
 

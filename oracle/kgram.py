@@ -16,11 +16,11 @@ Readings where the pages leave a step open:
 * Recency = larger end position first.  Positions are distinct, so the order is
   total; identical continuations are not merged (the pages mention no merging).
 * Candidate w continues its occurrence: cand[w][j] = x[p_w + 1 + j] for
-  j < L_w = min(D, n - 1 - p_w).  The paper says "each of length D", the
-  write-up "at most D"; a recent occurrence too close to the end to supply D
-  tokens is kept with the tokens it has.
-* When the probe does not fire, nothing is retrieved (retrieval happens "when
-  the copy-regime is triggered"), and the gate is closed.
+  j < L_w = min(D, n - 1 - p_w).  The paper gives every candidate length D,
+  the write-up caps it at D; a recent occurrence too close to the end to supply
+  D tokens is kept with the tokens it has.
+* When the probe does not fire, nothing is retrieved (the paper retrieves only
+  once the copy regime is triggered), and the gate is closed.
 """
 import numpy as np
 

@@ -7,7 +7,12 @@ Bars (stated once, used everywhere):
   oracle score lies within 1e-5 * sum|w_k h_k| of the threshold is a tie-zone
   case (float32 vs float64 rounding can flip it) and is counted, not compared.
 * probe score z: |z_gpu - z| <= 1e-5 * sum|w_k h_k|.
-* attention output: |O_gpu - O| <= 1e-5 (float32 inputs), 2e-2 (bfloat16).
+* attention output: |O_gpu - O| <= 1e-5 (float32 inputs), 2e-2 (bfloat16), and,
+  relative to the largest reference output of the case, max|O_gpu - O| / max|O|
+  <= 1e-4 (float32), 2e-2 (bfloat16).  Under N(0,1) queries and keys |O| shrinks
+  like sqrt(e/n), so at long contexts the absolute bar alone would pass a mask
+  error; the relative bar and the peaked-query cases (queries x4, softmax
+  concentrated on a few keys, |O| of order 1) do not.
 * logits: |l_gpu - l| <= 5e-2.
 * argmax: equal wherever the oracle's top-2 margin is >= 1e-2; rows below that
   margin are counted as margin-excluded.
@@ -22,6 +27,7 @@ from workloads import to_torch
 
 DEV = "cuda:0"
 TOL_ATT = {"f32": 1e-5, "bf16": 2e-2}
+REL_ATT = {"f32": 1e-4, "bf16": 2e-2}
 TOL_LOGIT = 5e-2
 ARGMAX_MARGIN = 1e-2
 PROBE_TIE = 1e-5
@@ -110,11 +116,16 @@ def check_verify(wl, d, g, rows_att=None, rows_lm=None, logits=True, events=None
     ref, ev = oracle.blocktri_attention(wl.q, wl.k_pre, wl.v_pre, wl.cu_len, wl.k_cand, wl.v_cand,
                                         cand_len, gate, s.Hq, s.Hkv, s.d, s.W, s.D, wl.scale,
                                         rows=rows_att)
-    err_att = 0.0
+    err_att = ref_max = 0.0
     for (b, r) in ev:
         e = np.max(np.abs(O[b, r] - ref[b, r]))
         err_att = max(err_att, e)
+        ref_max = max(ref_max, float(np.max(np.abs(ref[b, r]))))
+    rel_att = err_att / ref_max if ref_max > 0 else 0.0
+    print(f"[att] rows {len(ev)} max|O-O*| {err_att:.3e} max|O*| {ref_max:.3e} "
+          f"relative {rel_att:.3e}", flush=True)
     assert err_att <= TOL_ATT[s.dtype], err_att
+    assert rel_att <= REL_ATT[s.dtype], rel_att
     # LM head on the device's own attention output
     lm_rows = sorted(real) if rows_lm is None else [x for x in rows_lm if x in real]
     excluded = 0
@@ -131,7 +142,7 @@ def check_verify(wl, d, g, rows_att=None, rows_lm=None, logits=True, events=None
             Lsel = L[[b for b, _ in lm_rows], [r for _, r in lm_rows]].astype(np.float64)
             err_logit = float(np.max(np.abs(Lsel - res["logits"])))
             assert err_logit <= TOL_LOGIT, err_logit
-    return attn, am, {"err_att": err_att, "err_logit": err_logit, "argmax_rows": len(lm_rows),
+    return attn, am, {"err_att": err_att, "rel_att": rel_att, "err_logit": err_logit, "argmax_rows": len(lm_rows),
                       "margin_excluded": excluded, "att_rows": len(ev)}
 
 

@@ -8,8 +8,14 @@ Bars:
   (one unit in the 8th bit), and such flips propagate through the next
   projections.
 * rows that are not real: x = 0 and argmax = -1.
-* argmax: equal wherever the oracle's top-2 logit margin is >= 5e-2 (logits are
-  O(1) with these weights); closer rows are counted.
+* argmax, per stage: the oracle's final norm and LM head applied to the GPU's own
+  final residual give the reference; the GPU's argmax must equal it wherever that
+  reference's top-2 margin is >= 1e-2.
+* argmax, chained: against the oracle's whole forward, equal wherever the
+  oracle's margin is >= max(1e-2, 2 * delta), where delta is the largest logit
+  difference between the two references on the checked rows (the effect of the
+  residual-stream differences above on the logits, measured, not assumed).
+  Closer rows are counted.
 Every test prints its case before touching the GPU."""
 import numpy as np
 import pytest
@@ -25,7 +31,7 @@ from workloads import generate_forward
 pytestmark = pytest.mark.gpu
 
 X_TOL = 2e-2
-MARGIN = 5e-2
+MARGIN = 1e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -92,17 +98,26 @@ def _check(fw, n_layers, kg, am, x):
     err = np.abs(x[real] - ref["x"][real]) / (1.0 + np.abs(ref["x"][real]))
     worst = float(err.max()) if err.size else 0.0
     assert worst <= X_TOL, worst
-    close = compared = 0
-    for i, (b, r) in enumerate(ref["rows"]):
-        if not real[b, r]:
-            continue
-        if ref["margin"][i] < MARGIN:
-            close += 1
-            continue
-        assert am[b, r] == ref["pred"][i], (b, r)
-        compared += 1
-    print(f"[ok] layers {n_layers} rows {int(real.sum())} max rel x err {worst:.2e} "
-          f"argmax compared {compared} close {close}", flush=True)
+    rows = [(b, r) for (b, r) in ref["rows"] if real[b, r]]
+    if rows:
+        # per stage: the final norm and LM head on the GPU's own residual stream
+        h_gpu = F.round_bf16(F.rmsnorm(x[[b for b, _ in rows], [r for _, r in rows]],
+                                       oracle.bf16_bits_to_f64(fw.final_norm), 1e-5))
+        st = oracle.lmhead_argmax(h_gpu, fw.lm_head)
+        got = np.array([am[b, r] for b, r in rows])
+        ok = st["margin"] >= MARGIN
+        assert np.array_equal(got[ok], st["pred"][ok]), np.nonzero(got[ok] != st["pred"][ok])
+        # chained: against the oracle's own forward, beyond twice the measured logit gap
+        idx = {rc: i for i, rc in enumerate(ref["rows"])}
+        sel = [idx[rc] for rc in rows]
+        delta = float(np.max(np.abs(st["logits"] - ref["logits"][sel])))
+        bar = max(MARGIN, 2.0 * delta)
+        ok_c = ref["margin"][sel] >= bar
+        assert np.array_equal(got[ok_c], ref["pred"][sel][ok_c])
+        print(f"[ok] layers {n_layers} rows {len(rows)} max rel x err {worst:.2e} "
+              f"per-stage argmax compared {int(ok.sum())} (margin < {MARGIN}: {int((~ok).sum())}); "
+              f"chained logit gap {delta:.2e}, compared {int(ok_c.sum())} at margin >= {bar:.2e}",
+              flush=True)
     return worst
 
 

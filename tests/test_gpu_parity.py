@@ -64,8 +64,8 @@ def test_bf16_chain_other_candidate_shapes(W, D):
 
 def test_bf16_chain_many_key_splits():
     # one sequence whose rows fit one tile of one KV head: the 12000-token context is
-    # cut into 23 key splits (21 of them hold keys), more slots than the merge loads
-    # at once, so its running (max, sum, output) is carried across load groups
+    # cut into 23 key splits, 21 of which hold keys; the merge combines 21 prefix
+    # partials and the candidate slot, which comes last
     st = _chain(generate("small_bf16", B=1, n=(12000, 12000), W=1, D=20, lm_std=1.0, q_scale=4.0))
     assert st["att_rows"] > 0
 
@@ -315,8 +315,9 @@ def test_max_n_only_sizes_the_launch():
     d = Dev(wl)
     g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D, None)
     outs = []
-    # 32 * max_n gives 22 key splits, most of them past every context: the candidate
-    # slot then sits in the merge's second load group
+    # 32 * max_n gives 22 key splits, most of them past every context: the merge skips
+    # the slots past each context (it counts the splits from n_b) and still reads the
+    # candidate slot, the last one
     for mn in (wl.max_n, 64, 4 * wl.max_n, 32 * wl.max_n):
         a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, mn, d.kc, d.vc, g["cand_len"],
                                    g["copy_gate"], d.lm, s.W, s.D, wl.scale)
@@ -348,6 +349,23 @@ def test_full_llama8b_b1_every_row():
 def test_full_llama8b_b1_wide_head_every_row():
     st = _chain(generate("llama8b_b1", lm_std=1.0), logits=True)
     assert st["margin_excluded"] <= 0.1 * st["argmax_rows"]
+
+
+def test_full_llama8b_b1_peaked_every_row():
+    # queries x4: each row's softmax concentrates on a few keys and |O| is of order 1,
+    # so the 2e-2 bar sees a leaked or dropped candidate key.  Every row of the 8B
+    # shape: g = 4 packed heads, 7 row tiles, the prefix split over several key slots
+    wl = generate("llama8b_b1", q_scale=4.0, lm_std=1.0)
+    st = _chain(wl, rows_lm=_sample_rows(wl, 24, 3), logits=False)
+    assert st["att_rows"] == wl.R and st["err_att"] <= 2e-2
+
+
+def test_full_llama70b_peaked_one_sequence():
+    # the 70B share's tiling (g = 8, 13 row tiles of packed heads) over one 32768-token
+    # context, peaked queries, every row
+    wl = generate("llama70b_b4", B=1, q_scale=4.0, lm_std=1.0)
+    st = _chain(wl, rows_lm=_sample_rows(wl, 12, 4), logits=False)
+    assert st["att_rows"] == wl.R
 
 
 @pytest.mark.parametrize("name,over", [("llama8b_b32", {}), ("llama8b_b32", {"anchor": "natural"}),

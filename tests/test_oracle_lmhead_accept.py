@@ -2,8 +2,9 @@
 
 LM head: SwitchSD paper §3.3 (one target forward pass verifies all candidates),
 write-up §3.1 (T = 0): the target's choice per row is the argmax of the logits.
-Accept: paper §3.3 "selects the longest validated continuation"; the VIA-SD
-page's "Draft–Verify and Lossy Acceptance" (stop at the first rejection).
+Accept: paper §3.3 (the candidate with the longest verified continuation is
+kept); the VIA-SD page's "Draft–Verify and Lossy Acceptance" (acceptance halts at
+the first rejected token).
 
 References here: hand-computed logits, Python-loop dot products on non-square
 shapes (a transposed weight fails), planted argmax columns, a hand-computed
