@@ -6,11 +6,20 @@ synchronisation inside: probe_score -> kgram_retrieve -> blocktri_verify
 synthetic (seeded) and resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-configs] [--config-steps K2]
 
-Prints one JSON line: copy-steps/s (whole job), verified candidate tokens/s,
-the LM-head kernel's roofline position (HIP events around that kernel in the
-timed region) and the CPU oracle timed on the host on a bounded sample.
+Protocol: W untimed steps; K steps back to back between two events (reported as
+ms_per_step_back_to_back); then K steps each between its own stage events, with a
+512 MiB buffer rewritten before each step (outside its events) so that no input
+is served from the 256 MB last-level cache.  value = B / the median of those
+steps; p10 / p90 and the per-stage medians (probe, retrieval, attention, LM head,
+argmax reduce, accept) are reported with it.
+
+Prints one JSON line: copy-steps/s (whole job), verified candidate tokens/s, the
+LM-head and attention roofline positions, the same figures for the tiny, batch-32,
+Qwen3-8B and 70B-share workloads (`configs`; their large tensors are drawn on the
+device by torch's seeded generator), and the CPU oracle timed on the host on a
+bounded sample, stage by stage.
 
     python bench.py --calibration [--steps K] [--warmup W]
 
@@ -42,8 +51,13 @@ FP32_PEAK_TFS = 157.3
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config-steps", type=int, default=30,
+                   help="timed steps of each further configuration (batch 32, Qwen3, 70B; the tiny "
+                        "workload takes --steps)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="time the headline workload only, not the further configurations")
     p.add_argument("--workload", default="llama8b_b1")
     p.add_argument("--anchor", default=None, choices=("full", "natural"),
                    help="anchor mode of the synthetic contexts (default: the workload's own)")
@@ -124,24 +138,47 @@ def lm_algorithmic(s, R_tot):
     return byts, flops
 
 
-def cpu_baseline(wl, budget_s):
-    """Time the oracle (as it stands) on the host for one step of this workload.
+def host_cpu():
+    """CPU model and logical CPU count of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
 
-    Integer stages and the probe run on every sequence.  Attention and the LM head
-    run on a seeded sample of real rows sized to the budget, and their time is
-    scaled to all real rows of the step."""
-    import oracle
-    from oracle.attention import real_rows
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+        return 1
+
+
+def cpu_baseline(wl, budget_s, gpu_stage_ms=None):
+    """Time the oracle (as it stands) on the host for one step of this workload.
+
+    The probe, the kappa-gram retrieval and the acceptance are Python loops: one
+    thread, every sequence.  Attention and the LM head are numpy float64 matmuls on
+    the BLAS threads, on a seeded sample of real rows sized to the budget, their
+    time scaled to all real rows of the step.  With the GPU's per-stage medians
+    (ms) the per-stage GPU/oracle speedups are reported too."""
+    import oracle
+    from oracle.attention import real_rows
+    threads = blas_threads()
+    model, nproc = host_cpu()
     s = wl.spec
     t0 = time.perf_counter()
     pr = oracle.probe_score(wl.h, wl.w, s.tau)
+    t_probe = time.perf_counter() - t0
+    t0 = time.perf_counter()
     kg = oracle.kgram_retrieve(wl.ids, wl.cu_len, s.kappa, s.W, s.D, pr["fire"])
-    t_int = time.perf_counter() - t0
+    t_kg = time.perf_counter() - t0
     real = [(b, r) for b in range(s.B) for r in real_rows(kg["cand_len"][b], kg["copy_gate"][b], s.W, s.D)]
     if not real:
         return None
@@ -180,13 +217,34 @@ def cpu_baseline(wl, budget_s):
     t0 = time.perf_counter()
     oracle.accept_longest(kg["cand"], kg["cand_len"], kg["copy_gate"], am, s.W, s.D)
     t_acc = time.perf_counter() - t0
-    t_step = t_int + t_att * n_real / k_att + t_lm * n_real / k_lm + t_acc
-    return {"value": s.B / t_step, "unit": "copy-steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"{s.name}: probe+kgram+accept on all {s.B} sequences; attention on {k_att} "
-                       f"of {n_real} real rows ({t_att:.2f}s), LM head+argmax on {k_lm} rows "
-                       f"({t_lm:.2f}s, includes widening the {s.V}x{s.hid} weights to float64); "
-                       f"scaled to all rows: {t_step:.2f}s per step"),
-            "measured_s": round(t_int + t_att + t_lm + t_acc, 2)}
+    att_all = t_att * n_real / k_att
+    lm_all = t_lm * n_real / k_lm
+    t_step = t_probe + t_kg + att_all + lm_all + t_acc
+    stages = {"probe": {"s": round(t_probe, 5), "threads": 1},
+              "kgram_retrieve": {"s": round(t_kg, 5), "threads": 1},
+              "attention": {"s": round(att_all, 4), "threads": threads,
+                            "measured_rows": k_att, "rows": n_real},
+              "lm_head_argmax": {"s": round(lm_all, 4), "threads": threads,
+                                 "measured_rows": k_lm, "rows": n_real},
+              "accept": {"s": round(t_acc, 5), "threads": 1}}
+    res = {"value": s.B / t_step, "unit": "copy-steps/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"{s.name}: probe+kgram+accept on all {s.B} sequences (one thread, Python "
+                      f"loops); attention on {k_att} of {n_real} real rows ({t_att:.2f}s), LM "
+                      f"head+argmax on {k_lm} rows ({t_lm:.2f}s, includes widening the "
+                      f"{s.V}x{s.hid} weights to float64), both numpy float64 on {threads} BLAS "
+                      f"threads; scaled to all rows: {t_step:.2f}s per step"),
+           "cpu_model": model, "nproc": nproc, "blas_threads": int(threads),
+           "stages": stages, "measured_s": round(t_probe + t_kg + t_att + t_lm + t_acc, 2)}
+    if gpu_stage_ms:
+        pairs = {"probe": "probe", "kgram_retrieve": "kgram_retrieve", "attention": "attention",
+                 "lm_head_argmax": "lm_head", "accept": "accept"}
+        sp = {}
+        for k, g in pairs.items():
+            gm = gpu_stage_ms.get(g)
+            if gm and gm > 0:
+                sp[k] = round(stages[k]["s"] / (gm * 1e-3), 1)
+        res["oracle_over_gpu"] = sp
+    return res
 
 
 def calibration_cpu_baseline(c, budget_s):
@@ -540,6 +598,198 @@ def bench_forward(a):
     print(json.dumps(line), flush=True)
 
 
+FLUSH_BYTES = 512 << 20      # written between timed steps: twice the 256 MB last-level cache
+STAGES = ("probe", "kgram_retrieve", "attention", "lm_head", "reduce", "accept")
+
+
+def attn_algorithmic(s, n, gate, cand_len):
+    """Attention work the method needs for one step: per open sequence the prefix K
+    and V once, the real rows' queries in and outputs out, the real candidate
+    tokens' K and V; 4*Hq*d flops per visible (row, key) pair, masked pairs and
+    padded rows not counted."""
+    elt = 2 if s.dtype == "bf16" else 4
+    hid = s.Hq * s.d
+    byts = flops = 0
+    for b in range(len(n)):
+        if not gate[b]:
+            continue
+        L = cand_len[b].astype(np.int64)
+        r_real = 1 + int(L.sum())
+        byts += int(n[b]) * s.Hkv * s.d * 2 * elt + 2 * r_real * hid * elt + int(L.sum()) * s.Hkv * s.d * 2 * elt
+        flops += 4 * s.Hq * s.d * (r_real * int(n[b]) + int((L * (L + 1) // 2).sum()))
+    return byts, float(flops)
+
+
+def roofline(byts, flops, ms, dtype, kernel):
+    """The bound a stage's algorithmic bytes and flops put on it, and where the
+    measured time sits against that bound's peak."""
+    if ms <= 0 or (byts == 0 and flops == 0):
+        return None
+    peak_f = MFMA_BF16_PEAK_TFS if dtype == "bf16" else FP32_PEAK_TFS
+    gbs = byts / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    if byts / (HBM_PEAK_GBS * 1e9) >= flops / (peak_f * 1e12):
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        r = {"bound": "mfma", "achieved": round(tfs, 1), "peak": peak_f, "unit": "TFLOP/s",
+             "frac": round(tfs / peak_f, 4)}
+    r.update({"kernel": kernel, "kernel_ms": round(ms, 4), "algorithmic_bytes": int(byts),
+              "algorithmic_flops": flops, "tflops": round(tfs, 1), "gbs": round(gbs, 1)})
+    return r
+
+
+class StepRunner:
+    """One copy step of a workload on the device: probe -> retrieve -> verify
+    (attention, LM head, argmax) -> accept, all on one stream, every output and the
+    workspace allocated once.  With events, the stage boundaries are recorded."""
+
+    def __init__(self, wl, tensors, stream, temperature=0.0, seed=0):
+        import torch
+        import copy_draft_verification_amd as cdv
+        from workloads import to_torch
+        self.cdv, self.wl, self.stream, self.T, self.seed = cdv, wl, stream, temperature, seed
+        s = wl.spec
+        dev = "cuda:0"
+        up = lambda x: to_torch(x, dev)  # noqa: E731
+        self.ids, self.cu, self.h, self.w = up(wl.ids), up(wl.cu_len), up(wl.h), up(wl.w)
+        t = tensors
+        self.q, self.kp, self.vp, self.kc, self.vc = t["q"], t["k_pre"], t["v_pre"], t["k_cand"], t["v_cand"]
+        lm = t["lm_head"]
+        self.lm = cdv.pack_weight(lm, stream=stream) if lm.dtype == torch.bfloat16 else lm
+        B, R = s.B, wl.R
+        tdt = self.q.dtype
+        self.z = torch.empty(B, dtype=torch.float32, device=dev)
+        self.fire = torch.empty(B, dtype=torch.uint8, device=dev)
+        self.kout = {"match_end": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+                     "n_match": torch.empty(B, dtype=torch.int32, device=dev),
+                     "cand": torch.empty(B, s.W, s.D, dtype=torch.int32, device=dev),
+                     "cand_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+                     "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev)}
+        self.attn = torch.empty(B, R, s.Hq * s.d, dtype=tdt, device=dev)
+        self.am = torch.empty(B, R, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(cdv.verify_workspace_bytes(B, wl.max_n, s.W, s.D, s.Hq, s.Hkv, s.d, s.V, tdt),
+                              dtype=torch.uint8, device=dev)
+        self.aout = {"accept_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
+                     "best_w": torch.empty(B, dtype=torch.int32, device=dev),
+                     "best_len": torch.empty(B, dtype=torch.int32, device=dev),
+                     "next_token": torch.empty(B, dtype=torch.int32, device=dev)}
+        if temperature > 0:
+            self.srows = {"n_children": torch.empty(B, R, dtype=torch.int32, device=dev),
+                          "children": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
+                          "child_w": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
+                          "child_logit": torch.empty(B, R, s.W, dtype=torch.float32, device=dev),
+                          "lse": torch.empty(B, R, dtype=torch.float32, device=dev),
+                          "resample": torch.empty(B, R, dtype=torch.int32, device=dev)}
+
+    @staticmethod
+    def events(n):
+        """n sets of stage events (e0 probe e1 kgram e2 attention [lm0 LM head lm1]
+        reduce e3 accept e4), each recorded once here so that torch creates them."""
+        import torch
+        sets = []
+        for _ in range(n):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            for e in ev:
+                e.record()
+            sets.append(ev)
+        return sets
+
+    def step(self, ev=None, i=0):
+        cdv, s, st = self.cdv, self.wl.spec, self.stream
+        rec = (lambda k: ev[k].record(st)) if ev is not None else (lambda k: None)
+        lm_ev = (ev[3], ev[4]) if ev is not None else None
+        rec(0)
+        cdv.probe_score(self.h, self.w, s.tau, z_out=self.z, fire_out=self.fire, stream=st)
+        rec(1)
+        cdv.kgram_retrieve(self.ids, self.cu, s.kappa, s.W, s.D, self.fire, out=self.kout, stream=st)
+        rec(2)
+        wl = self.wl
+        if self.T > 0:
+            seed = self.seed + i
+            cdv.blocktri_verify_sample(self.q, self.kp, self.vp, self.cu, wl.max_n, self.kc, self.vc,
+                                       self.kout["cand"], self.kout["cand_len"], self.kout["copy_gate"],
+                                       self.lm, s.W, s.D, wl.scale, self.T, seed, attn_out=self.attn,
+                                       rows=self.srows, workspace=self.ws, events=lm_ev, stream=st)
+            rec(5)
+            cdv.accept_sample(self.srows, self.kout["copy_gate"], s.W, s.D, seed,
+                              out={k: self.aout[k] for k in ("best_w", "best_len", "next_token")},
+                              stream=st)
+        else:
+            cdv.blocktri_verify(self.q, self.kp, self.vp, self.cu, wl.max_n, self.kc, self.vc,
+                                self.kout["cand_len"], self.kout["copy_gate"], self.lm, s.W, s.D,
+                                wl.scale, attn_out=self.attn, argmax_out=self.am, workspace=self.ws,
+                                events=lm_ev, stream=st)
+            rec(5)
+            cdv.accept_longest(self.kout["cand"], self.kout["cand_len"], self.kout["copy_gate"], self.am,
+                               s.W, s.D, out=self.aout, stream=st)
+        rec(6)
+
+
+def stage_times(ev):
+    """Stage durations (ms) of one step from its events."""
+    t = lambda a, b: ev[a].elapsed_time(ev[b])  # noqa: E731
+    return {"probe": t(0, 1), "kgram_retrieve": t(1, 2), "attention": t(2, 3), "lm_head": t(3, 4),
+            "reduce": t(4, 5), "accept": t(5, 6), "step": t(0, 6)}
+
+
+def pct(x):
+    x = np.asarray(x, dtype=np.float64)
+    return {"p10": round(float(np.percentile(x, 10)), 4), "p50": round(float(np.percentile(x, 50)), 4),
+            "p90": round(float(np.percentile(x, 90)), 4), "mean": round(float(x.mean()), 4)}
+
+
+def measure(runner, steps, warmup, flush):
+    """warmup untimed steps; then `steps` steps back to back between two events (the
+    driver's bracket); then `steps` steps each timed by its own stage events, with
+    the last-level cache flushed before each step, outside its events."""
+    import torch
+    st = runner.stream
+    for i in range(warmup):
+        runner.step(None, i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for i in range(steps):
+        runner.step(None, i)
+    t1.record(st)
+    torch.cuda.synchronize()
+    b2b = t0.elapsed_time(t1) / steps
+    evs = runner.events(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.add_(1)
+        runner.step(evs[i], i)
+    torch.cuda.synchronize()
+    per = [stage_times(e) for e in evs]
+    out = {k: pct([p[k] for p in per]) for k in per[0]}
+    out["back_to_back_ms"] = round(b2b, 4)
+    return out
+
+
+def step_result(runner, tm):
+    """Throughput and rooflines of a measured workload."""
+    s, wl = runner.wl.spec, runner.wl
+    gate = runner.kout["copy_gate"].cpu().numpy().astype(bool)
+    cl = runner.kout["cand_len"].cpu().numpy()
+    n = np.diff(wl.cu_len)
+    sum_L = int(cl[gate].sum())
+    R_tot = int(gate.sum()) + sum_L
+    ms = tm["step"]["p50"]
+    lm_bytes, lm_flops = lm_algorithmic(s, R_tot)
+    at_bytes, at_flops = attn_algorithmic(s, n, gate, cl)
+    kname = ("lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel") + ("<sample>" if runner.T > 0 else "")
+    aname = "attn_prefix_bf16_kernel+attn_merge_bf16_kernel" if s.dtype == "bf16" else "attn_prefix_f32_kernel+attn_merge_kernel"
+    return {"workload": s.name, "B": s.B, "anchor": s.anchor, "gates": int(gate.sum()), "sum_L": sum_L,
+            "copy_steps_per_s": round(s.B / (ms * 1e-3), 2),
+            "verified_cand_tokens_per_s": round(sum_L / (ms * 1e-3), 1),
+            "step_ms": tm["step"], "step_us_p50": round(1000 * ms, 2),
+            "back_to_back_ms": tm["back_to_back_ms"],
+            "stages_ms_p50": {k: tm[k]["p50"] for k in STAGES},
+            "lm_head_roofline": roofline(lm_bytes, lm_flops, tm["lm_head"]["p50"], s.dtype, kname),
+            "attention_roofline": roofline(at_bytes, at_flops, tm["attention"]["p50"], s.dtype, aname)}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -560,146 +810,96 @@ def main():
         bench_forward(a)
         return
     import torch
-    import copy_draft_verification_amd as cdv
-    from workloads import generate, to_torch
+    from workloads import device_tensors, generate, to_torch
 
     over = {k: v for k, v in (("anchor", a.anchor), ("W", a.W), ("D", a.D)) if v is not None}
     wl = generate(a.workload, **over)
     s = wl.spec
     dev = "cuda:0"
-    up = lambda x: to_torch(x, dev)  # noqa: E731
-    ids, cu, h, w = up(wl.ids), up(wl.cu_len), up(wl.h), up(wl.w)
-    q, kp, vp, kc, vc, lm = (up(wl.q), up(wl.k_pre), up(wl.v_pre), up(wl.k_cand), up(wl.v_cand),
-                             up(wl.lm_head))
-    B, R = s.B, wl.R
-    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
-    if tdt == torch.bfloat16:
-        lm = cdv.pack_weight(lm)   # packed once, as at model load (outside the timed region)
-    # every output and the workspace are allocated once, outside the timed region
-    z = torch.empty(B, dtype=torch.float32, device=dev)
-    fire = torch.empty(B, dtype=torch.uint8, device=dev)
-    kout = {"match_end": torch.empty(B, s.W, dtype=torch.int32, device=dev),
-            "n_match": torch.empty(B, dtype=torch.int32, device=dev),
-            "cand": torch.empty(B, s.W, s.D, dtype=torch.int32, device=dev),
-            "cand_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
-            "copy_gate": torch.empty(B, dtype=torch.uint8, device=dev)}
-    attn = torch.empty(B, R, s.Hq * s.d, dtype=tdt, device=dev)
-    am = torch.empty(B, R, dtype=torch.int32, device=dev)
-    ws = torch.empty(cdv.verify_workspace_bytes(B, wl.max_n, s.W, s.D, s.Hq, s.Hkv, s.d, s.V, tdt),
-                     dtype=torch.uint8, device=dev)
-    aout = {"accept_len": torch.empty(B, s.W, dtype=torch.int32, device=dev),
-            "best_w": torch.empty(B, dtype=torch.int32, device=dev),
-            "best_len": torch.empty(B, dtype=torch.int32, device=dev),
-            "next_token": torch.empty(B, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream()
-    T = a.temperature
-    if T > 0:
-        srows = {"n_children": torch.empty(B, R, dtype=torch.int32, device=dev),
-                 "children": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
-                 "child_w": torch.empty(B, R, s.W, dtype=torch.int32, device=dev),
-                 "child_logit": torch.empty(B, R, s.W, dtype=torch.float32, device=dev),
-                 "lse": torch.empty(B, R, dtype=torch.float32, device=dev),
-                 "resample": torch.empty(B, R, dtype=torch.int32, device=dev)}
-
-    def step(lm_events=None, i=0):
-        cdv.probe_score(h, w, s.tau, z_out=z, fire_out=fire, stream=stream)
-        cdv.kgram_retrieve(ids, cu, s.kappa, s.W, s.D, fire, out=kout, stream=stream)
-        if T > 0:
-            seed = a.seed + i
-            cdv.blocktri_verify_sample(q, kp, vp, cu, wl.max_n, kc, vc, kout["cand"],
-                                       kout["cand_len"], kout["copy_gate"], lm, s.W, s.D, wl.scale,
-                                       T, seed, attn_out=attn, rows=srows, workspace=ws,
-                                       events=lm_events, stream=stream)
-            cdv.accept_sample(srows, kout["copy_gate"], s.W, s.D, seed,
-                              out={k: aout[k] for k in ("best_w", "best_len", "next_token")},
-                              stream=stream)
-            return
-        cdv.blocktri_verify(q, kp, vp, cu, wl.max_n, kc, vc, kout["cand_len"], kout["copy_gate"], lm,
-                            s.W, s.D, wl.scale, attn_out=attn, argmax_out=am, workspace=ws,
-                            events=lm_events, stream=stream)
-        cdv.accept_longest(kout["cand"], kout["cand_len"], kout["copy_gate"], am, s.W, s.D,
-                           out=aout, stream=stream)
-
-    print(f"[bench] workload={s.name} B={B} n={np.diff(wl.cu_len).tolist()[:4]} V={s.V} "
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    tens = {k: to_torch(getattr(wl, k), dev) for k in ("q", "k_pre", "v_pre", "k_cand", "v_cand", "lm_head")}
+    runner = StepRunner(wl, tens, stream, a.temperature, a.seed)
+    del tens
+    print(f"[bench] workload={s.name} B={s.B} n={np.diff(wl.cu_len).tolist()[:4]} V={s.V} "
           f"warmup={a.warmup} steps={a.steps}", file=sys.stderr, flush=True)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    lm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(a.steps)]
-    # torch creates an event on its first record(): record each pair once here, outside
-    # the timed region, so that the library can record the handles around the kernel
-    for e0, e1 in lm_ev:
-        e0.record(stream)
-        e1.record(stream)
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(a.steps):
-        step(lm_ev[i], i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms = t_begin.elapsed_time(t_end) / a.steps
-    lm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in lm_ev]))
-    gate = kout["copy_gate"].cpu().numpy().astype(bool)
-    cl = kout["cand_len"].cpu().numpy()
-    sum_L = int(cl[gate].sum())
-    R_tot = int(gate.sum()) + sum_L
-    print(f"[bench] {ms:.4f} ms/step, lm-head kernel {lm_ms:.4f} ms, gates={int(gate.sum())} "
-          f"sumL={sum_L}", file=sys.stderr, flush=True)
+    tm = measure(runner, a.steps, a.warmup, flush)
+    head = step_result(runner, tm)
+    ms = tm["step"]["p50"]
+    print(f"[bench] {s.name}: step p50 {ms:.4f} ms (p10 {tm['step']['p10']:.4f}, p90 "
+          f"{tm['step']['p90']:.4f}; back to back {tm['back_to_back_ms']:.4f}), stages "
+          f"{head['stages_ms_p50']}", file=sys.stderr, flush=True)
+    roof = dict(head["lm_head_roofline"]) if head["lm_head_roofline"] else None
+    if roof is not None:
+        # the committed counters were taken on the workload's own full anchors and W, D
+        from workloads import spec as base_spec
+        b0 = base_spec(s.name)
+        same = (s.anchor, s.W, s.D) == (b0.anchor, b0.W, b0.D)
+        roof["traffic"] = (measured_traffic(s.name, SAMPLE_TRAFFIC_FILE if a.temperature > 0 else TRAFFIC_FILE)
+                           if same else None)
+    del runner
+    torch.cuda.empty_cache()
 
-    lm_bytes, lm_flops = lm_algorithmic(s, R_tot)
-    # the contraction runs over every row of the batch (B*R), padded rows included;
-    # the algorithmic figures count real rows only
-    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
-    tflops = lm_flops / (lm_ms * 1e-3) / 1e12
-    mfma_peak = MFMA_BF16_PEAK_TFS if s.dtype == "bf16" else FP32_PEAK_TFS
-    hbm_time = lm_bytes / (HBM_PEAK_GBS * 1e9)
-    mfma_time = lm_flops / (mfma_peak * 1e12)
-    if hbm_time >= mfma_time:
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": round(tflops / mfma_peak, 4)}
-    # the committed counters were taken on the workload's own full anchors and W, D
-    from workloads import spec as base_spec
-    b0 = base_spec(s.name)
-    same = (s.anchor, s.W, s.D) == (b0.anchor, b0.W, b0.D)
-    roof.update({"traffic": measured_traffic(s.name, SAMPLE_TRAFFIC_FILE if T > 0 else TRAFFIC_FILE)
-                 if same else None,
-                 "kernel": ("lmhead_bf16_kernel" if s.dtype == "bf16" else "lmhead_f32_kernel") +
-                           ("<sample>" if T > 0 else ""),
-                 "kernel_ms": round(lm_ms, 4), "algorithmic_bytes": int(lm_bytes),
-                 "algorithmic_flops": lm_flops, "mfma_tflops": round(tflops, 1)})
+    configs = []
+    if not a.no_configs and a.temperature == 0 and not over and a.workload == "llama8b_b1":
+        for name in CONFIG_WORKLOADS:
+            cw = generate(name, with_tensors=(name == "tiny"))
+            if name == "tiny":
+                tens = {k: to_torch(getattr(cw, k), dev) for k in ("q", "k_pre", "v_pre", "k_cand", "v_cand", "lm_head")}
+            else:
+                tens = device_tensors(cw, dev)
+            r = StepRunner(cw, tens, stream)
+            del tens
+            steps = a.steps if name == "tiny" else min(a.steps, a.config_steps)
+            print(f"[bench] config {name} B={cw.spec.B} steps={steps}", file=sys.stderr, flush=True)
+            ctm = measure(r, steps, min(a.warmup, 5), flush)
+            res = step_result(r, ctm)
+            res["steps"] = steps
+            res["inputs"] = "host seeded generator" if name == "tiny" else "device seeded generator (same laws)"
+            configs.append(res)
+            print(f"[bench] config {name}: step p50 {ctm['step']['p50']:.4f} ms, "
+                  f"{res['copy_steps_per_s']} copy-steps/s", file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
 
     cpu = None
-    if not a.no_cpu_baseline and T == 0:
+    if not a.no_cpu_baseline and a.temperature == 0:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, a.cpu_budget_s)
+        cpu = cpu_baseline(wl, a.cpu_budget_s, head["stages_ms_p50"])
 
     line = {
         "metric": "copy-steps/sec & verified cand tokens/sec @8B shape; % HBM/MFMA peak",
-        "value": round(B / (ms * 1e-3), 2),
+        "value": head["copy_steps_per_s"],
         "unit": "copy-steps/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_p10": tm["step"]["p10"],
+        "ms_per_step_p90": tm["step"]["p90"],
+        "ms_per_step_back_to_back": tm["back_to_back_ms"],
+        "timing": ("each step between its own HIP events, the 256 MB last-level cache flushed "
+                   "(a 512 MiB buffer rewritten) before each step, outside its events; value = "
+                   "B / median step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": s.dtype,
         "data": "synthetic",
-        "config": {"workload": s.name, "anchor": s.anchor, "B": B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
+        "config": {"workload": s.name, "anchor": s.anchor, "B": s.B, "n": [int(x) for x in np.diff(wl.cu_len)[:4]],
                    "hid": s.hid, "Hq": s.Hq, "Hkv": s.Hkv, "d": s.d, "V": s.V, "kappa": s.kappa,
-                   "W": s.W, "D": s.D, "tau": s.tau, "temperature": T, "parallelism": "single-gpu"},
-        "verified_cand_tokens_per_s": round(sum_L / (ms * 1e-3), 1),
+                   "W": s.W, "D": s.D, "tau": s.tau, "temperature": a.temperature, "parallelism": "single-gpu"},
+        "verified_cand_tokens_per_s": head["verified_cand_tokens_per_s"],
+        "stages_ms_p50": head["stages_ms_p50"],
         "roofline": roof,
+        "attention_roofline": head["attention_roofline"],
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+CONFIG_WORKLOADS = ("tiny", "llama8b_b32", "qwen3_8b_b8", "llama70b_b4")
 
 
 if __name__ == "__main__":

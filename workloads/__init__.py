@@ -14,11 +14,12 @@ trigger rates of its Table 1 set the planted-repeat densities; no dataset item
 of any benchmark is used.
 """
 from .gen import (CALIB_CONFIGS, CONFIGS, FWD_CONFIGS, SCAN_N, SCAN_SIZES, CalibWorkload,
-                  FwdWorkload, Workload, f32_to_bf16_bits, generate, generate_calibration,
+                  FwdWorkload, Workload, device_tensors, f32_to_bf16_bits, generate, generate_calibration,
                   generate_forward, generate_with_ids, scan_ids_device, scan_ids_planted, spec,
                   to_torch)
 
 __all__ = ["CALIB_CONFIGS", "CONFIGS", "FWD_CONFIGS", "CalibWorkload", "FwdWorkload", "Workload",
+           "device_tensors",
            "f32_to_bf16_bits", "generate", "generate_calibration", "generate_forward",
            "generate_with_ids", "SCAN_N", "SCAN_SIZES", "scan_ids_device", "scan_ids_planted",
            "spec", "to_torch"]

@@ -348,6 +348,33 @@ def generate(name_or_spec, with_tensors=True, **overrides):
     return Workload(s, ids, cu, copy_pos, h, w, **t)
 
 
+def device_tensors(wl, device="cuda"):
+    """The float tensors of workload `wl` (q, k_pre, v_pre, k_cand, v_cand, lm_head)
+    drawn on `device` by torch's generator seeded with the workload's seed, with the
+    laws `generate` uses: N(0, q_scale^2) queries, N(0, 1) keys and values,
+    N(0, lm_std^2) LM-head weights, in float32 and rounded once to bfloat16 for bf16
+    workloads.  Same shapes and laws as the host draws, not the same values: for
+    timing runs whose host generation would take longer than the measurement."""
+    import torch
+    s = wl.spec
+    g = torch.Generator(device=device)
+    g.manual_seed(s.seed)
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    R, N = 1 + s.W * s.D, int(wl.cu_len[-1])
+
+    def draw(shape, std):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        return x.to(dt)
+
+    return {"q": draw((s.B, R, s.Hq, s.d), s.q_scale),
+            "k_pre": draw((N, s.Hkv, s.d), 1.0), "v_pre": draw((N, s.Hkv, s.d), 1.0),
+            "k_cand": draw((s.B, s.W * s.D, s.Hkv, s.d), 1.0),
+            "v_cand": draw((s.B, s.W * s.D, s.Hkv, s.d), 1.0),
+            "lm_head": draw((s.V, s.hid), s.lm_std)}
+
+
 def to_torch(arr, device):
     """numpy -> torch on `device`; uint16 arrays are reinterpreted as bfloat16."""
     import torch
