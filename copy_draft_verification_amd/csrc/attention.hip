@@ -21,55 +21,361 @@ namespace ssd {
 // ----------------------------------------------------------------- bf16 MFMA
 constexpr int kAttD = 128;          // head dim of the MFMA path
 constexpr int kKB = 64;             // keys per LDS block
-constexpr int kKStride = kAttD + 8; // bf16 per K row in LDS (272 B: conflict-free b128 reads)
-constexpr int kAttRowsPerBlock = 128;
+constexpr int kAttWaves = 8;        // one 32-row MFMA tile per wave, two waves per SIMD
+constexpr int kAttThreads = kAttWaves * kWave;
+constexpr int kAttRowsPerBlock = kAttWaves * 32;                 // 256 (row, head) rows
+constexpr int kStage = kKB * kAttD;                              // bf16 per K or V stage (16 KB)
+constexpr int kDmaPerWave = kStage * 2 / 16 / kWave / kAttWaves; // 16-byte copies per wave and stage (2)
 constexpr int kXcds = 8;            // workgroups are dealt round-robin over the 8 XCDs
-constexpr float kLazyRescale = 8.f; // the running max moves only when exceeded by 2^8
-constexpr int kAttAhead = 4;        // LDS fragment reads in flight ahead of their MFMA
-constexpr int kAttIssueAt = 2;      // S MFMA after which the next block's loads start
+constexpr float kFreeRange = 32.f;  // scores may exceed the running max by 2^32 before it moves
+constexpr float kLazyRescale = 8.f; // masked blocks: the running max moves when exceeded by 2^8
+constexpr int kAhead = 2;           // LDS fragment reads in flight ahead of their MFMA
+constexpr int kOutOfRange = 0x7ffffff0;
 
-// V^T in LDS: row d holds the block's 64 keys (128 B, no padding) as sixteen 8-byte
-// units of 4 keys; unit u sits at position u ^ vt_swz(d).  With this swizzle both the
-// transposing writes (16 lanes = 16 rows d = 8*dc + e, one unit) and the MFMA
-// A-operand reads (32 lanes = 32 consecutive rows, one unit) hit distinct banks.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 15; }
+// LDS layouts (16-byte chunks, 16 per 256-byte key row, no padding).  The LDS
+// serves 64 banks of 4 bytes (256 bytes) per cycle and a 256-byte row starts at
+// bank 0, so the accesses served together must fall on distinct chunk positions:
+//  * K: chunk c of key k sits at position c ^ (k & 15).  The S MFMA's A operand
+//    reads one chunk of 32 consecutive keys; every 16 consecutive lanes hit the 16
+//    positions of a row once.
+//  * V: chunk c of key k sits at position c ^ 4(k & 3).  A transposing read of the
+//    O MFMA's A operand takes, per half wave, the four chunks of a 32-wide d tile
+//    of 4 consecutive keys; the 16 chunks land on the 16 positions once.
+__device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
+__device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 3) << 2); }
 
-// One workgroup = 128 query rows (the g query heads of one KV head packed together)
-// x one key range of one sequence.  Key ranges ("slots") 0..nsplit-1 split the
-// prefix; slot nsplit holds the W*D candidate keys, where row (w, j) may only see
-// keys (w, 0..j): that mask is evaluated in registers from the key and row
-// indices.  Each slot leaves a partial (running max m, sum l, unnormalised o) in
-// the workspace, in the exp2 domain; the merge kernel combines them.
+using v4i16 = __attribute__((ext_vector_type(4))) short;
+using lds_v4i16 = __attribute__((address_space(3))) v4i16;
+using bf16x2 = __attribute__((ext_vector_type(2))) __bf16;
+
+// What one wave needs to stream the workgroup's key range.
+struct AttnCtx {
+  __amdgpu_buffer_rsrc_t kres, vres;
+  int key_bytes, kvo;        // bytes per key (all kv heads), this kv head's byte offset
+  int k0;                    // first key of the range
+  int wave, lane, l32, h;
+};
+
+// Copy keys key0 .. key0+63 of K (or V) into an LDS stage: this wave's share, two
+// 1 KB copies.  Unit p of the stage (16 bytes) is key p / 16 at position p % 16;
+// it receives that key's chunk at the position (the swizzles are involutions).
+template <bool kV>
+__device__ __forceinline__ void dma_stage(const AttnCtx& c, uint16_t* st, int key0, bool past) {
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; ++u) {
+    const int p = (c.wave * kDmaPerWave + u) * kWave + c.lane;
+    const int key = p >> 4, pos = p & 15;
+    const int ch = kV ? v_pos(key, pos) : k_pos(key, pos);
+    const int off = (key0 + key) * c.key_bytes + c.kvo + ch * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kV ? c.vres : c.kres,
+        (__attribute__((address_space(3))) void*)(st + (c.wave * kDmaPerWave + u) * kWave * 8), 16,
+        past ? kOutOfRange : off, 0, 0, 0);
+  }
+}
+
+// S MFMA A operand: keys 32 kt + l32, d chunk 2 s + h (d 16 s + 8 h .. + 7).
+__device__ __forceinline__ bf16x8 k_frag(const uint16_t* st, int i, int l32, int h) {
+  const int kt = i & 1, s = i >> 1;
+  const int key = kt * 32 + l32;
+  return *reinterpret_cast<const bf16x8*>(st + key * kAttD + k_pos(key, 2 * s + h) * 8);
+}
+
+// O MFMA A operand V^T for key step ks (16 keys) and d tile dt: lane (l32, h) gets d
+// = 32 dt + l32 and keys 16 ks + {4h .. 4h+3, 8+4h .. 8+4h+3}, the order in which the
+// S accumulator holds them (elements 8 s2 .. 8 s2 + 7 of subtile ks / 2, s2 = ks % 2).
+// Two transposing reads: in read t, 16-lane group G sends lane 4e + c to key
+// 16 ks + 8 t + 4 (G >> 1) + e, d 32 dt + 16 (G & 1) + 4 c .. + 3; the read returns to
+// lane i of the group column i & 3 of lanes (i >> 2) + 4e, e = 0..3.
+__device__ __forceinline__ bf16x8 v_frag(const uint16_t* st, int ks, int dt, int lane) {
+  const int G = lane >> 4, i = lane & 15, e = i >> 2, cc = i & 3;
+  const int d0 = dt * 32 + 16 * (G & 1) + 4 * cc;
+  const int ch = d0 >> 3, sub = d0 & 7;
+  v4i16 r[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = ks * 16 + 8 * t + 4 * (G >> 1) + e;
+    r[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(st + key * kAttD + v_pos(key, ch) * 8 + sub));
+  }
+  struct Two { v4i16 a, b; } two{r[0], r[1]};
+  return __builtin_bit_cast(bf16x8, two);
+}
+
+// The wave's tile: 32 (row, head) rows.
+struct AttnRows {
+  bf16x8 q[8];            // B operand of S^T = K Q^T: Q[row][16 s + 8 h .. + 7]
+  f32x16 o[4];            // O^T[d][row], d tile dt
+  float m, l;             // running max (scaled, base 2) and this lane's half of the sum
+  float alpha;            // pending rescale of o (applied before the next O MFMAs)
+  bool pend;
+};
+
+// Row maximum of a block of scores (both halves of the row), scaled.
+__device__ __forceinline__ float block_max(const f32x16 (&s)[2], float scale) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  return mx * scale;   // scale > 0: the max commutes with it
+}
+
+// Moves the running max when the block's scores exceed it by more than 2^range
+// (always for the first block with a visible key): l is rescaled at once, o before
+// it next accumulates (O MFMAs still pending use the old max).
+__device__ __forceinline__ void move_max(AttnRows& R, float mb, float range) {
+  const bool need = mb > R.m + range || (R.m == -INFINITY && mb != -INFINITY);
+  if (__ballot(need)) {
+    const float m_new = need ? mb : R.m;
+    const float a = R.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(R.m - m_new);
+    R.m = m_new;
+    R.l *= a;
+    R.alpha = R.pend ? R.alpha * a : a;
+    R.pend = true;
+  }
+}
+
+__device__ __forceinline__ void apply_pending(AttnRows& R) {
+  if (R.pend) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) R.o[dt][r] *= R.alpha;
+    R.pend = false;
+  }
+}
+
+// p = 2^(scale s - m) in place (a row without a visible key yet has m = -inf: it
+// exponentiates against 0, its scores are -inf and every p is 0).
+__device__ __forceinline__ void exp_in_place(f32x16 (&s)[2], float scale, float m) {
+  const float nm = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale, nm));
+}
+
+// Pack probabilities to the O MFMA's bf16 B operand; returns the sum of the packed
+// values (dot products with (1, 1)), the half-row sum this lane contributes to l.
+__device__ __forceinline__ float pack_p(const f32x16 (&s)[2], bf16x8 (&p)[2][2]) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float sum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const bf16x2 pr = {static_cast<__bf16>(s[kt][8 * s2 + 2 * e2]),
+                           static_cast<__bf16>(s[kt][8 * s2 + 2 * e2 + 1])};
+        w[e2] = __builtin_bit_cast(uint32_t, pr);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
+      }
+      p[kt][s2] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  return sum;
+}
+
+// Scores of keys a row may not see become -inf: keys at or past k1 and, in the
+// candidate slot, keys outside [vis_lo, vis_hi] (the row's own candidate prefix).
+// kb is the block's first key; lane half h holds keys kb + 32 kt + 8 (r / 4) + 4 h + r % 4.
+__device__ __forceinline__ void mask_block(f32x16 (&s)[2], int kb, int k1, int h, bool cand,
+                                           int vis_lo, int vis_hi) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const bool vis = key < k1 && (!cand || (key >= vis_lo && key <= vis_hi));
+      s[kt][r] = vis ? s[kt][r] : -INFINITY;
+    }
+}
+
+// S^T of the tile from one K stage: 16 fragments, one MFMA each.
+__device__ __forceinline__ void s_mfmas(const uint16_t* kst, const AttnRows& R, f32x16 (&s)[2],
+                                        int l32, int h) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+  bf16x8 f[kAhead + 1];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) f[i] = k_frag(kst, i, l32, h);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + kAhead < 16) f[(i + kAhead) % (kAhead + 1)] = k_frag(kst, i + kAhead, l32, h);
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i % (kAhead + 1)], R.q[i >> 1], s[i & 1], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T from one V stage: 16 fragments (4 key steps x 4 d tiles).
+__device__ __forceinline__ void o_mfmas(const uint16_t* vst, AttnRows& R, const bf16x8 (&p)[2][2],
+                                        int lane) {
+  bf16x8 f[kAhead + 1];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) f[i] = v_frag(vst, i >> 2, i & 3, lane);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ks = i >> 2, dt = i & 3;
+    if (i + kAhead < 16) {
+      const int j = i + kAhead;
+      f[j % (kAhead + 1)] = v_frag(vst, j >> 2, j & 3, lane);
+    }
+    R.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i % (kAhead + 1)], p[ks >> 1][ks & 1], R.o[dt], 0, 0, 0);
+  }
+}
+
+// The worker: the wave's tile (kRows) or none (the wave still issues its share of
+// every copy and passes every barrier) over the workgroup's key range.
+//
+// The range's 64-key blocks run in a two-block pipeline.  Iteration j: the running max is
+// checked against block j's scores; then, while the vector ALU exponentiates them,
+// the matrix core runs the O MFMAs of block j-1 and the S MFMAs of block j+1, and
+// block j's probabilities are packed once block j-1's O MFMAs hold no reference to
+// the packed buffer.  Copies: iteration j copies K of block j+4 and V of block j+2
+// (four stages each); K of block j+1 and V of block j-1 are read in iteration j,
+// and a stage is rewritten only after the barrier that follows its last read.
+// Blocks past the last one are copied as zeros (offsets past the buffers) and their
+// products are discarded; keys past the last one of the buffer read as zero too.
+//
+// Masks: in a partial last block of the prefix, keys past the range; in the
+// candidate slot, every key outside the row's own candidate prefix.  Both are
+// applied to the block's scores before the running max sees them.
+template <bool kRows>
+__device__ __forceinline__ void attn_worker(const AttnCtx& c, AttnRows& R, uint16_t* k0s,
+                                            uint16_t* k1s, uint16_t* k2s, uint16_t* k3s,
+                                            uint16_t* v0s, uint16_t* v1s, uint16_t* v2s,
+                                            uint16_t* v3s, int nb, int k1, int vis_lo, int vis_hi,
+                                            bool cand, float scale) {
+  uint16_t* const ks[4] = {k0s, k1s, k2s, k3s};
+  uint16_t* const vs[4] = {v0s, v1s, v2s, v3s};
+  const int k0 = c.k0;
+  auto issue = [&](auto Kc, auto Vc, int xk, int xv) {
+    dma_stage<false>(c, ks[decltype(Kc)::value], k0 + xk * kKB, xk >= nb);
+    dma_stage<true>(c, vs[decltype(Vc)::value], k0 + xv * kKB, xv < 0 || xv >= nb);
+  };
+  constexpr int kPer = 2 * kDmaPerWave;   // copies per wave per issue slot
+  if (nb > 0) {
+    f32x16 s[2][2];                       // scores of block x in s[x % 2]
+    // packed probabilities of the block whose O MFMAs are next; zero for block -1,
+    // whose V stage is zeros
+    bf16x8 p[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int a2 = 0; a2 < 2; ++a2) p[a][a2] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    // issue slots -4 .. -1: K of blocks 0..3, V of blocks -2..1
+    issue(IntC<0>{}, IntC<2>{}, 0, -2);
+    issue(IntC<1>{}, IntC<3>{}, 1, -1);
+    issue(IntC<2>{}, IntC<0>{}, 2, 0);
+    issue(IntC<3>{}, IntC<1>{}, 3, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kPer));
+    lds_barrier();
+    if constexpr (kRows) s_mfmas(k0s, R, s[0], c.l32, c.h);
+    // iteration j (U = j % 4): reads K of j+1 (stage (U+1) % 4), V of j-1 (stage
+    // (U+3) % 4); copies K of j+4 into stage U and V of j+2 into stage (U+2) % 4
+    auto iter = [&](auto Uc, int j) {
+      constexpr int U = decltype(Uc)::value;
+      constexpr int cur = U & 1, nxt = cur ^ 1;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPer));
+      lds_barrier();
+      issue(IntC<U>{}, IntC<(U + 2) % 4>{}, j + 4, j + 2);
+      if constexpr (kRows) {
+        apply_pending(R);                 // a max moved by block j-1: before its O MFMAs
+        const bool live = j < nb;
+        if (live && (cand || k0 + (j + 1) * kKB > k1))
+          mask_block(s[cur], k0 + j * kKB, k1, c.h, cand, vis_lo, vis_hi);
+        if (live) move_max(R, block_max(s[cur], scale), kFreeRange);
+        exp_in_place(s[cur], scale, R.m);
+        o_mfmas(vs[(U + 3) % 4], R, p, c.lane);
+        s_mfmas(ks[(U + 1) % 4], R, s[nxt], c.l32, c.h);
+        const float sum = pack_p(s[cur], p);
+        R.l += live ? sum : 0.f;
+        // schedule: each O MFMA with its fragment's two transposing reads and four
+        // exponentiation instructions, each S MFMA with its fragment read and the
+        // packing of block j's probabilities
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+    };
+    for (int j0 = 0; j0 <= nb; j0 += 4) {
+      iter(IntC<0>{}, j0);
+      if (j0 + 1 > nb) break;
+      iter(IntC<1>{}, j0 + 1);
+      if (j0 + 2 > nb) break;
+      iter(IntC<2>{}, j0 + 2);
+      if (j0 + 3 > nb) break;
+      iter(IntC<3>{}, j0 + 3);
+    }
+    if constexpr (kRows) apply_pending(R);
+    // the copies of blocks past the range still in flight land before the
+    // workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// One workgroup = 256 query rows (the g query heads of one KV head packed together,
+// one tile of 32 per wave) x one key range of one sequence.  Key ranges ("slots")
+// 0..nsplit-1 split the prefix; slot nsplit holds the W*D candidate keys, where row
+// (w, j) may only see keys (w, 0..j).  Each slot leaves a partial (running max m,
+// sum l, unnormalised o) in the workspace, in the exp2 domain; the merge kernel
+// combines them.
 //
 // Grid: the (sequence, kv head, slot) groups are dealt to XCDs so that all row
 // tiles of a group share one XCD's L2 (they read the same keys).  With
-// compact.row_list set, the grid has one more workgroup, the last, which writes
-// the compact list of real rows for the LM head while the others attend.
-__global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
+// compact.row_list set, the grid has one more workgroup, the last, which writes the
+// compact list of real rows for the LM head while the others attend.
+__global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
     const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
     const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ cand_len, int B, int R,
     int Hq, int Hkv, int W, int D, int nsplit, int chunk, int qtiles, float scale_log2,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, LmWsView compact) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kAttD * kKB];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks3[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs3[kStage];
   if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
-    __shared__ int s_cwave[256 / kWave];
-    compact_rows_body<256>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
-                           compact.n_rows, s_cwave);
+    __shared__ int s_cwave[kAttThreads / kWave];
+    compact_rows_body<kAttThreads>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
+                                   compact.n_rows, s_cwave);
     return;
   }
 
-  // XCD-aware decode: block L runs on XCD L % 8; groups g with g % 8 == x run there
+  // XCD-aware decode.  Workgroup L runs on XCD x = L % 8 and takes the (sequence,
+  // kv head) pair bk = 8 q + x: each XCD holds the same kv heads of every sequence,
+  // so the XCDs get equal work whatever the context lengths.  On an XCD the prefix
+  // slots come first and the (short) candidate slots last; the row tiles of one
+  // (pair, slot) are consecutive there and share the XCD's L2 (they read the same
+  // keys).
   const int nslots = nsplit + 1;
-  const int groups = B * Hkv * nslots;
+  const int bkn = B * Hkv, per_x = (bkn + kXcds - 1) / kXcds;
   const int xcd = static_cast<int>(blockIdx.x % kXcds), idx = static_cast<int>(blockIdx.x / kXcds);
   const int qtile = idx % qtiles;
-  const int grp = (idx / qtiles) * kXcds + xcd;
-  if (grp >= groups) return;
-  const int slot = grp % nslots;
-  const int b = (grp / nslots) / Hkv, kvh = (grp / nslots) % Hkv;
+  const int slot = (idx / qtiles) / per_x, qx = (idx / qtiles) % per_x;
+  const int bk = qx * kXcds + xcd;
+  if (slot >= nslots || bk >= bkn) return;
+  const int b = bk / Hkv, kvh = bk % Hkv;
   if (copy_gate[b] == 0) return;
   const int base = cu_len[b];
   const int n_b = cu_len[b + 1] - base;
@@ -89,225 +395,70 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
     kp = k_pre + static_cast<size_t>(base) * Hkv * kAttD;
     vp = v_pre + static_cast<size_t>(base) * Hkv * kAttD;
   }
-  // keys of this sequence (or its candidates).  The key index goes into the
-  // per-lane offset, so keys past the last one fall outside the buffer's range:
-  // they read as zero and never touch the memory after it.
-  const int key_bytes = Hkv * kAttD * 2;
-  const __amdgpu_buffer_rsrc_t kres =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, nkeys * key_bytes, kBufFlags);
-  const __amdgpu_buffer_rsrc_t vres =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), 0, nkeys * key_bytes, kBufFlags);
+  const int nb = (k1 - k0 + kKB - 1) / kKB;   // blocks of the range, the last one maybe partial
 
   const int g = Hq / Hkv, G = R * g;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int h = lane >> 5, l32 = lane & 31;
-  const int i_row = qtile * kAttRowsPerBlock + wave * 32 + l32;  // this lane's query row (B operand column)
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // wave index in a scalar register: the LDS destination of a copy must be wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  AttnCtx c;
+  // keys of this sequence (or its candidates); keys past the last one read as zero
+  // and never touch the memory after it
+  c.key_bytes = Hkv * kAttD * 2;
+  c.kvo = kvh * kAttD * 2;
+  c.kres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, nkeys * c.key_bytes, kBufFlags);
+  c.vres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), 0, nkeys * c.key_bytes, kBufFlags);
+  c.k0 = k0;
+  c.wave = wave;
+  c.lane = lane;
+  c.l32 = lane & 31;
+  c.h = lane >> 5;
+
+  // this wave's tile; a tile whose rows are all padding (candidates past M, tokens
+  // past L_w) does no arithmetic
+  const int i_row = qtile * kAttRowsPerBlock + wave * 32 + c.l32;
   const bool row_ok = i_row < G;
-  const int r_row = row_ok ? i_row / g : 0, hh = row_ok ? i_row - (i_row / g) * g : 0;
-  // A tile whose rows are all padding (candidates past M, tokens past L_w) has
-  // nothing to contribute: the merge reads partials of real rows only.
-  if (!__syncthreads_or(row_ok && real_row(r_row, D, cand_len + static_cast<size_t>(b) * W, true)))
-    return;
+  const int r_row = row_ok ? i_row / g : 0, hh = row_ok ? i_row - r_row * g : 0;
+  const bool row_real = row_ok && real_row(r_row, D, cand_len + static_cast<size_t>(b) * W, true);
+  // a workgroup without a real row has nothing to contribute (the merge reads
+  // partials of real rows only)
+  if (!__syncthreads_or(row_real)) return;
+  const bool has = __ballot(row_real) != 0;
   // candidate mask of this row: keys cw*D .. cw*D + cj (none for the anchor row)
   const int cw = r_row > 0 ? (r_row - 1) / D : -1;
   const int cj = r_row > 0 ? (r_row - 1) - cw * D : -1;
-  // Keys this row may see in this slot: [vis_lo, vis_hi] and below k1.  In the
-  // candidate slot that is its own candidate's keys cw*D .. cw*D + cj (an empty
-  // range for the anchor row); in a prefix slot, every key.
-  const int vis_lo = !cand ? 0 : (cw >= 0 ? cw * D : 1);
-  const int vis_hi = !cand ? INT_MAX : (cw >= 0 ? cw * D + cj : 0);
+  const int vis_lo = cw >= 0 ? cw * D : 1;
+  const int vis_hi = cw >= 0 ? cw * D + cj : 0;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16s + 8h .. +7]
-  bf16x8 qf[8];
+  AttnRows Rw;
+  if (!has) {
+    attn_worker<false>(c, Rw, ks0, ks1, ks2, ks3, vs0, vs1, vs2, vs3, nb, k1, vis_lo, vis_hi, cand,
+                       scale_log2);
+    return;
+  }
   {
-    const uint16_t* qp = q + ((static_cast<size_t>(b) * R + r_row) * Hq + kvh * g + hh) * kAttD + 8 * h;
+    const uint16_t* qp = q + ((static_cast<size_t>(b) * R + r_row) * Hq + kvh * g + hh) * kAttD + 8 * c.h;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-      qf[s] = __builtin_bit_cast(bf16x8, u);
+      Rw.q[s] = __builtin_bit_cast(bf16x8, u);
     }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Rw.o[dt][r] = 0.f;
+    Rw.m = -INFINITY;
+    Rw.l = 0.f;
+    Rw.alpha = 1.f;
+    Rw.pend = false;
   }
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Staging of a 64-key block.  K: thread loads 16 B (d chunk tid%16) of keys
-  // tid/16 + 16c.  V: thread loads d chunk dc = tid%16 of the four keys 4kq..4kq+3,
-  // kq = tid/16, and writes them transposed as eight 8-byte units (one per d).
-  const int koff = ((tid >> 4) * Hkv + kvh) * kAttD * 2 + (tid & 15) * 16;
-  const int kq = tid >> 4, dc = tid & 15;
-  const int voff = ((4 * kq) * Hkv + kvh) * kAttD * 2 + dc * 16;
-  uint4 kreg[4], vreg[4];
-  // A block past the key range (past = true) is "loaded" with an offset beyond both
-  // buffers: zeros, no memory touched, and no branch around the loads.
-  constexpr int kOutOfRange = 0x7ffffff0;
-  auto load_block = [&](int kb, bool past) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      kreg[c] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     kres, past ? kOutOfRange : koff + (kb + 16 * c) * key_bytes, 0, 0));
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      vreg[k] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     vres, past ? kOutOfRange : voff + (kb + k) * key_bytes, 0, 0));
-  };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<uint4*>(&k_lds[((tid >> 4) + 16 * c) * kKStride + (tid & 15) * 8]) = kreg[c];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = dc * 8 + e;
-      const uint32_t w0 = (&vreg[0].x)[e >> 1], w1 = (&vreg[1].x)[e >> 1];
-      const uint32_t w2 = (&vreg[2].x)[e >> 1], w3 = (&vreg[3].x)[e >> 1];
-      uint2 u;
-      if (e & 1) {
-        u.x = (w0 >> 16) | (w1 & 0xffff0000u);
-        u.y = (w2 >> 16) | (w3 & 0xffff0000u);
-      } else {
-        u.x = (w0 & 0xffffu) | (w1 << 16);
-        u.y = (w2 & 0xffffu) | (w3 << 16);
-      }
-      *reinterpret_cast<uint2*>(&vt_lds[d * kKB + 4 * (kq ^ vt_swz(d))]) = u;
-    }
-  };
-
-  load_block(k0, false);
-  for (int kb = k0; kb < k1; kb += kKB) {
-    lds_barrier();  // every wave is done reading the previous block
-    store_block();
-    lds_barrier();  // this block is in LDS
-    // The next block's loads go out from inside the S MFMAs below (one after each
-    // of MFMAs kAttIssueAt .. kAttIssueAt+7), so the first MFMAs after the barrier
-    // wait only on their K fragments: 3-4.5% faster where a workgroup walks many
-    // blocks (batch 32, long contexts).
-    const bool next_past = kb + kKB >= k1;
-
-    // S^T[key][row] for two 32-key subtiles.  The two accumulation chains alternate
-    // (MFMA i works on subtile i % 2, k-step i / 2), and the K fragments are read
-    // kAttAhead MFMAs ahead of their use, so no MFMA waits on its own LDS read.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-    {
-      auto kfrag = [&](int i) {
-        return *reinterpret_cast<const uint4*>(&k_lds[((i & 1) * 32 + l32) * kKStride + 16 * (i >> 1) + 8 * h]);
-      };
-      uint4 kq[kAttAhead + 1];
-#pragma unroll
-      for (int i = 0; i < kAttAhead; ++i) kq[i] = kfrag(i);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i == kAttIssueAt) load_block(kb + kKB, next_past);
-        if (i + kAttAhead < 16) kq[(i + kAttAhead) % (kAttAhead + 1)] = kfrag(i + kAttAhead);
-        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, kq[i % (kAttAhead + 1)]), qf[i >> 1], sacc[i & 1], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, kAttAhead, 0);  // DS reads
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-        if (i + kAttAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i >= kAttIssueAt && i < kAttIssueAt + 8)
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // a global load
-      }
-    }
-    // Online softmax in the exp2 domain; lanes l and l^32 share a row.  Keys past
-    // k1 and candidate keys outside this row's own prefix are masked (only partial
-    // prefix blocks and candidate blocks need the test).
-    float smax = -INFINITY;
-    if (!cand && kb + kKB <= k1) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kt][r]);
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool vis = key < k1 && key >= vis_lo && key <= vis_hi;
-          sacc[kt][r] = vis ? sacc[kt][r] : -INFINITY;
-          smax = fmaxf(smax, sacc[kt][r]);
-        }
-    }
-    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
-    const float m_blk = smax * scale_log2;  // scale > 0: the max commutes with it
-    // Lazy rescale: keep the running max until a block exceeds it by more than 2^8
-    // (probabilities then stay <= 256, exact enough in bf16 and fp32).
-    const bool need = m_blk > m_run + kLazyRescale;
-    if (__ballot(need)) {
-      const float m_new = need ? m_blk : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
-    // a row with no visible key yet keeps m = -inf; exponentiate against 0 then
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    float psum = 0.f;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * s2 + e], scale_log2, neg_m));
-          psum += p;
-          pf[kt][s2][e] = static_cast<__bf16>(p);
-        }
-    l_run += psum;
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; key order of a P fragment element e
-    // for lane half h: kt*32 + 16*s2 + 8*(e/4) + 4*h + e%4 (the S^T output layout),
-    // i.e. 4-key units 8kt + 4s2 + h (e < 4) and that + 2 (e >= 4)
-    // MFMA i = (dt, kt, s2) = (i / 4, i / 2 % 2, i % 2); its two 8-byte V^T reads
-    // are issued kAttAhead MFMAs ahead
-    {
-      auto vfrag = [&](int i) {
-        const int d = (i >> 2) * 32 + l32;
-        const uint16_t* vr = &vt_lds[d * kKB];
-        const int sw = vt_swz(d);
-        const int u0 = 8 * ((i >> 1) & 1) + 4 * (i & 1) + h;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * (u0 ^ sw));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4 * ((u0 + 2) ^ sw));
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
-      };
-      uint4 vq[kAttAhead + 1];
-#pragma unroll
-      for (int i = 0; i < kAttAhead; ++i) vq[i] = vfrag(i);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + kAttAhead < 16) vq[(i + kAttAhead) % (kAttAhead + 1)] = vfrag(i + kAttAhead);
-        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, vq[i % (kAttAhead + 1)]), pf[(i >> 1) & 1][i & 1], oacc[i >> 2], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAttAhead, 0);  // DS reads
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-        if (i + kAttAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-  }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  attn_worker<true>(c, Rw, ks0, ks1, ks2, ks3, vs0, vs1, vs2, vs3, nb, k1, vis_lo, vis_hi, cand,
+                    scale_log2);
+  const float l_tot = Rw.l + __shfl_xor(Rw.l, 32, kWave);
   if (!row_ok) return;
   const size_t po = ((static_cast<size_t>(slot) * B + b) * R + r_row) * Hq + kvh * g + hh;
-  if (h == 0) {
-    ws_m[po] = m_run;
+  if (c.h == 0) {
+    ws_m[po] = Rw.m;
     ws_l[po] = l_tot;
   }
   float* op = ws_o + po * kAttD;
@@ -315,9 +466,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefix_bf16_kernel(
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = dt * 32 + 8 * rq + 4 * h;
+      const int d0 = dt * 32 + 8 * rq + 4 * c.h;
       *reinterpret_cast<float4*>(op + d0) =
-          make_float4(oacc[dt][4 * rq], oacc[dt][4 * rq + 1], oacc[dt][4 * rq + 2], oacc[dt][4 * rq + 3]);
+          make_float4(Rw.o[dt][4 * rq], Rw.o[dt][4 * rq + 1], Rw.o[dt][4 * rq + 2], Rw.o[dt][4 * rq + 3]);
     }
 }
 
@@ -480,18 +631,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
   AttnPlan p;
   const int g = Hq / Hkv;
-  int units, min_keys, target;
   if (bf16) {
+    // One workgroup per CU, 256 CUs.  With little work per CU (under 64 key blocks)
+    // the split is latency-bound: take as many splits as fit, with the candidate
+    // slot, in one round of workgroups.  Otherwise cut the prefix into ranges of at
+    // most 4096 keys: long contexts then spread over more CUs (ragged batches balance,
+    // and units whose rows are all padding, which exit at once, leave the CUs to
+    // the others), at the cost of one more partial slot per range for the merge.
+    constexpr int kCus = 256, kMaxBlocks = 64;
     p.qtiles = (R * g + kAttRowsPerBlock - 1) / kAttRowsPerBlock;
-    units = B * Hkv * p.qtiles;
-    min_keys = 512;
-    target = 512;
-  } else {
-    p.qtiles = (R * Hq + 3) / 4;
-    units = B * p.qtiles;
-    min_keys = 256;
-    target = 1024;
+    const long long units = static_cast<long long>(B) * Hkv * p.qtiles;
+    const int blocks = (max_n + kKB - 1) / kKB;
+    int cap = max_n / 256;
+    if (cap < 1) cap = 1;
+    if (cap > 32) cap = 32;
+    int ns;
+    if (units * blocks < static_cast<long long>(kKB) * kCus) {
+      ns = static_cast<int>(kCus / units) - 1;
+    } else {
+      ns = (blocks + kMaxBlocks - 1) / kMaxBlocks;
+    }
+    if (ns > cap) ns = cap;
+    if (ns < 1) ns = 1;
+    int ch = (max_n + ns - 1) / ns;
+    ch = (ch + kKB - 1) / kKB * kKB;
+    if (ch < kKB) ch = kKB;
+    p.nsplit = ns;
+    p.chunk = ch;
+    p.nslots = ns + 1;  // one more slot for the candidate keys
+    return p;
   }
+  p.qtiles = (R * Hq + 3) / 4;
+  const int units = B * p.qtiles;
+  const int min_keys = 256, target = 1024;
   int ns = (target + units - 1) / units;
   int cap = max_n / min_keys;
   if (cap < 1) cap = 1;
@@ -502,7 +674,7 @@ AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
   if (ch < kKB) ch = kKB;
   p.nsplit = ns;
   p.chunk = ch;
-  p.nslots = bf16 ? ns + 1 : ns;  // bf16: one more slot for the candidate keys
+  p.nslots = ns;
   return p;
 }
 
@@ -527,11 +699,10 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   const size_t items = static_cast<size_t>(B) * R * Hq;
   const dim3 mgrid(static_cast<unsigned>((items + 3) / 4));
   if (bf16) {
-    const int groups = B * Hkv * plan.nslots;
-    const int per_xcd = (groups + kXcds - 1) / kXcds;
+    const int per_xcd = (B * Hkv + kXcds - 1) / kXcds * plan.nslots;
     const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr};
     hipLaunchKernelGGL(attn_prefix_bf16_kernel,
-                       dim3(kXcds * per_xcd * plan.qtiles + (compact != nullptr ? 1 : 0)), dim3(256), 0, s,
+                       dim3(kXcds * per_xcd * plan.qtiles + (compact != nullptr ? 1 : 0)), dim3(kAttThreads), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pre),
                        static_cast<const uint16_t*>(v_pre), cu_len,
                        static_cast<const uint16_t*>(k_cand), static_cast<const uint16_t*>(v_cand),

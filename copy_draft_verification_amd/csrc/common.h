@@ -1,9 +1,13 @@
 // Device helpers shared by the gfx950 kernels of the copy-speculation path.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ssd {
+
+// A compile-time int as a value (selects unrolled steps and stages).
+template <int N> using IntC = std::integral_constant<int, N>;
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;

@@ -69,8 +69,6 @@ constexpr int kLmLoadsPerIter = kLmBlocksPerWave + kLmVA * 4;
 static_assert(kLmBlocks % kLmWaves == 0, "row blocks split evenly over the waves");
 static_assert(kLmLoadsPerIter * 3 <= 63, "vmcnt holds the loads of three iterations");
 
-template <int N> using IntC = std::integral_constant<int, N>;
-
 template <typename F, int... Ts>
 __device__ __forceinline__ void for_each_tile(F& f, std::integer_sequence<int, Ts...>) {
   (f(IntC<Ts>{}), ...);
