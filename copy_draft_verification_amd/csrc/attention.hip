@@ -31,6 +31,7 @@ constexpr float kFreeRange = 32.f;  // scores may exceed the running max by 2^32
 constexpr float kLazyRescale = 8.f; // masked blocks: the running max moves when exceeded by 2^8
 constexpr int kAhead = 2;           // LDS fragment reads in flight ahead of their MFMA
 constexpr int kOutOfRange = 0x7ffffff0;
+constexpr int kPersistCus = 256;    // persistent grid: one workgroup per CU
 
 // LDS layouts (16-byte chunks, 16 per 256-byte key row, no padding).  The LDS
 // serves 64 banks of 4 bytes (256 bytes) per cycle and a 256-byte row starts at
@@ -51,26 +52,35 @@ using bf16x2 = __attribute__((ext_vector_type(2))) __bf16;
 // What one wave needs to stream the workgroup's key range.
 struct AttnCtx {
   __amdgpu_buffer_rsrc_t kres, vres;
-  int key_bytes, kvo;        // bytes per key (all kv heads), this kv head's byte offset
+  int key_bytes;             // bytes per key (all kv heads)
   int k0;                    // first key of the range
   int wave, lane, l32, h;
+  int koff[kDmaPerWave], voff[kDmaPerWave];  // this lane's copy offsets within a block
 };
 
 // Copy keys key0 .. key0+63 of K (or V) into an LDS stage: this wave's share, two
-// 1 KB copies.  Unit p of the stage (16 bytes) is key p / 16 at position p % 16;
-// it receives that key's chunk at the position (the swizzles are involutions).
+// 1 KB copies at the offsets dma_offsets computed.
 template <bool kV>
 __device__ __forceinline__ void dma_stage(const AttnCtx& c, uint16_t* st, int key0, bool past) {
+  const int kb = key0 * c.key_bytes;   // wave-uniform
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kV ? c.vres : c.kres,
+        (__attribute__((address_space(3))) void*)(st + (c.wave * kDmaPerWave + u) * kWave * 8), 16,
+        past ? kOutOfRange : kb + (kV ? c.voff[u] : c.koff[u]), 0, 0, 0);
+}
+
+// This lane's offsets of its copies within a block (see dma_stage): unit p of the
+// stage is key p / 16 at position p % 16, which receives that key's chunk at the
+// position (the swizzles are involutions).
+__device__ __forceinline__ void dma_offsets(AttnCtx& c, int kvo) {
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; ++u) {
     const int p = (c.wave * kDmaPerWave + u) * kWave + c.lane;
     const int key = p >> 4, pos = p & 15;
-    const int ch = kV ? v_pos(key, pos) : k_pos(key, pos);
-    const int off = (key0 + key) * c.key_bytes + c.kvo + ch * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        kV ? c.vres : c.kres,
-        (__attribute__((address_space(3))) void*)(st + (c.wave * kDmaPerWave + u) * kWave * 8), 16,
-        past ? kOutOfRange : off, 0, 0, 0);
+    c.koff[u] = key * c.key_bytes + kvo + k_pos(key, pos) * 16;
+    c.voff[u] = key * c.key_bytes + kvo + v_pos(key, pos) * 16;
   }
 }
 
@@ -329,48 +339,19 @@ __device__ __forceinline__ void attn_worker(const AttnCtx& c, AttnRows& R, uint1
   }
 }
 
-// One workgroup = 256 query rows (the g query heads of one KV head packed together,
-// one tile of 32 per wave) x one key range of one sequence.  Key ranges ("slots")
-// 0..nsplit-1 split the prefix; slot nsplit holds the W*D candidate keys, where row
-// (w, j) may only see keys (w, 0..j).  Each slot leaves a partial (running max m,
-// sum l, unnormalised o) in the workspace, in the exp2 domain; the merge kernel
-// combines them.
-//
-// Grid: the (sequence, kv head, slot) groups are dealt to XCDs so that all row
-// tiles of a group share one XCD's L2 (they read the same keys).  With
-// compact.row_list set, the grid has one more workgroup, the last, which writes the
-// compact list of real rows for the LM head while the others attend.
-__global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
-    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
-    const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
-    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ cand_len, int B, int R,
-    int Hq, int Hkv, int W, int D, int nsplit, int chunk, int qtiles, float scale_log2,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, LmWsView compact) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t ks2[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t ks3[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs2[kStage];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs3[kStage];
-  if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
-    __shared__ int s_cwave[kAttThreads / kWave];
-    compact_rows_body<kAttThreads>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
-                                   compact.n_rows, s_cwave);
-    return;
-  }
-
-  // XCD-aware decode.  Workgroup L runs on XCD x = L % 8 and takes the (sequence,
-  // kv head) pair bk = 8 q + x: each XCD holds the same kv heads of every sequence,
-  // so the XCDs get equal work whatever the context lengths.  On an XCD the prefix
-  // slots come first and the (short) candidate slots last; the row tiles of one
-  // (pair, slot) are consecutive there and share the XCD's L2 (they read the same
-  // keys).
+// One work item (see attn_prefix_bf16_kernel): returns at once when it has nothing
+// to contribute.
+__device__ __forceinline__ void attn_item(
+    int idx, int xcd, uint16_t* ks0, uint16_t* ks1, uint16_t* ks2, uint16_t* ks3, uint16_t* vs0,
+    uint16_t* vs1, uint16_t* vs2, uint16_t* vs3, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_pre, const uint16_t* __restrict__ v_pre,
+    const int32_t* __restrict__ cu_len, const uint16_t* __restrict__ k_cand,
+    const uint16_t* __restrict__ v_cand, const uint8_t* __restrict__ copy_gate,
+    const int32_t* __restrict__ cand_len, int B, int R, int Hq, int Hkv, int W, int D, int nsplit,
+    int chunk, int qtiles, float scale_log2, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o) {
   const int nslots = nsplit + 1;
   const int bkn = B * Hkv, per_x = (bkn + kXcds - 1) / kXcds;
-  const int xcd = static_cast<int>(blockIdx.x % kXcds), idx = static_cast<int>(blockIdx.x / kXcds);
   const int qtile = idx % qtiles;
   const int slot = (idx / qtiles) / per_x, qx = (idx / qtiles) % per_x;
   const int bk = qx * kXcds + xcd;
@@ -405,7 +386,6 @@ __global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
   // keys of this sequence (or its candidates); keys past the last one read as zero
   // and never touch the memory after it
   c.key_bytes = Hkv * kAttD * 2;
-  c.kvo = kvh * kAttD * 2;
   c.kres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), 0, nkeys * c.key_bytes, kBufFlags);
   c.vres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), 0, nkeys * c.key_bytes, kBufFlags);
   c.k0 = k0;
@@ -413,6 +393,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
   c.lane = lane;
   c.l32 = lane & 31;
   c.h = lane >> 5;
+  dma_offsets(c, kvh * kAttD * 2);
 
   // this wave's tile; a tile whose rows are all padding (candidates past M, tokens
   // past L_w) does no arithmetic
@@ -470,6 +451,69 @@ __global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
       *reinterpret_cast<float4*>(op + d0) =
           make_float4(Rw.o[dt][4 * rq], Rw.o[dt][4 * rq + 1], Rw.o[dt][4 * rq + 2], Rw.o[dt][4 * rq + 3]);
     }
+}
+
+// One workgroup = 256 query rows (the g query heads of one KV head packed together,
+// one tile of 32 per wave) x one key range of one sequence.  Key ranges ("slots")
+// 0..nsplit-1 split the prefix; slot nsplit holds the W*D candidate keys, where row
+// (w, j) may only see keys (w, 0..j).  Each slot leaves a partial (running max m,
+// sum l, unnormalised o) in the workspace, in the exp2 domain; the merge kernel
+// combines them.
+//
+// Grid: the (sequence, kv head, slot) groups are dealt to XCDs so that all row
+// tiles of a group share one XCD's L2 (they read the same keys).  With
+// compact.row_list set, the grid has one more workgroup, the last, which writes the
+// compact list of real rows for the LM head while the others attend.
+__global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pre,
+    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_len,
+    const uint16_t* __restrict__ k_cand, const uint16_t* __restrict__ v_cand,
+    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ cand_len, int B, int R,
+    int Hq, int Hkv, int W, int D, int nsplit, int chunk, int qtiles, float scale_log2,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, LmWsView compact,
+    int* __restrict__ work, int items_x) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks3[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs3[kStage];
+  if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
+    __shared__ int s_cwave[kAttThreads / kWave];
+    compact_rows_body<kAttThreads>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
+                                   compact.n_rows, s_cwave);
+    return;
+  }
+
+  // XCD-aware work items.  Workgroup L runs on XCD x = L % 8; item idx of that XCD
+  // is the (sequence, kv head) pair bk = 8 q + x, so each XCD holds the same kv
+  // heads of every sequence and the XCDs get equal work whatever the context
+  // lengths.  On an XCD the prefix slots come first and the (short) candidate slots
+  // last; the row tiles of one (pair, slot) are consecutive and share the XCD's L2
+  // (they read the same keys).  Without `work`, workgroup L takes item L / 8.  With
+  // it (a persistent grid), the workgroups of an XCD take its items in order from
+  // the XCD's counter work[16 x] (zero at launch) until none is left: items with no
+  // real row, or past a context's end, are skipped at once, so the CUs stay busy.
+  __shared__ int s_item;
+  const int xcd = static_cast<int>(blockIdx.x % kXcds);
+  if (work == nullptr) {
+    attn_item(static_cast<int>(blockIdx.x / kXcds), xcd, ks0, ks1, ks2, ks3, vs0, vs1, vs2, vs3, q,
+              k_pre, v_pre, cu_len, k_cand, v_cand, copy_gate, cand_len, B, R, Hq, Hkv, W, D, nsplit,
+              chunk, qtiles, scale_log2, ws_m, ws_l, ws_o);
+    return;
+  }
+  for (;;) {
+    __syncthreads();   // the previous item is done with LDS and with s_item
+    if (threadIdx.x == 0) s_item = atomicAdd(work + 16 * xcd, 1);
+    __syncthreads();
+    const int idx = s_item;
+    if (idx >= items_x) return;
+    attn_item(idx, xcd, ks0, ks1, ks2, ks3, vs0, vs1, vs2, vs3, q, k_pre, v_pre, cu_len, k_cand,
+              v_cand, copy_gate, cand_len, B, R, Hq, Hkv, W, D, nsplit, chunk, qtiles, scale_log2,
+              ws_m, ws_l, ws_o);
+  }
 }
 
 // bf16 merge: one wave per (sequence, row, query head).  Combines the prefix slots
@@ -646,11 +690,15 @@ AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
     if (cap < 1) cap = 1;
     if (cap > 32) cap = 32;
     int ns;
-    if (units * blocks < static_cast<long long>(kKB) * kCus) {
+    const bool latency = units * blocks < static_cast<long long>(kKB) * kCus;
+    if (latency) {
       ns = static_cast<int>(kCus / units) - 1;
     } else {
       ns = (blocks + kMaxBlocks - 1) / kMaxBlocks;
     }
+    // with enough work the items go to a persistent grid (load balance); a single
+    // round of workgroups needs no counters
+    p.persist = latency ? 0 : 1;
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
     int ch = (max_n + ns - 1) / ns;
@@ -675,12 +723,21 @@ AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
   p.nsplit = ns;
   p.chunk = ch;
   p.nslots = ns;
+  p.persist = 0;
   return p;
 }
 
+// Work counters of the persistent grid: one per XCD, 64 bytes apart, after the
+// partials.
+constexpr size_t kWorkBytes = kXcds * 64;
+
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int R, int Hq, int d) {
   const size_t rows = static_cast<size_t>(p.nslots) * B * R * Hq;
-  return rows * sizeof(float) * (2 + static_cast<size_t>(d));
+  return rows * sizeof(float) * (2 + static_cast<size_t>(d)) + kWorkBytes;
+}
+
+__global__ void attn_work_reset_kernel(int* __restrict__ work) {
+  if (threadIdx.x < kXcds) work[16 * threadIdx.x] = 0;
 }
 
 hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
@@ -700,14 +757,21 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   const dim3 mgrid(static_cast<unsigned>((items + 3) / 4));
   if (bf16) {
     const int per_xcd = (B * Hkv + kXcds - 1) / kXcds * plan.nslots;
+    const int items_x = per_xcd * plan.qtiles;
     const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL(attn_prefix_bf16_kernel,
-                       dim3(kXcds * per_xcd * plan.qtiles + (compact != nullptr ? 1 : 0)), dim3(kAttThreads), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pre),
-                       static_cast<const uint16_t*>(v_pre), cu_len,
+    int* work = nullptr;
+    int grid = kXcds * items_x;
+    if (plan.persist) {
+      work = reinterpret_cast<int*>(ws + rows * (2 + static_cast<size_t>(d)));
+      hipLaunchKernelGGL(attn_work_reset_kernel, dim3(1), dim3(kWave), 0, s, work);
+      grid = kPersistCus < grid ? kPersistCus : grid;
+    }
+    hipLaunchKernelGGL(attn_prefix_bf16_kernel, dim3(grid + (compact != nullptr ? 1 : 0)),
+                       dim3(kAttThreads), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_pre), static_cast<const uint16_t*>(v_pre), cu_len,
                        static_cast<const uint16_t*>(k_cand), static_cast<const uint16_t*>(v_cand),
                        copy_gate, cand_len, B, R, Hq, Hkv, W, D, plan.nsplit, plan.chunk, plan.qtiles,
-                       scale_log2, ws_m, ws_l, ws_o, cv);
+                       scale_log2, ws_m, ws_l, ws_o, cv, work, items_x);
     hipLaunchKernelGGL(attn_merge_bf16_kernel, mgrid, dim3(256), 0, s, cu_len, cand_len, copy_gate,
                        B, R, Hq, W, D, plan.nsplit, plan.chunk, ws_m, ws_l, ws_o,
                        static_cast<uint16_t*>(attn_out));

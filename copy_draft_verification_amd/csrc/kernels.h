@@ -24,6 +24,7 @@ struct AttnPlan {
   int chunk;    // keys per split (multiple of 64); the last split runs to n_b
   int qtiles;   // row tiles per (sequence, kv head)
   int nslots;   // partial slots in the workspace (bf16: nsplit + the candidate slot)
+  int persist;  // bf16: a persistent grid takes the work items from per-XCD counters
 };
 AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16);
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int R, int Hq, int d);
