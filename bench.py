@@ -8,12 +8,12 @@ synthetic (seeded) and resident in HBM before timing starts.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
                     [--no-cpu-baseline] [--no-configs] [--config-steps K2]
 
-Protocol: W untimed steps; K steps back to back between two events (reported as
-ms_per_step_back_to_back); then K steps each between its own stage events, with a
-512 MiB buffer rewritten before each step (outside its events) so that no input
-is served from the 256 MB last-level cache.  value = B / the median of those
-steps; p10 / p90 and the per-stage medians (probe, retrieval, attention, LM head,
-argmax reduce, accept) are reported with it.
+Protocol: W untimed steps; K steps between stage events (per-stage medians: probe,
+retrieval, attention, LM head, argmax reduce, accept; this phase also brings the
+GPU clocks up); K steps each between two events, with a 512 MiB buffer rewritten
+before each step (outside its events) so that no input is served from the 256 MB
+last-level cache: value = B / the median of those steps, with p10 / p90; then K
+steps back to back between two events (ms_per_step_back_to_back, warm caches).
 
 Prints one JSON line: copy-steps/s (whole job), verified candidate tokens/s, the
 LM-head and attention roofline positions, the same figures for the tiny, batch-32,
@@ -740,21 +740,20 @@ def pct(x):
 
 
 def measure(runner, steps, warmup, flush):
-    """warmup untimed steps; then `steps` steps back to back between two events (the
-    driver's bracket); then `steps` steps each timed by its own stage events, with
-    the last-level cache flushed before each step, outside its events."""
+    """warmup untimed steps, then three phases of `steps` steps each:
+    * stages: each step between its seven stage events (the per-stage medians; the
+      event records themselves add about 18 us to a step, so this phase gives no
+      step time; it also brings the GPU clocks up, which the first tens of
+      milliseconds of load do not have);
+    * step: each step between two events, the last-level cache flushed before each
+      step outside its events (the step times, p10 / p50 / p90);
+    * back to back: the steps between two events with nothing between them, the
+      driver's bracket (warm caches)."""
     import torch
     st = runner.stream
     for i in range(warmup):
         runner.step(None, i)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(st)
-    for i in range(steps):
-        runner.step(None, i)
-    t1.record(st)
-    torch.cuda.synchronize()
-    b2b = t0.elapsed_time(t1) / steps
     evs = runner.events(steps)
     torch.cuda.synchronize()
     for i in range(steps):
@@ -762,8 +761,26 @@ def measure(runner, steps, warmup, flush):
         runner.step(evs[i], i)
     torch.cuda.synchronize()
     per = [stage_times(e) for e in evs]
-    out = {k: pct([p[k] for p in per]) for k in per[0]}
-    out["back_to_back_ms"] = round(b2b, 4)
+    out = {k: pct([p[k] for p in per]) for k in per[0] if k != "step"}
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in pairs:
+        e0.record(st)
+        e1.record(st)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.add_(1)
+        pairs[i][0].record(st)
+        runner.step(None, i)
+        pairs[i][1].record(st)
+    torch.cuda.synchronize()
+    out["step"] = pct([e0.elapsed_time(e1) for e0, e1 in pairs])
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for i in range(steps):
+        runner.step(None, i)
+    t1.record(st)
+    torch.cuda.synchronize()
+    out["back_to_back_ms"] = round(t0.elapsed_time(t1) / steps, 4)
     return out
 
 
@@ -878,9 +895,9 @@ def main():
         "ms_per_step_p10": tm["step"]["p10"],
         "ms_per_step_p90": tm["step"]["p90"],
         "ms_per_step_back_to_back": tm["back_to_back_ms"],
-        "timing": ("each step between its own HIP events, the 256 MB last-level cache flushed "
+        "timing": ("each step between two HIP events, the 256 MB last-level cache flushed "
                    "(a 512 MiB buffer rewritten) before each step, outside its events; value = "
-                   "B / median step"),
+                   "B / median step; stage medians from a separate pass with stage events"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
