@@ -35,6 +35,10 @@ _SIGS = {
                                            _c_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_int, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
                                            ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "ssd_blocktri_verify_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p,
+                                                   _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, ctypes.c_int, ctypes.c_float, _c_p, _c_p,
+                                                   _c_p, _c_p]),
     "ssd_accept_longest": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p,
                                           _c_p, _c_p, _c_p]),
     "ssd_commit_accepted": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32,
@@ -354,6 +358,29 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
         "blocktri_verify")
+    return attn_out, argmax_out
+
+
+def blocktri_verify_noalloc(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate,
+                            lm_head, W, D, scale, attn_out, argmax_out, logits_out=None, stream=None):
+    """blocktri_verify with no workspace: the library's own device scratch (64 MiB per
+    GPU) holds the partials, so nothing is allocated.  The outputs must be given
+    (attn_out [B, R, Hq*d] of q's dtype, argmax_out [B, R] int32, logits_out [B, R, V]
+    float32 or None).  Calls that overlap on one GPU race on the shared scratch."""
+    B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
+                                      copy_gate, W, D, (torch.float32, torch.bfloat16))
+    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    dev = q.device
+    ts = _torch_stream(stream, dev)
+    _out(attn_out, "attn_out", q.dtype, (B, R, Hq * d), dev)
+    _out(argmax_out, "argmax_out", torch.int32, (B, R), dev)
+    if logits_out is not None:
+        _out(logits_out, "logits_out", torch.float32, (B, R, V), dev)
+    _check(load().ssd_blocktri_verify_noalloc(
+        _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
+        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q), float(scale),
+        _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _torch_stream_handle(ts)),
+        "blocktri_verify_noalloc")
     return attn_out, argmax_out
 
 

@@ -1,6 +1,8 @@
 // C ABI of the copy-speculation path: argument validation, launch planning and
-// dispatch.  No allocation, no synchronisation, no global state.
+// dispatch.  No allocation, no synchronisation; the only global state is the
+// device scratch of ssd_blocktri_verify_noalloc (below).
 #include <cmath>
+#include <mutex>
 
 #include "switchsd.h"
 #include "kernels.h"
@@ -138,15 +140,20 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
   return L.attn_bytes + L.lm_bytes;
 }
 
-ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
-                                 const int32_t* cu_len, int32_t max_n, const void* k_cand,
-                                 const void* v_cand, const int32_t* cand_len,
-                                 const uint8_t* copy_gate, const void* lm_head, int32_t B,
-                                 int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
-                                 int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
-                                 int32_t* argmax_out, float* logits_out, void* workspace,
-                                 size_t workspace_bytes, hipEvent_t lm_begin, hipEvent_t lm_end,
-                                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// ssd_blocktri_verify and its no-allocation variant; the workspace (or the scratch)
+// is resolved by `get_ws` once the layout is known: it returns the buffer, or null
+// with *err set.
+template <typename GetWs>
+ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, const int32_t* cu_len,
+                         int32_t max_n, const void* k_cand, const void* v_cand,
+                         const int32_t* cand_len, const uint8_t* copy_gate, const void* lm_head,
+                         int32_t B, int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                         int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                         int32_t* argmax_out, float* logits_out, GetWs get_ws, hipEvent_t lm_begin,
+                         hipEvent_t lm_end, hipStream_t stream) {
   if (!q || !k_pre || !v_pre || !cu_len || !k_cand || !v_cand || !cand_len || !copy_gate ||
       !lm_head || !attn_out || !argmax_out)
     return SSD_ERR_INVALID_ARG;
@@ -155,7 +162,9 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
   if (st != SSD_OK) return st;
   const bool bf16 = dtype == SSD_BF16;
   const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, bf16);
-  if (!workspace || workspace_bytes < L.attn_bytes + L.lm_bytes) return SSD_ERR_WORKSPACE;
+  ssd_status_t ws_err = SSD_OK;
+  void* workspace = get_ws(L.attn_bytes + L.lm_bytes, &ws_err);
+  if (!workspace) return ws_err;
   float* ws_attn = static_cast<float*>(workspace);
   void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
   const int R = 1 + W * D;
@@ -173,6 +182,82 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
                          lm_begin, lm_end, stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
   return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream));
+}
+
+// The no-allocation variant's scratch: one array per GPU (each device that loads
+// the library holds its own copy until the process ends).  In host code the name
+// `scratch` is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+__device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (null and *err set on failure).
+void* scratch_of_current_device(ssd_status_t* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *err = SSD_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = SSD_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      *err = SSD_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
+                                 const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                 const void* v_cand, const int32_t* cand_len,
+                                 const uint8_t* copy_gate, const void* lm_head, int32_t B,
+                                 int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                                 int32_t* argmax_out, float* logits_out, void* workspace,
+                                 size_t workspace_bytes, hipEvent_t lm_begin, hipEvent_t lm_end,
+                                 hipStream_t stream) {
+  auto get_ws = [&](size_t need, ssd_status_t* err) -> void* {
+    if (!workspace || workspace_bytes < need) {
+      *err = SSD_ERR_WORKSPACE;
+      return nullptr;
+    }
+    return workspace;
+  };
+  return verify_impl(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
+                     B, W, D, Hq, Hkv, d, V, dtype, scale, attn_out, argmax_out, logits_out, get_ws,
+                     lm_begin, lm_end, stream);
+}
+
+ssd_status_t ssd_blocktri_verify_noalloc(const void* q, const void* k_pre, const void* v_pre,
+                                         const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                         const void* v_cand, const int32_t* cand_len,
+                                         const uint8_t* copy_gate, const void* lm_head, int32_t B,
+                                         int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                                         int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                                         int32_t* argmax_out, float* logits_out, hipStream_t stream) {
+  auto get_ws = [&](size_t need, ssd_status_t* err) -> void* {
+    if (need > SSD_NOALLOC_SCRATCH_BYTES) {
+      *err = SSD_ERR_WORKSPACE;
+      return nullptr;
+    }
+    return scratch_of_current_device(err);
+  };
+  return verify_impl(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
+                     B, W, D, Hq, Hkv, d, V, dtype, scale, attn_out, argmax_out, logits_out, get_ws,
+                     nullptr, nullptr, stream);
 }
 
 ssd_status_t ssd_blocktri_verify_sample(

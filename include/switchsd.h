@@ -59,7 +59,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 
 typedef enum {
   SSD_OK = 0,
@@ -202,6 +202,30 @@ ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v
                                  int32_t* argmax_out, float* logits_out, void* workspace,
                                  size_t workspace_bytes, hipEvent_t lm_begin, hipEvent_t lm_end,
                                  hipStream_t stream);
+
+/*
+ * ssd_blocktri_verify without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It computes exactly what ssd_blocktri_verify
+ * computes (same arguments and outputs; no timing events) and allocates nothing:
+ * its scratch is a device array of SSD_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends.  The current device must be the device of `stream` and of the buffers.
+ * Every call on a GPU shares that GPU's scratch, so calls that overlap on one GPU
+ * (on different streams, or from several threads) race; calls on one stream are
+ * ordered and safe.  Nothing in the scratch needs to be zero on entry.
+ * Errors: as ssd_blocktri_verify; WORKSPACE when ssd_verify_workspace_bytes(...)
+ *   of the call exceeds SSD_NOALLOC_SCRATCH_BYTES; HIP when the scratch's device
+ *   address cannot be obtained.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (64ull << 20)
+ssd_status_t ssd_blocktri_verify_noalloc(const void* q, const void* k_pre, const void* v_pre,
+                                         const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                         const void* v_cand, const int32_t* cand_len,
+                                         const uint8_t* copy_gate, const void* lm_head, int32_t B,
+                                         int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
+                                         int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
+                                         int32_t* argmax_out, float* logits_out, hipStream_t stream);
 
 /*
  * Longest accepted continuation at T = 0.  Paper §3.3: the longest validated
