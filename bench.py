@@ -1,15 +1,16 @@
 """Benchmark of one SwitchSD copy-speculation step on one MI355X.
 
 A step is the whole hot path over one batch, all on one HIP stream with no host
-synchronisation inside: probe_score -> kgram_retrieve -> blocktri_verify
-(block-triangular attention, LM head, argmax) -> accept_longest.  Inputs are
+synchronisation inside: probe_kgram_retrieve (the probe and the retrieval in one
+launch) -> blocktri_verify (block-triangular attention, LM head, argmax) ->
+accept_longest.  Inputs are
 synthetic (seeded) and resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
                     [--no-cpu-baseline] [--no-configs] [--config-steps K2]
 
-Protocol: W untimed steps; K steps between stage events (per-stage medians: probe,
-retrieval, attention, LM head, argmax reduce, accept; this phase also brings the
+Protocol: W untimed steps; K steps between stage events (per-stage medians: probe
+and retrieval, attention, LM head, argmax reduce, accept; this phase also brings the
 GPU clocks up); K steps each between two events, with a 512 MiB buffer rewritten
 before each step (outside its events) so that no input is served from the 256 MB
 last-level cache: value = B / the median of those steps, with p10 / p90; then K
@@ -236,13 +237,15 @@ def cpu_baseline(wl, budget_s, gpu_stage_ms=None):
            "cpu_model": model, "nproc": nproc, "blas_threads": int(threads),
            "stages": stages, "measured_s": round(t_probe + t_kg + t_att + t_lm + t_acc, 2)}
     if gpu_stage_ms:
-        pairs = {"probe": "probe", "kgram_retrieve": "kgram_retrieve", "attention": "attention",
-                 "lm_head_argmax": "lm_head", "accept": "accept"}
+        # the GPU runs the probe and the retrieval as one launch
+        pairs = {"probe_kgram_retrieve": (("probe", "kgram_retrieve"), "probe_kgram_retrieve"),
+                 "attention": (("attention",), "attention"),
+                 "lm_head_argmax": (("lm_head_argmax",), "lm_head"), "accept": (("accept",), "accept")}
         sp = {}
-        for k, g in pairs.items():
+        for k, (cpu, g) in pairs.items():
             gm = gpu_stage_ms.get(g)
             if gm and gm > 0:
-                sp[k] = round(stages[k]["s"] / (gm * 1e-3), 1)
+                sp[k] = round(sum(stages[c]["s"] for c in cpu) / (gm * 1e-3), 1)
         res["oracle_over_gpu"] = sp
     return res
 
@@ -599,7 +602,7 @@ def bench_forward(a):
 
 
 FLUSH_BYTES = 512 << 20      # written between timed steps: twice the 256 MB last-level cache
-STAGES = ("probe", "kgram_retrieve", "attention", "lm_head", "reduce", "accept")
+STAGES = ("probe_kgram_retrieve", "attention", "lm_head", "reduce", "accept")
 
 
 def attn_algorithmic(s, n, gate, cand_len):
@@ -684,8 +687,8 @@ class StepRunner:
 
     @staticmethod
     def events(n):
-        """n sets of stage events (e0 probe e1 kgram e2 attention [lm0 LM head lm1]
-        reduce e3 accept e4), each recorded once here so that torch creates them."""
+        """n sets of stage events (e0 probe+kgram e2 attention [e3 LM head e4] reduce
+        e5 accept e6; e1 unused), each recorded once here so that torch creates them."""
         import torch
         sets = []
         for _ in range(n):
@@ -700,9 +703,8 @@ class StepRunner:
         rec = (lambda k: ev[k].record(st)) if ev is not None else (lambda k: None)
         lm_ev = (ev[3], ev[4]) if ev is not None else None
         rec(0)
-        cdv.probe_score(self.h, self.w, s.tau, z_out=self.z, fire_out=self.fire, stream=st)
-        rec(1)
-        cdv.kgram_retrieve(self.ids, self.cu, s.kappa, s.W, s.D, self.fire, out=self.kout, stream=st)
+        cdv.probe_kgram_retrieve(self.h, self.w, s.tau, self.ids, self.cu, s.kappa, s.W, s.D,
+                                 z_out=self.z, fire_out=self.fire, out=self.kout, stream=st)
         rec(2)
         wl = self.wl
         if self.T > 0:
@@ -729,7 +731,7 @@ class StepRunner:
 def stage_times(ev):
     """Stage durations (ms) of one step from its events."""
     t = lambda a, b: ev[a].elapsed_time(ev[b])  # noqa: E731
-    return {"probe": t(0, 1), "kgram_retrieve": t(1, 2), "attention": t(2, 3), "lm_head": t(3, 4),
+    return {"probe_kgram_retrieve": t(0, 2), "attention": t(2, 3), "lm_head": t(3, 4),
             "reduce": t(4, 5), "accept": t(5, 6), "step": t(0, 6)}
 
 
@@ -741,7 +743,7 @@ def pct(x):
 
 def measure(runner, steps, warmup, flush):
     """warmup untimed steps, then three phases of `steps` steps each:
-    * stages: each step between its seven stage events (the per-stage medians; the
+    * stages: each step between its stage events (the per-stage medians; the
       event records themselves add about 18 us to a step, so this phase gives no
       step time; it also brings the GPU clocks up, which the first tens of
       milliseconds of load do not have);

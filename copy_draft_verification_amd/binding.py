@@ -25,6 +25,9 @@ _SIGS = {
                                        _c_p, _c_p]),
     "ssd_kgram_retrieve": (ctypes.c_int, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p,
                                           _c_p, _c_p, _c_p, _c_p]),
+    "ssd_probe_kgram_retrieve": (ctypes.c_int, [_c_p, ctypes.c_int, _c_p, _i32, ctypes.c_float, _c_p,
+                                                _c_p, _c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p,
+                                                _c_p, _c_p, _c_p, _c_p]),
     "ssd_pack_weight_bytes": (ctypes.c_size_t, [_i32, _i32]),
     "ssd_pack_weight": (ctypes.c_int, [_c_p, _i32, _i32, _c_p, ctypes.c_size_t, _c_p]),
     "ssd_pack_gate_up_bytes": (ctypes.c_size_t, [_i32, _i32]),
@@ -212,6 +215,45 @@ def kgram_retrieve(ids, cu_len, kappa, W, D, fire=None, out=None, stream=None):
                                      _torch_stream_handle(ts)),
            "kgram_retrieve")
     return out
+
+
+def probe_kgram_retrieve(h, w, tau, ids, cu_len, kappa, W, D, z_out=None, fire_out=None, out=None,
+                         stream=None):
+    """probe_score then kgram_retrieve gated by its decision, in one launch.  Returns
+    (z_out, fire_out, out) with out as from kgram_retrieve."""
+    _dev(h, "h", (torch.float32, torch.bfloat16))
+    _dev(w, "w", (torch.float32,))
+    _dev(ids, "ids", (torch.int32,))
+    _dev(cu_len, "cu_len", (torch.int32,))
+    if h.dim() != 2:
+        raise SwitchSDError("h must be [B, hid]")
+    B, hid = h.shape
+    if cu_len.numel() != B + 1:
+        raise SwitchSDError(f"cu_len has {cu_len.numel()} entries, expected B + 1 = {B + 1}")
+    _shape(w, "w", (hid,))
+    dev = h.device
+    _same_device(dev, (w, "w"), (ids, "ids"), (cu_len, "cu_len"))
+    ts = _torch_stream(stream, dev)
+    if z_out is None:
+        z_out = _alloc(ts, (B,), torch.float32, dev)
+    if fire_out is None:
+        fire_out = _alloc(ts, (B,), torch.uint8, dev)
+    _out(z_out, "z_out", torch.float32, (B,), dev)
+    _out(fire_out, "fire_out", torch.uint8, (B,), dev)
+    shapes = {"match_end": ((B, W), torch.int32), "n_match": ((B,), torch.int32),
+              "cand": ((B, W, D), torch.int32), "cand_len": ((B, W), torch.int32),
+              "copy_gate": ((B,), torch.uint8)}
+    if out is None:
+        out = {k: _alloc(ts, sh, dt, dev) for k, (sh, dt) in shapes.items()}
+    for k, (sh, dt) in shapes.items():
+        _out(out[k], f"out[{k!r}]", dt, sh, dev)
+    _check(load().ssd_probe_kgram_retrieve(_ptr(h), _dt(h), _ptr(w), hid, float(tau), _ptr(z_out),
+                                           _ptr(fire_out), _ptr(ids), _ptr(cu_len), B, kappa, W, D,
+                                           _ptr(out["match_end"]), _ptr(out["n_match"]),
+                                           _ptr(out["cand"]), _ptr(out["cand_len"]),
+                                           _ptr(out["copy_gate"]), _torch_stream_handle(ts)),
+           "probe_kgram_retrieve")
+    return z_out, fire_out, out
 
 
 class PackedWeight:

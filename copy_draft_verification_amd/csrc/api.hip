@@ -99,6 +99,31 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
                                     cand_len, copy_gate, stream));
 }
 
+ssd_status_t ssd_probe_kgram_retrieve(const void* h, ssd_dtype_t h_dtype, const float* w,
+                                      int32_t hidden, float tau, float* z_out, uint8_t* fire_out,
+                                      const int32_t* ids, const int32_t* cu_len, int32_t B,
+                                      int32_t kappa, int32_t W, int32_t D, int32_t* match_end,
+                                      int32_t* n_match, int32_t* cand, int32_t* cand_len,
+                                      uint8_t* copy_gate, hipStream_t stream) {
+  if (!h || !w || !fire_out || hidden < 1 || !valid_dtype(h_dtype)) return SSD_ERR_INVALID_ARG;
+  if (!(tau > 0.f && tau < 1.f)) return SSD_ERR_INVALID_ARG;
+  if (!ids || !cu_len || !match_end || !n_match || !cand || !cand_len || !copy_gate)
+    return SSD_ERR_INVALID_ARG;
+  if (B < 1 || kappa < 1 || kappa > SSD_MAX_KAPPA || W < 1 || W > SSD_MAX_W || D < 1 || D > SSD_MAX_D)
+    return SSD_ERR_INVALID_ARG;
+  const double t = static_cast<double>(tau);
+  ssd::KgProbe pr;
+  pr.h = h;
+  pr.bf16 = h_dtype == SSD_BF16;
+  pr.w = w;
+  pr.hidden = hidden;
+  pr.thr = static_cast<float>(std::log(t / (1.0 - t)));
+  pr.z_out = z_out;
+  pr.fire_out = fire_out;
+  return from_hip(ssd::launch_kgram(ids, cu_len, B, kappa, W, D, nullptr, match_end, n_match, cand,
+                                    cand_len, copy_gate, stream, &pr));
+}
+
 size_t ssd_pack_weight_bytes(int32_t rows, int32_t K) {
   if (rows < 1 || K < 1 || K % ssd::lm_k_align() != 0 || K > (1 << 20)) return 0;
   return ssd::packed_weight_bytes(rows, K, false);

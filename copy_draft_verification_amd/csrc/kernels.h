@@ -10,9 +10,21 @@ namespace ssd {
 hipError_t launch_probe(const void* h, bool bf16, const float* w, int B, int hidden, float thr,
                         float* z_out, uint8_t* fire_out, hipStream_t s);
 
+// The probe computed inside the retrieval launch (ssd_probe_kgram_retrieve): h [B][hidden]
+// (bf16 or fp32), w [hidden], thr = logit(tau); z_out may be null.
+struct KgProbe {
+  const void* h = nullptr;
+  bool bf16 = false;
+  const float* w = nullptr;
+  int hidden = 0;
+  float thr = 0.f;
+  float* z_out = nullptr;
+  uint8_t* fire_out = nullptr;
+};
 hipError_t launch_kgram(const int32_t* ids, const int32_t* cu_len, int B, int kappa, int W, int D,
                         const uint8_t* fire, int32_t* match_end, int32_t* n_match, int32_t* cand,
-                        int32_t* cand_len, uint8_t* copy_gate, hipStream_t s);
+                        int32_t* cand_len, uint8_t* copy_gate, hipStream_t s,
+                        const KgProbe* probe = nullptr);
 
 hipError_t launch_accept(const int32_t* cand, const int32_t* cand_len, const uint8_t* copy_gate,
                          const int32_t* argmax, int B, int W, int D, int32_t* accept_len,

@@ -58,22 +58,79 @@ __device__ __forceinline__ void lds_ld8(const int* p, i32x4& a, i32x4& b) {
                : "=&v"(a), "=&v"(b) : "v"(lds_addr(p)) : "memory");
 }
 
+// The probe of sequence b, computed by the whole workgroup (paper §3.2 "Layer and
+// Threshold Selection", write-up §2.3): z = w . h_b in fp32 (each thread sums
+// eight consecutive k per chunk, then a wave sum and a sum over the waves in wave
+// order), fire = z >= thr.  Thread 0 writes z_out[b] (if given) and fire_out[b].
+// Returns fire to every thread.
+__device__ __forceinline__ bool probe_in_block(const KgProbe& pr, int b, float* s_part, int* s_fire) {
+  const int t = threadIdx.x;
+  float acc = 0.f;
+  if ((pr.hidden & 7) == 0) {
+    const int nch = pr.hidden >> 3;
+    for (int c = t; c < nch; c += kKgThreads) {
+      float hv[8];
+      if (pr.bf16) {
+        Chunk8<uint16_t> x;
+        x.load(static_cast<const uint16_t*>(pr.h) + static_cast<size_t>(b) * pr.hidden + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = x.at(e);
+      } else {
+        Chunk8<float> x;
+        x.load(static_cast<const float*>(pr.h) + static_cast<size_t>(b) * pr.hidden + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = x.at(e);
+      }
+      Chunk8<float> wv;
+      wv.load(pr.w + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += wv.at(e) * hv[e];
+    }
+  } else {
+    for (int k = t; k < pr.hidden; k += kKgThreads) {
+      const float hk = pr.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(pr.h)[static_cast<size_t>(b) * pr.hidden + k])
+                               : static_cast<const float*>(pr.h)[static_cast<size_t>(b) * pr.hidden + k];
+      acc += pr.w[k] * hk;
+    }
+  }
+  acc = wave_sum(acc);
+  if ((t & (kWave - 1)) == 0) s_part[t / kWave] = acc;
+  __syncthreads();
+  if (t == 0) {
+    float z = 0.f;
+    for (int i = 0; i < kKgThreads / kWave; ++i) z += s_part[i];
+    const bool f = z >= pr.thr;
+    if (pr.z_out) pr.z_out[b] = z;
+    pr.fire_out[b] = f ? 1 : 0;
+    *s_fire = f ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_fire != 0;
+}
+
 // Two workgroups per CU (8 waves per SIMD, 2 x 72 KB of LDS): while one
-// compares, the other's loads are in flight.
+// compares, the other's loads are in flight.  With pr.h set, the workgroup first
+// computes its sequence's probe (probe_in_block) while its first chunk copies are
+// in flight, and scans only if the probe fired; `fire` is then not read.
 __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_len, int kappa, int W, int D,
     const uint8_t* __restrict__ fire, int32_t* __restrict__ match_end, int32_t* __restrict__ n_match,
-    int32_t* __restrict__ cand, int32_t* __restrict__ cand_len, uint8_t* __restrict__ copy_gate) {
+    int32_t* __restrict__ cand, int32_t* __restrict__ cand_len, uint8_t* __restrict__ copy_gate,
+    KgProbe pr) {
   // the two stages, read through the asm helpers above
   __shared__ int s_suffix[SSD_MAX_KAPPA];
   __shared__ int s_list[SSD_MAX_W];
   __shared__ int s_wave[kKgThreads / kWave];
+  __shared__ float s_part[kKgThreads / kWave];
+  __shared__ int s_fire;
   __shared__ __attribute__((aligned(16))) int st0[kKgSlots];
   __shared__ __attribute__((aligned(16))) int st1[kKgSlots];
   const int b = blockIdx.x, t = threadIdx.x;
   const int base = cu_len[b];
   const int n = cu_len[b + 1] - base;
-  const bool active = (fire == nullptr || fire[b] != 0) && n >= kappa + 1;
+  const bool fused = pr.h != nullptr;
+  const bool active = (fused || fire == nullptr || fire[b] != 0) && n >= kappa + 1;
+  if (fused && !active) probe_in_block(pr, b, s_part, &s_fire);
   int found = 0;
   if (active) {
     const int lo = kappa - 1;
@@ -163,7 +220,10 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     int top = n - 2;
     issue(st0, top);
     issue(st1, top - kKgChunk);
-    for (;;) {
+    // fused probe: computed while the first copies are in flight; a closed probe
+    // retrieves nothing
+    const bool fired = !fused || probe_in_block(pr, b, s_part, &s_fire);
+    for (; fired;) {
       if (!chunk(st0, top)) break;
       top -= kKgChunk;
       if (!chunk(st1, top)) break;
@@ -197,9 +257,10 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
 
 hipError_t launch_kgram(const int32_t* ids, const int32_t* cu_len, int B, int kappa, int W, int D,
                         const uint8_t* fire, int32_t* match_end, int32_t* n_match, int32_t* cand,
-                        int32_t* cand_len, uint8_t* copy_gate, hipStream_t s) {
+                        int32_t* cand_len, uint8_t* copy_gate, hipStream_t s, const KgProbe* probe) {
+  const KgProbe pr = probe != nullptr ? *probe : KgProbe{};
   hipLaunchKernelGGL(kgram_kernel, dim3(B), dim3(kKgThreads), 0, s, ids, cu_len, kappa, W, D, fire,
-                     match_end, n_match, cand, cand_len, copy_gate);
+                     match_end, n_match, cand, cand_len, copy_gate, pr);
   return hipGetLastError();
 }
 

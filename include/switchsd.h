@@ -7,6 +7,7 @@
  *
  *   ssd_probe_score     copy-intent probe on the layer-l hidden state
  *   ssd_kgram_retrieve  kappa-gram evidence + up to W recency-ordered candidates
+ *                       (ssd_probe_kgram_retrieve: both in one launch)
  *   ssd_blocktri_verify one verification pass: block-triangular attention, then
  *                       LM-head projection and greedy (T = 0) argmax per row
  *   ssd_accept_longest  longest accepted continuation and the token after it
@@ -59,7 +60,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 8
+#define SSD_ABI_VERSION 9
 
 typedef enum {
   SSD_OK = 0,
@@ -126,6 +127,26 @@ ssd_status_t ssd_kgram_retrieve(const int32_t* ids, const int32_t* cu_len, int32
                                 int32_t kappa, int32_t W, int32_t D, const uint8_t* fire,
                                 int32_t* match_end, int32_t* n_match, int32_t* cand,
                                 int32_t* cand_len, uint8_t* copy_gate, hipStream_t stream);
+
+/*
+ * The probe and the retrieval in one launch: exactly ssd_probe_score followed by
+ * ssd_kgram_retrieve with fire = fire_out (paper §3.2 "Layer and Threshold
+ * Selection" and §3.3; write-up §2.3 and §2.5, the dual gate), for callers that
+ * want one launch per step less.  Sequence b's workgroup starts the copies of its
+ * first context chunks, computes z_b = w . h_b while they are in flight, and
+ * scans only if the probe fired.  Arguments, layouts and outputs are those of the
+ * two calls (h [B][hidden] of dtype h_dtype, w [hidden] float, z_out [B] float or
+ * NULL, fire_out [B] uint8; ids, cu_len, match_end, n_match, cand, cand_len,
+ * copy_gate as in ssd_kgram_retrieve).  z_b may differ from ssd_probe_score's in
+ * the last bits (another summation order); fire_b is then decided on this z_b.
+ * Errors: the union of the two calls' (INVALID_ARG).
+ */
+ssd_status_t ssd_probe_kgram_retrieve(const void* h, ssd_dtype_t h_dtype, const float* w,
+                                      int32_t hidden, float tau, float* z_out, uint8_t* fire_out,
+                                      const int32_t* ids, const int32_t* cu_len, int32_t B,
+                                      int32_t kappa, int32_t W, int32_t D, int32_t* match_end,
+                                      int32_t* n_match, int32_t* cand, int32_t* cand_len,
+                                      uint8_t* copy_gate, hipStream_t stream);
 
 /*
  * Packed bf16 weights.  The projection of the verification pass (paper §3.3: all

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_blocktri_verify_sample", "ssd_accept_sample",
                           "ssd_verify_forward", "ssd_verify_forward_workspace_bytes",
                           "ssd_pack_weight", "ssd_pack_weight_bytes", "ssd_pack_gate_up",
-                          "ssd_pack_gate_up_bytes"}
+                          "ssd_pack_gate_up_bytes", "ssd_probe_kgram_retrieve",
+                          "ssd_blocktri_verify_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -122,6 +123,18 @@ def test_kgram_validation(lib):
     f = lib.ssd_kgram_retrieve
     args = [FAKE, FAKE, 1, 5, 10, 20, None, FAKE, FAKE, FAKE, FAKE, FAKE, None]
     for i, bad in ((2, 0), (3, 0), (3, 65), (4, 0), (4, 65), (5, 0), (5, 65), (0, None), (7, None)):
+        a = list(args)
+        a[i] = bad
+        assert f(*a) == 1, (i, bad)
+
+
+def test_probe_kgram_validation(lib):
+    f = lib.ssd_probe_kgram_retrieve
+    args = [FAKE, 1, FAKE, 4096, 0.4, None, FAKE, FAKE, FAKE, 1, 5, 10, 20, FAKE, FAKE, FAKE, FAKE,
+            FAKE, None]
+    for i, bad in ((0, None), (2, None), (6, None), (7, None), (8, None), (13, None), (17, None),
+                   (1, 7), (3, 0), (4, 0.0), (4, 1.0), (4, float("nan")), (9, 0), (10, 0),
+                   (10, 65), (11, 0), (11, 65), (12, 0), (12, 65)):
         a = list(args)
         a[i] = bad
         assert f(*a) == 1, (i, bad)
