@@ -2,16 +2,17 @@
 
 A step is the whole hot path over one batch, all on one HIP stream with no host
 synchronisation inside: probe_kgram_retrieve (the probe and the retrieval in one
-launch) -> blocktri_verify (block-triangular attention, LM head, argmax) ->
-accept_longest.  Inputs are
-synthetic (seeded) and resident in HBM before timing starts.
+launch) -> blocktri_verify_accept (block-triangular attention, then the LM head
+with the argmax and the accept in its launch).  At T > 0 the verification and
+accept are blocktri_verify_sample -> accept_sample.  Inputs are synthetic (seeded)
+and resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
                     [--no-cpu-baseline] [--no-configs] [--config-steps K2]
 
 Protocol: W untimed steps; K steps between stage events (per-stage medians: probe
-and retrieval, attention, LM head, argmax reduce, accept; this phase also brings the
-GPU clocks up); K steps each between two events, with a 512 MiB buffer rewritten
+and retrieval, attention, LM head, what follows the LM head; this phase also brings
+the GPU clocks up); K steps each between two events, with a 512 MiB buffer rewritten
 before each step (outside its events) so that no input is served from the 256 MB
 last-level cache: value = B / the median of those steps, with p10 / p90; then K
 steps back to back between two events (ms_per_step_back_to_back, warm caches).
@@ -237,14 +238,15 @@ def cpu_baseline(wl, budget_s, gpu_stage_ms=None):
            "cpu_model": model, "nproc": nproc, "blas_threads": int(threads),
            "stages": stages, "measured_s": round(t_probe + t_kg + t_att + t_lm + t_acc, 2)}
     if gpu_stage_ms:
-        # the GPU runs the probe and the retrieval as one launch
-        pairs = {"probe_kgram_retrieve": (("probe", "kgram_retrieve"), "probe_kgram_retrieve"),
-                 "attention": (("attention",), "attention"),
-                 "lm_head_argmax": (("lm_head_argmax",), "lm_head"), "accept": (("accept",), "accept")}
+        # the GPU runs the probe and the retrieval as one launch, and the argmax and
+        # the accept inside the LM-head launch
+        pairs = {"probe_kgram_retrieve": (("probe", "kgram_retrieve"), ("probe_kgram_retrieve",)),
+                 "attention": (("attention",), ("attention",)),
+                 "lm_head_argmax_accept": (("lm_head_argmax", "accept"), ("lm_head", "after_lm_head"))}
         sp = {}
         for k, (cpu, g) in pairs.items():
-            gm = gpu_stage_ms.get(g)
-            if gm and gm > 0:
+            gm = sum(gpu_stage_ms.get(x) or 0.0 for x in g)
+            if gm > 0:
                 sp[k] = round(sum(stages[c]["s"] for c in cpu) / (gm * 1e-3), 1)
         res["oracle_over_gpu"] = sp
     return res
@@ -602,7 +604,9 @@ def bench_forward(a):
 
 
 FLUSH_BYTES = 512 << 20      # written between timed steps: twice the 256 MB last-level cache
-STAGES = ("probe_kgram_retrieve", "attention", "lm_head", "reduce", "accept")
+# after_lm_head: from the end of the LM-head launch to the end of the step (T = 0
+# with bf16: nothing, the argmax and the accept run inside the LM-head launch)
+STAGES = ("probe_kgram_retrieve", "attention", "lm_head", "after_lm_head")
 
 
 def attn_algorithmic(s, n, gate, cand_len):
@@ -687,8 +691,8 @@ class StepRunner:
 
     @staticmethod
     def events(n):
-        """n sets of stage events (e0 probe+kgram e2 attention [e3 LM head e4] reduce
-        e5 accept e6; e1 unused), each recorded once here so that torch creates them."""
+        """n sets of stage events (e0 probe+kgram e2 attention [e3 LM head e4] ... e6;
+        e1 and e5 unused), each recorded once here so that torch creates them."""
         import torch
         sets = []
         for _ in range(n):
@@ -718,13 +722,11 @@ class StepRunner:
                               out={k: self.aout[k] for k in ("best_w", "best_len", "next_token")},
                               stream=st)
         else:
-            cdv.blocktri_verify(self.q, self.kp, self.vp, self.cu, wl.max_n, self.kc, self.vc,
-                                self.kout["cand_len"], self.kout["copy_gate"], self.lm, s.W, s.D,
-                                wl.scale, attn_out=self.attn, argmax_out=self.am, workspace=self.ws,
-                                events=lm_ev, stream=st)
-            rec(5)
-            cdv.accept_longest(self.kout["cand"], self.kout["cand_len"], self.kout["copy_gate"], self.am,
-                               s.W, s.D, out=self.aout, stream=st)
+            cdv.blocktri_verify_accept(self.q, self.kp, self.vp, self.cu, wl.max_n, self.kc, self.vc,
+                                       self.kout["cand"], self.kout["cand_len"], self.kout["copy_gate"],
+                                       self.lm, s.W, s.D, wl.scale, attn_out=self.attn,
+                                       argmax_out=self.am, out=self.aout, workspace=self.ws,
+                                       events=lm_ev, stream=st)
         rec(6)
 
 
@@ -732,7 +734,7 @@ def stage_times(ev):
     """Stage durations (ms) of one step from its events."""
     t = lambda a, b: ev[a].elapsed_time(ev[b])  # noqa: E731
     return {"probe_kgram_retrieve": t(0, 2), "attention": t(2, 3), "lm_head": t(3, 4),
-            "reduce": t(4, 5), "accept": t(5, 6), "step": t(0, 6)}
+            "after_lm_head": t(4, 6), "step": t(0, 6)}
 
 
 def pct(x):

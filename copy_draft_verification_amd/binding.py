@@ -38,6 +38,11 @@ _SIGS = {
                                            _c_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.c_int, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
                                            ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "ssd_blocktri_verify_accept": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p,
+                                                  _c_p, _c_p, _c_p, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, ctypes.c_int, ctypes.c_float, _c_p,
+                                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                  ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ssd_blocktri_verify_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _c_p,
                                                    _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _i32,
                                                    _i32, ctypes.c_int, ctypes.c_float, _c_p, _c_p,
@@ -424,6 +429,45 @@ def blocktri_verify_noalloc(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand
         _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _torch_stream_handle(ts)),
         "blocktri_verify_noalloc")
     return attn_out, argmax_out
+
+
+def blocktri_verify_accept(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand, cand_len, copy_gate,
+                           lm_head, W, D, scale, attn_out=None, argmax_out=None, out=None,
+                           workspace=None, events=None, stream=None):
+    """blocktri_verify then accept_longest on its argmax, in the verification's
+    launches (bf16: the accept runs in the LM-head launch).  cand [B, W, D] int32;
+    other arguments as blocktri_verify; out as accept_longest's.  Returns
+    (attn_out, argmax_out, out)."""
+    B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
+                                      copy_gate, W, D, (torch.float32, torch.bfloat16))
+    _dev(cand, "cand", (torch.int32,))
+    _shape(cand, "cand", (B, W, D))
+    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    dev = q.device
+    _same_device(dev, (cand, "cand"))
+    ts = _torch_stream(stream, dev)
+    if attn_out is None:
+        attn_out = _alloc(ts, (B, R, Hq * d), q.dtype, dev)
+    _out(attn_out, "attn_out", q.dtype, (B, R, Hq * d), dev)
+    if argmax_out is None:
+        argmax_out = _alloc(ts, (B, R), torch.int32, dev)
+    _out(argmax_out, "argmax_out", torch.int32, (B, R), dev)
+    shapes = {"accept_len": (B, W), "best_w": (B,), "best_len": (B,), "next_token": (B,)}
+    if out is None:
+        out = {k: _alloc(ts, sh, torch.int32, dev) for k, sh in shapes.items()}
+    for k, sh in shapes.items():
+        _out(out[k], f"out[{k!r}]", torch.int32, sh, dev)
+    need = verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, q.dtype)
+    workspace = _workspace(workspace, need, ts, dev)
+    ev0, ev1 = _events(events)
+    _check(load().ssd_blocktri_verify_accept(
+        _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
+        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q),
+        float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(out["accept_len"]), _ptr(out["best_w"]),
+        _ptr(out["best_len"]), _ptr(out["next_token"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
+        "blocktri_verify_accept")
+    return attn_out, argmax_out, out
 
 
 def _events(events):

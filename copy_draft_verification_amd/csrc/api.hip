@@ -178,7 +178,7 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
                          int32_t B, int32_t W, int32_t D, int32_t Hq, int32_t Hkv, int32_t d,
                          int32_t V, ssd_dtype_t dtype, float scale, void* attn_out,
                          int32_t* argmax_out, float* logits_out, GetWs get_ws, hipEvent_t lm_begin,
-                         hipEvent_t lm_end, hipStream_t stream) {
+                         hipEvent_t lm_end, hipStream_t stream, const ssd::AcceptArgs* acc = nullptr) {
   if (!q || !k_pre || !v_pre || !cu_len || !k_cand || !v_cand || !cand_len || !copy_gate ||
       !lm_head || !attn_out || !argmax_out)
     return SSD_ERR_INVALID_ARG;
@@ -206,7 +206,13 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
   e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
                          lm_begin, lm_end, stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
-  return from_hip(ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream));
+  // bf16: one launch turns the LM head's per-row keys into argmax_out and accepts
+  if (bf16) return from_hip(ssd::launch_argmax_finish(ws_lm, B, R, argmax_out, acc, stream));
+  e = ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream);
+  if (e != hipSuccess || acc == nullptr) return from_hip(e);
+  return from_hip(ssd::launch_accept(acc->cand, acc->cand_len, acc->copy_gate, argmax_out, B, W, D,
+                                     acc->accept_len, acc->best_w, acc->best_len, acc->next_token,
+                                     stream));
 }
 
 // The no-allocation variant's scratch: one array per GPU (each device that loads
@@ -283,6 +289,40 @@ ssd_status_t ssd_blocktri_verify_noalloc(const void* q, const void* k_pre, const
   return verify_impl(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
                      B, W, D, Hq, Hkv, d, V, dtype, scale, attn_out, argmax_out, logits_out, get_ws,
                      nullptr, nullptr, stream);
+}
+
+ssd_status_t ssd_blocktri_verify_accept(const void* q, const void* k_pre, const void* v_pre,
+                                        const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                        const void* v_cand, const int32_t* cand,
+                                        const int32_t* cand_len, const uint8_t* copy_gate,
+                                        const void* lm_head, int32_t B, int32_t W, int32_t D,
+                                        int32_t Hq, int32_t Hkv, int32_t d, int32_t V,
+                                        ssd_dtype_t dtype, float scale, void* attn_out,
+                                        int32_t* argmax_out, int32_t* accept_len, int32_t* best_w,
+                                        int32_t* best_len, int32_t* next_token, void* workspace,
+                                        size_t workspace_bytes, hipEvent_t lm_begin,
+                                        hipEvent_t lm_end, hipStream_t stream) {
+  if (!cand || !accept_len || !best_w || !best_len || !next_token) return SSD_ERR_INVALID_ARG;
+  auto get_ws = [&](size_t need, ssd_status_t* err) -> void* {
+    if (!workspace || workspace_bytes < need) {
+      *err = SSD_ERR_WORKSPACE;
+      return nullptr;
+    }
+    return workspace;
+  };
+  ssd::AcceptArgs acc;
+  acc.cand = cand;
+  acc.cand_len = cand_len;
+  acc.copy_gate = copy_gate;
+  acc.W = W;
+  acc.D = D;
+  acc.accept_len = accept_len;
+  acc.best_w = best_w;
+  acc.best_len = best_len;
+  acc.next_token = next_token;
+  return verify_impl(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, copy_gate, lm_head,
+                     B, W, D, Hq, Hkv, d, V, dtype, scale, attn_out, argmax_out, nullptr, get_ws,
+                     lm_begin, lm_end, stream, &acc);
 }
 
 ssd_status_t ssd_blocktri_verify_sample(

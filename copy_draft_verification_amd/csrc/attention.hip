@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
   if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
     __shared__ int s_cwave[kAttThreads / kWave];
     compact_rows_body<kAttThreads>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
-                                   compact.n_rows, s_cwave);
+                                   compact.n_rows, s_cwave, compact.keys);
     return;
   }
 
@@ -758,7 +758,7 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   if (bf16) {
     const int per_xcd = (B * Hkv + kXcds - 1) / kXcds * plan.nslots;
     const int items_x = per_xcd * plan.qtiles;
-    const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr};
+    const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr, nullptr};
     int* work = nullptr;
     int grid = kXcds * items_x;
     if (plan.persist) {

@@ -211,10 +211,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int& total) {
 // order: row_list[k] = k-th real row, inv[row] = its position or -1, *n_rows = the
 // count.  Run by every thread of one workgroup of NT threads; s_wave holds NT / 64
 // ints of LDS.
+// It also zeroes the greedy LM head's per-row argmax keys (keys; may be null).
 template <int NT>
 __device__ void compact_rows_body(int rows, int R, int W, int D, const int32_t* __restrict__ cand_len,
                                   const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
-                                  int32_t* __restrict__ inv, int32_t* __restrict__ n_rows, int* s_wave) {
+                                  int32_t* __restrict__ inv, int32_t* __restrict__ n_rows, int* s_wave,
+                                  unsigned long long* __restrict__ keys) {
+  if (keys != nullptr)
+    for (int i = static_cast<int>(threadIdx.x); i < rows; i += NT) keys[i] = 0ull;
   int base = 0;
   for (int r0 = 0; r0 < rows; r0 += NT) {
     const int row = r0 + static_cast<int>(threadIdx.x);

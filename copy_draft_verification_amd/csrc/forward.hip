@@ -356,7 +356,7 @@ hipError_t launch_forward(const int32_t* ids, const int32_t* cu_len, const int32
   }
   e = launch_lmhead(hb, lm_head, rows, hid, V, true, L.lm, nullptr, lmws, nullptr, nullptr, s);
   if (e != hipSuccess) return e;
-  e = launch_argmax_reduce(lmws, L.lm, rows, argmax_out, s);
+  e = launch_argmax_finish(lmws, B, R, argmax_out, nullptr, s);
   if (e == hipSuccess && ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   return e;
 }

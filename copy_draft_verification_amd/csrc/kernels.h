@@ -47,6 +47,7 @@ struct LmWsView {
   int32_t* n_rows;
   int32_t* row_list;
   int32_t* inv;
+  unsigned long long* keys;  // [rows] greedy argmax keys, zeroed with the compaction
 };
 
 // With `compact` (bf16 only), one more workgroup of the prefix launch writes the
@@ -104,11 +105,30 @@ struct GemmArgs {
   const int32_t* row_list;    // compact row -> global row
 };
 
-// sample == nullptr: greedy partials (value, index); otherwise sampling partials.
+// Accept at T = 0 after the greedy argmax (launch_argmax_finish); cand == null: no
+// accept.  The arrays of launch_accept.
+struct AcceptArgs {
+  const int32_t* cand = nullptr;
+  const int32_t* cand_len = nullptr;
+  const uint8_t* copy_gate = nullptr;
+  int W = 0, D = 0;
+  int32_t* accept_len = nullptr;
+  int32_t* best_w = nullptr;
+  int32_t* best_len = nullptr;
+  int32_t* next_token = nullptr;
+};
+
+// sample != nullptr: sampling partials.  Otherwise greedy: the fp32 path writes
+// (value, index) partials for launch_argmax_reduce; the bf16 path folds each row's
+// best (value, lowest index) into a 64-bit key per row (launch_argmax_finish).
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
                          const SampleArgs* sample = nullptr);
+// bf16 greedy: argmax_out [B][R] from the keys of launch_lmhead (-1 for rows that are
+// not real), then, with `accept`, the accept of every sequence; one launch.
+hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, const AcceptArgs* accept,
+                                hipStream_t s);
 
 // Lists the real rows (open gate; row 0 or candidate token j < L_w) in the LM-head
 // workspace; the LM head then contracts only those rows.

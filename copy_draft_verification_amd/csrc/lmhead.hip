@@ -10,8 +10,9 @@
 // dimension (A operand, loaded straight from HBM into registers, three k-steps
 // ahead, from the packed layout in which each wave's fragments of a k-step are
 // one contiguous 8 KB run).  The epilogue reduces each row over the tile to a
-// (max, lowest index) pair without writing logits; a second tiny kernel reduces
-// the tiles.  The same main loop, with other epilogues, serves the sampling
+// (max, lowest index) pair without writing logits and folds it into the row's
+// 64-bit key by an atomic max; a one-wave-per-sequence launch turns the keys into
+// argmax indices (and may run the accept).  The same main loop, with other epilogues, serves the sampling
 // verification and the projections of the forward.  An fp32 variant on the
 // vector ALU serves fp32 inputs (plain [V][hid] weights).
 #include <limits.h>
@@ -19,6 +20,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "accept_seq.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -277,13 +279,26 @@ __device__ __forceinline__ void sample_epilogue(
   }
 }
 
+// 64-bit argmax key of a (value, index) pair: the value's bits made
+// order-preserving in the high half (-0 taken as +0, so that equal values tie), the
+// complemented index in the low half.  The unsigned maximum of keys is then the
+// largest value with the lowest index, the order of `better`.  0 stands for no
+// value (every value NaN or past V); no real pair maps to it, since its high half
+// would be a NaN's.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  if (i == INT_MAX) return 0ull;
+  uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+}
+
 // Greedy epilogue: per row (this lane's column l32 of each row tile), the best
-// (value, lowest index) over this workgroup's tile, combined over the four waves.
+// (value, lowest index) over this workgroup's tile, combined over the four waves,
+// then folded into the row's key by a device-wide 64-bit atomic max.
 __device__ __forceinline__ void argmax_epilogue(
-    const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows, int vbase, int V, int vt, int vtiles,
-    int wave, int tid, int l32, int h, const int32_t* __restrict__ row_list,
-    float* __restrict__ logits_out, float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC],
-    int2* __restrict__ part) {
+    const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows, int vbase, int V, int wave, int tid,
+    int l32, int h, const int32_t* __restrict__ row_list, float* __restrict__ logits_out,
+    float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC], unsigned long long* __restrict__ keys) {
 #pragma unroll
   for (int t = 0; t < kLmNT; ++t) {
     const int row = row0 + t * 32 + l32;
@@ -315,7 +330,7 @@ __device__ __forceinline__ void argmax_epilogue(
 #pragma unroll
     for (int w = 1; w < kLmWaves; ++w)
       if (better(red_v[w][i], red_i[w][i], bv, bi)) { bv = red_v[w][i]; bi = red_i[w][i]; }
-    part[static_cast<size_t>(row) * vtiles + vt] = make_int2(__float_as_int(bv), bi);
+    __hip_atomic_fetch_max(keys + row, argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -353,14 +368,13 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   const int n_sm = (mchunks + sm - 1) / sm;
   const int vt = (super / n_sm) * sv + (li % per) / sm;
   const int mc = (super % n_sm) * sm + (li % per) % sm;
-  if (vt >= vtiles || mc >= mchunks) return;
-  // rows of this chunk are compact indices row0.. into the list of real rows
-  const int rows = *n_rows;
-  if (mc * kLmMC >= rows) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   // wave index in a scalar register: the LDS destination of a buffer-to-LDS load
   // (M0) must be wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  // rows of this chunk are compact indices row0.. into the list of real rows
+  const int rows = *n_rows;
+  if (vt >= vtiles || mc >= mchunks || mc * kLmMC >= rows) return;
   const int h = lane >> 5, l32 = lane & 31;
   const int row0 = mc * kLmMC;
   // the gate / up GEMM takes its two A tiles from two matrices (the same 32
@@ -548,8 +562,8 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
                     red_v, red_i, reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_m),
                     reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_s), static_cast<float4*>(part_out));
   } else {
-    argmax_epilogue(acc, row0, rows, vbase, V, vt, vtiles, wave, tid, l32, h, row_list, logits_out,
-                    red_v, red_i, static_cast<int2*>(part_out));
+    argmax_epilogue(acc, row0, rows, vbase, V, wave, tid, l32, h, row_list, logits_out, red_v, red_i,
+                    static_cast<unsigned long long*>(part_out));
   }
 }
 
@@ -658,9 +672,10 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
 __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(
     int rows, int R, int W, int D, const int32_t* __restrict__ cand_len,
     const uint8_t* __restrict__ copy_gate, int32_t* __restrict__ row_list,
-    int32_t* __restrict__ inv, int32_t* __restrict__ n_rows) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ n_rows, unsigned long long* __restrict__ keys) {
   __shared__ int s_wave[kCompactThreads / kWave];
-  compact_rows_body<kCompactThreads>(rows, R, W, D, cand_len, copy_gate, row_list, inv, n_rows, s_wave);
+  compact_rows_body<kCompactThreads>(rows, R, W, D, cand_len, copy_gate, row_list, inv, n_rows, s_wave,
+                                     keys);
 }
 
 // One wave per row: the row's tile partials are contiguous ([row][vtile]), each
@@ -699,7 +714,33 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(
     const int oi = __shfl_xor(bi, o, kWave);
     if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
-  if (lane == 0) argmax_out[row] = bi;
+  // no value (every logit NaN): -1, as the bf16 path reports it
+  if (lane == 0) argmax_out[row] = bi == INT_MAX ? -1 : bi;
+}
+
+// One wave per sequence: the argmax of each of its R rows from the row's key (the
+// low half of a nonzero key is the complemented index; 0 = no value), -1 for rows
+// that are not real; then, when asked, the sequence's accept on those rows.
+__global__ __launch_bounds__(kWave) void argmax_finish_kernel(
+    const unsigned long long* __restrict__ keys, const int32_t* __restrict__ inv, int R,
+    int32_t* __restrict__ argmax_out, AcceptArgs acc) {
+  __shared__ int s_pred[SSD_MAX_W][kWave];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  for (int r = lane; r < R; r += kWave) {
+    const size_t row = static_cast<size_t>(b) * R + r;
+    const int ci = inv[row];
+    int out = -1;
+    if (ci >= 0) {
+      const unsigned long long k = keys[ci];
+      out = k == 0ull ? -1 : static_cast<int>(~static_cast<uint32_t>(k));
+    }
+    argmax_out[row] = out;
+  }
+  if (acc.cand == nullptr) return;
+  // the accept reads this wave's argmax stores back
+  __syncthreads();
+  accept_seq(b, lane, acc.cand, acc.cand_len, acc.copy_gate, argmax_out, acc.W, acc.D, acc.accept_len,
+             acc.best_w, acc.best_len, acc.next_token, s_pred);
 }
 
 // One wave per row: merges the row's per-tile (max, sum-exp, best score, best
@@ -792,6 +833,7 @@ struct LmWs {
   int32_t* row_list;
   int32_t* inv;
   int2* part;
+  unsigned long long* keys;  // greedy bf16: the start of the partials region
 };
 LmWs lm_ws(void* ws, int rows) {
   char* p = static_cast<char*>(ws);
@@ -803,6 +845,7 @@ LmWs lm_ws(void* ws, int rows) {
   w.inv = reinterpret_cast<int32_t*>(p);
   p += al256(sizeof(int32_t) * rows);
   w.part = reinterpret_cast<int2*>(p);
+  w.keys = reinterpret_cast<unsigned long long*>(p);
   return w;
 }
 }  // namespace
@@ -811,7 +854,7 @@ LmWs lm_ws(void* ws, int rows) {
 // (max, sum-exp, best score, best token) when sampling.
 LmWsView lm_ws_view(void* ws, int rows) {
   const LmWs w = lm_ws(ws, rows);
-  return LmWsView{w.n_rows, w.row_list, w.inv};
+  return LmWsView{w.n_rows, w.row_list, w.inv, w.keys};
 }
 
 size_t lm_workspace_bytes(const LmPlan& p, int rows) {
@@ -832,7 +875,7 @@ hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const in
                                const uint8_t* copy_gate, hipStream_t s) {
   const LmWs w = lm_ws(ws, rows);
   hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, s, rows, R, W, D,
-                     cand_len, copy_gate, w.row_list, w.inv, w.n_rows);
+                     cand_len, copy_gate, w.row_list, w.inv, w.n_rows, w.keys);
   return hipGetLastError();
 }
 
@@ -850,7 +893,7 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   else if (bf16)
     launch_bf16<kEpiArgmax>(plan, dim3(plan.blocks), s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
-                       rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),
+                       rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.keys),
                        plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{}, GemmArgs{});
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
@@ -884,6 +927,14 @@ hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t*
   const LmWs w = lm_ws(ws, rows);
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, w.part,
                      plan.vtiles, rows, w.inv, argmax_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, const AcceptArgs* accept,
+                                hipStream_t s) {
+  const LmWs w = lm_ws(ws, B * R);
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(B), dim3(kWave), 0, s, w.keys, w.inv, R, argmax_out,
+                     accept != nullptr ? *accept : AcceptArgs{});
   return hipGetLastError();
 }
 

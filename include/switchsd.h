@@ -11,6 +11,8 @@
  *   ssd_blocktri_verify one verification pass: block-triangular attention, then
  *                       LM-head projection and greedy (T = 0) argmax per row
  *   ssd_accept_longest  longest accepted continuation and the token after it
+ *                       (ssd_blocktri_verify_accept: verification and accept in
+ *                       the verification's launches)
  *
  * and, after accept, ssd_commit_accepted copies the accepted tokens' keys and
  * values into the caller's KV cache and lists the tokens that extend the context.
@@ -60,7 +62,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 9
+#define SSD_ABI_VERSION 10
 
 typedef enum {
   SSD_OK = 0,
@@ -199,8 +201,9 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  * LM head + argmax:
  *   lm_head  fp32: [V][Hq*d]        transposed projection (row v = weights of token v)
  *            bf16: that matrix as written by ssd_pack_weight
- *   argmax_out [B][R] int32         lowest index among equal maxima; -1 on rows
- *                                   that are not real
+ *   argmax_out [B][R] int32         lowest index among equal maxima (NaN logits
+ *                                   never win); -1 on rows that are not real and
+ *                                   on rows whose logits are all NaN
  *   logits_out [B][R][V] float or NULL (debug output; written for every row)
  * dtype: SSD_F32 (all float) or SSD_BF16 (all bf16, fp32 accumulation).
  * max_n: host-side upper bound on the context lengths (every cu_len[b+1] -
@@ -265,6 +268,31 @@ ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
                                 const uint8_t* copy_gate, const int32_t* argmax, int32_t B,
                                 int32_t W, int32_t D, int32_t* accept_len, int32_t* best_w,
                                 int32_t* best_len, int32_t* next_token, hipStream_t stream);
+
+/*
+ * One verification pass followed by the accept, in the launches of the
+ * verification alone: exactly ssd_blocktri_verify (no logits output) and then
+ * ssd_accept_longest on its argmax_out (paper §3.3 "Parallel Verification with
+ * Block-Triangular Attention" and the longest-validated-continuation rule; write-up
+ * §3.1), for callers that want the step's fixed launch cost lower.  With bf16 the
+ * accept runs in the last workgroup of the LM-head launch; with fp32 it is a launch
+ * of its own.  Arguments and outputs are those of the two calls: cand [B][W][D]
+ * int32 (from ssd_kgram_retrieve), accept_len [B][W], best_w, best_len,
+ * next_token [B] int32; workspace of ssd_verify_workspace_bytes(...) bytes.
+ * Errors: those of ssd_blocktri_verify, and INVALID_ARG for null cand or accept
+ *   outputs.
+ */
+ssd_status_t ssd_blocktri_verify_accept(const void* q, const void* k_pre, const void* v_pre,
+                                        const int32_t* cu_len, int32_t max_n, const void* k_cand,
+                                        const void* v_cand, const int32_t* cand,
+                                        const int32_t* cand_len, const uint8_t* copy_gate,
+                                        const void* lm_head, int32_t B, int32_t W, int32_t D,
+                                        int32_t Hq, int32_t Hkv, int32_t d, int32_t V,
+                                        ssd_dtype_t dtype, float scale, void* attn_out,
+                                        int32_t* argmax_out, int32_t* accept_len, int32_t* best_w,
+                                        int32_t* best_len, int32_t* next_token, void* workspace,
+                                        size_t workspace_bytes, hipEvent_t lm_begin,
+                                        hipEvent_t lm_end, hipStream_t stream);
 
 /*
  * Commit of the accepted draft into the target's KV cache.  Paper §3.3: the

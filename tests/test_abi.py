@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "ssd_verify_forward", "ssd_verify_forward_workspace_bytes",
                           "ssd_pack_weight", "ssd_pack_weight_bytes", "ssd_pack_gate_up",
                           "ssd_pack_gate_up_bytes", "ssd_probe_kgram_retrieve",
-                          "ssd_blocktri_verify_noalloc"}
+                          "ssd_blocktri_verify_noalloc", "ssd_blocktri_verify_accept"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -162,6 +162,27 @@ def test_verify_validation(lib):
     assert f(*_verify_args(dtype=0, Hq=3, Hkv=1, ws_bytes=16)) == 3
     assert f(*_verify_args(ws_bytes=16)) == 3
     assert f(*_verify_args(ws=None)) == 3
+
+
+def _verify_accept_args(**over):
+    a = dict(q=FAKE, k_pre=FAKE, v_pre=FAKE, cu_len=FAKE, max_n=4096, k_cand=FAKE, v_cand=FAKE,
+             cand=FAKE, cand_len=FAKE, copy_gate=FAKE, lm_head=FAKE, B=1, W=10, D=20, Hq=32, Hkv=8,
+             d=128, V=128256, dtype=1, scale=0.088, attn_out=FAKE, argmax_out=FAKE,
+             accept_len=FAKE, best_w=FAKE, best_len=FAKE, next_token=FAKE, ws=FAKE,
+             ws_bytes=1 << 40, ev0=None, ev1=None, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_verify_accept_validation(lib):
+    f = lib.ssd_blocktri_verify_accept
+    for k in ("cand", "accept_len", "best_w", "best_len", "next_token", "q", "argmax_out"):
+        assert f(*_verify_accept_args(**{k: None})) == 1, k
+    assert f(*_verify_accept_args(W=65)) == 1
+    assert f(*_verify_accept_args(D=0)) == 1
+    assert f(*_verify_accept_args(scale=0.0)) == 1
+    assert f(*_verify_accept_args(d=64)) == 2
+    assert f(*_verify_accept_args(ws_bytes=16)) == 3
 
 
 def test_accept_validation(lib):
