@@ -16,8 +16,9 @@ __global__ __launch_bounds__(kWave) void accept_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ best_w, int32_t* __restrict__ best_len,
     int32_t* __restrict__ next_token) {
   __shared__ int s_pred[SSD_MAX_W][kWave];
-  accept_seq(blockIdx.x, threadIdx.x, cand, cand_len, copy_gate, argmax, W, D, accept_len, best_w,
-             best_len, next_token, s_pred);
+  const int b = blockIdx.x;
+  accept_seq(b, threadIdx.x, cand, cand_len, copy_gate, argmax + static_cast<size_t>(b) * (1 + W * D), W,
+             D, accept_len, best_w, best_len, next_token, s_pred);
 }
 
 hipError_t launch_accept(const int32_t* cand, const int32_t* cand_len, const uint8_t* copy_gate,

@@ -18,15 +18,14 @@ namespace ssd {
 // the accepted prefix is an LDS read rather than another global load.
 constexpr int kAcGroup = 16;
 
-// Sequence b, by the calling wavefront (lane = its lane).  s_pred: this wave's
+// Sequence b, by the calling wavefront (lane = its lane).  am: the argmax of
+// sequence b's 1 + W*D rows (global memory or LDS); s_pred: this wave's
 // SSD_MAX_W x 64 ints of LDS.
 __device__ __forceinline__ void accept_seq(
     int b, int lane, const int32_t* __restrict__ cand, const int32_t* __restrict__ cand_len,
-    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ argmax, int W, int D,
+    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ am, int W, int D,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ best_w, int32_t* __restrict__ best_len,
     int32_t* __restrict__ next_token, int (*s_pred)[kWave]) {
-  const int R = 1 + W * D;
-  const int32_t* am = argmax + static_cast<size_t>(b) * R;
   // the gate, every candidate length (lane w) and the first group's tokens and
   // predictions are all requested before any of them is used (the arrays are
   // fixed-size, so the reads are in bounds whatever the gate says)

@@ -47,7 +47,7 @@ struct LmWsView {
   int32_t* n_rows;
   int32_t* row_list;
   int32_t* inv;
-  unsigned long long* keys;  // [rows] greedy argmax keys, zeroed with the compaction
+  unsigned long long* keys;  // [rows] greedy argmax keys by global row, zeroed with the compaction
 };
 
 // With `compact` (bf16 only), one more workgroup of the prefix launch writes the

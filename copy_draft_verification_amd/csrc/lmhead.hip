@@ -294,11 +294,14 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
 
 // Greedy epilogue: per row (this lane's column l32 of each row tile), the best
 // (value, lowest index) over this workgroup's tile, combined over the four waves,
-// then folded into the row's key by a device-wide 64-bit atomic max.
+// then folded into the key of the row's global index (thread i of the workgroup
+// holds grow = the global row of chunk row i, or -1) by a device-wide 64-bit atomic
+// max.
 __device__ __forceinline__ void argmax_epilogue(
     const f32x16 (&acc)[kLmVA][kLmNT], int row0, int rows, int vbase, int V, int wave, int tid,
     int l32, int h, const int32_t* __restrict__ row_list, float* __restrict__ logits_out,
-    float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC], unsigned long long* __restrict__ keys) {
+    float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC], unsigned long long* __restrict__ keys,
+    int grow) {
 #pragma unroll
   for (int t = 0; t < kLmNT; ++t) {
     const int row = row0 + t * 32 + l32;
@@ -322,15 +325,15 @@ __device__ __forceinline__ void argmax_epilogue(
     }
   }
   __syncthreads();
-  for (int i = tid; i < kLmMC; i += 256) {
-    const int row = row0 + i;
-    if (row >= rows) continue;
+  static_assert(kLmMC <= kLmWaves * kWave, "one thread per chunk row");
+  if (grow >= 0) {
+    const int i = tid;
     float bv = red_v[0][i];
     int bi = red_i[0][i];
 #pragma unroll
     for (int w = 1; w < kLmWaves; ++w)
       if (better(red_v[w][i], red_i[w][i], bv, bi)) { bv = red_v[w][i]; bi = red_i[w][i]; }
-    __hip_atomic_fetch_max(keys + row, argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(keys + grow, argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -377,6 +380,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   if (vt >= vtiles || mc >= mchunks || mc * kLmMC >= rows) return;
   const int h = lane >> 5, l32 = lane & 31;
   const int row0 = mc * kLmMC;
+  // greedy: the global row of chunk row tid, for the epilogue (loaded now, used last)
+  int grow = -1;
+  if constexpr (kEpi == kEpiArgmax)
+    if (tid < kLmMC && row0 + tid < rows) grow = row_list[row0 + tid];
   // the gate / up GEMM takes its two A tiles from two matrices (the same 32
   // features of each), so a workgroup covers 128 features instead of 256; a
   // half-tile workgroup covers rows 64w + 32hh .. + 31 of packed tile vt / 2
@@ -563,7 +570,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
                     reinterpret_cast<float(&)[kLmWaves][kLmMC]>(red_s), static_cast<float4*>(part_out));
   } else {
     argmax_epilogue(acc, row0, rows, vbase, V, wave, tid, l32, h, row_list, logits_out, red_v, red_i,
-                    static_cast<unsigned long long*>(part_out));
+                    static_cast<unsigned long long*>(part_out), grow);
   }
 }
 
@@ -719,27 +726,38 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(
 }
 
 // One wave per sequence: the argmax of each of its R rows from the row's key (the
-// low half of a nonzero key is the complemented index; 0 = no value), -1 for rows
-// that are not real; then, when asked, the sequence's accept on those rows.
+// low half of a nonzero key is the complemented index; 0, the value the keys start
+// from, stays on rows that are not real and on real rows whose logits are all NaN:
+// -1); then, when asked, the sequence's accept on those rows, which reads them
+// from LDS.
 __global__ __launch_bounds__(kWave) void argmax_finish_kernel(
-    const unsigned long long* __restrict__ keys, const int32_t* __restrict__ inv, int R,
-    int32_t* __restrict__ argmax_out, AcceptArgs acc) {
+    const unsigned long long* __restrict__ keys, int R, int32_t* __restrict__ argmax_out,
+    AcceptArgs acc) {
+  __shared__ int s_am[1 + SSD_MAX_W * SSD_MAX_D];
   __shared__ int s_pred[SSD_MAX_W][kWave];
   const int b = blockIdx.x, lane = threadIdx.x;
-  for (int r = lane; r < R; r += kWave) {
-    const size_t row = static_cast<size_t>(b) * R + r;
-    const int ci = inv[row];
-    int out = -1;
-    if (ci >= 0) {
-      const unsigned long long k = keys[ci];
-      out = k == 0ull ? -1 : static_cast<int>(~static_cast<uint32_t>(k));
+  const unsigned long long* kb = keys + static_cast<size_t>(b) * R;
+  int32_t* ob = argmax_out + static_cast<size_t>(b) * R;
+  constexpr int kU = 8;  // keys in flight per lane
+  for (int r0 = 0; r0 < R; r0 += kU * kWave) {
+    unsigned long long k[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = r0 + u * kWave + lane;
+      k[u] = r < R ? kb[r] : 0ull;
     }
-    argmax_out[row] = out;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = r0 + u * kWave + lane;
+      if (r >= R) break;
+      const int v = k[u] == 0ull ? -1 : static_cast<int>(~static_cast<uint32_t>(k[u]));
+      ob[r] = v;
+      s_am[r] = v;
+    }
   }
   if (acc.cand == nullptr) return;
-  // the accept reads this wave's argmax stores back
   __syncthreads();
-  accept_seq(b, lane, acc.cand, acc.cand_len, acc.copy_gate, argmax_out, acc.W, acc.D, acc.accept_len,
+  accept_seq(b, lane, acc.cand, acc.cand_len, acc.copy_gate, s_am, acc.W, acc.D, acc.accept_len,
              acc.best_w, acc.best_len, acc.next_token, s_pred);
 }
 
@@ -933,7 +951,7 @@ hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t*
 hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, const AcceptArgs* accept,
                                 hipStream_t s) {
   const LmWs w = lm_ws(ws, B * R);
-  hipLaunchKernelGGL(argmax_finish_kernel, dim3(B), dim3(kWave), 0, s, w.keys, w.inv, R, argmax_out,
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(B), dim3(kWave), 0, s, w.keys, R, argmax_out,
                      accept != nullptr ? *accept : AcceptArgs{});
   return hipGetLastError();
 }
