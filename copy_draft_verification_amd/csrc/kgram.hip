@@ -4,8 +4,9 @@
 // Generation" and write-up §2.6 (up to W continuations of up to D tokens,
 // ranked by recency).
 //
-// One 1024-lane workgroup per sequence scans end positions from the newest
-// (n-2) backwards in chunks of 8192.  A chunk of ids (plus a kappa-1 halo) is
+// One workgroup per sequence (1024 lanes for fewer than 512 sequences, else 256)
+// scans end positions from the newest (n-2) backwards in chunks of 8 per lane
+// (8192 or 2048).  A chunk of ids (plus a kappa-1 halo) is
 // copied from HBM straight into LDS by buffer-to-LDS loads, which hold no
 // registers while in flight; two LDS stages let the next chunk's loads run
 // while the current chunk is tested, and a context of up to two chunks is
@@ -21,19 +22,27 @@
 
 namespace ssd {
 
-constexpr int kKgThreads = 1024;
-constexpr int kKgPer = 8;                              // end positions per lane and chunk
-constexpr int kKgChunk = kKgThreads * kKgPer;          // end positions per chunk
-// Staged ids per chunk: the chunk's end positions, the kappa-1 ids before the
-// oldest of them, and up to 3 more below those, so that the staged range starts
-// at a position congruent to top-7 (mod 4) and every lane's eight ids
-// (top-8t-7 .. top-8t) sit on a 16-byte boundary of LDS.
-constexpr int kKgStage = kKgChunk + (SSD_MAX_KAPPA - 1) + 3;
-constexpr int kKgLoads = (kKgStage + kKgThreads - 1) / kKgThreads;  // loads per lane and chunk (9)
+constexpr int kKgPer = 8;  // end positions per lane and chunk
 constexpr int kKgPad = 8;  // LDS slots before the staged ids (the lowest lane reads from 1 below)
-constexpr int kKgSlots = kKgPad + kKgLoads * kKgThreads;           // ints per LDS stage
 static_assert(kKgPad % 4 == 0 && kKgPad >= kKgPer - 1, "pad keeps 16-byte reads in the array");
-static_assert(kKgLoads <= 31, "vmcnt holds two chunks' loads");
+// Geometry of a workgroup of NT lanes.  Staged ids per chunk: the chunk's end
+// positions, the kappa-1 ids before the oldest of them, and up to 3 more below
+// those, so that the staged range starts at a position congruent to top-7 (mod 4)
+// and every lane's eight ids (top-8t-7 .. top-8t) sit on a 16-byte boundary of LDS.
+template <int NT>
+struct KgGeom {
+  static constexpr int kChunk = NT * kKgPer;                       // end positions per chunk
+  static constexpr int kStage = kChunk + (SSD_MAX_KAPPA - 1) + 3;  // staged ids per chunk
+  static constexpr int kLoads = (kStage + NT - 1) / NT;            // loads per lane and chunk (9)
+  static constexpr int kSlots = kKgPad + kLoads * NT;              // ints per LDS stage
+  static_assert(kLoads <= 31, "vmcnt holds two chunks' loads");
+};
+// Workgroup sizes: 1024 lanes when there are few contexts (each context's scan is
+// the latency of the launch), 256 when there are many (eight workgroups per CU, so
+// some are always streaming while others test or write).
+constexpr int kKgWide = 1024;
+constexpr int kKgNarrow = 256;
+constexpr int kKgNarrowFrom = 512;  // contexts from which the narrow workgroups run
 
 // LDS reads of the stages, written as asm that waits for its own result.  The
 // compiler cannot tell which LDS a pending buffer-to-LDS copy writes, so before a
@@ -63,12 +72,13 @@ __device__ __forceinline__ void lds_ld8(const int* p, i32x4& a, i32x4& b) {
 // eight consecutive k per chunk, then a wave sum and a sum over the waves in wave
 // order), fire = z >= thr.  Thread 0 writes z_out[b] (if given) and fire_out[b].
 // Returns fire to every thread.
+template <int NT>
 __device__ __forceinline__ bool probe_in_block(const KgProbe& pr, int b, float* s_part, int* s_fire) {
   const int t = threadIdx.x;
   float acc = 0.f;
   if ((pr.hidden & 7) == 0) {
     const int nch = pr.hidden >> 3;
-    for (int c = t; c < nch; c += kKgThreads) {
+    for (int c = t; c < nch; c += NT) {
       float hv[8];
       if (pr.bf16) {
         Chunk8<uint16_t> x;
@@ -87,7 +97,7 @@ __device__ __forceinline__ bool probe_in_block(const KgProbe& pr, int b, float* 
       for (int e = 0; e < 8; ++e) acc += wv.at(e) * hv[e];
     }
   } else {
-    for (int k = t; k < pr.hidden; k += kKgThreads) {
+    for (int k = t; k < pr.hidden; k += NT) {
       const float hk = pr.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(pr.h)[static_cast<size_t>(b) * pr.hidden + k])
                                : static_cast<const float*>(pr.h)[static_cast<size_t>(b) * pr.hidden + k];
       acc += pr.w[k] * hk;
@@ -98,7 +108,7 @@ __device__ __forceinline__ bool probe_in_block(const KgProbe& pr, int b, float* 
   __syncthreads();
   if (t == 0) {
     float z = 0.f;
-    for (int i = 0; i < kKgThreads / kWave; ++i) z += s_part[i];
+    for (int i = 0; i < NT / kWave; ++i) z += s_part[i];
     const bool f = z >= pr.thr;
     if (pr.z_out) pr.z_out[b] = z;
     pr.fire_out[b] = f ? 1 : 0;
@@ -108,11 +118,12 @@ __device__ __forceinline__ bool probe_in_block(const KgProbe& pr, int b, float* 
   return *s_fire != 0;
 }
 
-// Two workgroups per CU (8 waves per SIMD, 2 x 72 KB of LDS): while one
-// compares, the other's loads are in flight.  With pr.h set, the workgroup first
+// Eight waves per SIMD: two 1024-lane workgroups per CU (2 x 72 KB of LDS) or eight
+// 256-lane ones (8 x 19 KB); while some compare, the others' loads are in flight.  With pr.h set, the workgroup first
 // computes its sequence's probe (probe_in_block) while its first chunk copies are
 // in flight, and scans only if the probe fired; `fire` is then not read.
-__global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT, 8) void kgram_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ cu_len, int kappa, int W, int D,
     const uint8_t* __restrict__ fire, int32_t* __restrict__ match_end, int32_t* __restrict__ n_match,
     int32_t* __restrict__ cand, int32_t* __restrict__ cand_len, uint8_t* __restrict__ copy_gate,
@@ -120,8 +131,10 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
   // the two stages, read through the asm helpers above
   __shared__ int s_suffix[SSD_MAX_KAPPA];
   __shared__ int s_list[SSD_MAX_W];
-  __shared__ int s_wave[kKgThreads / kWave];
-  __shared__ float s_part[kKgThreads / kWave];
+  using G = KgGeom<NT>;
+  constexpr int kKgChunk = G::kChunk, kKgLoads = G::kLoads, kKgSlots = G::kSlots;
+  __shared__ int s_wave[NT / kWave];
+  __shared__ float s_part[NT / kWave];
   __shared__ int s_fire;
   __shared__ __attribute__((aligned(16))) int st0[kKgSlots];
   __shared__ __attribute__((aligned(16))) int st1[kKgSlots];
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
   const int n = cu_len[b + 1] - base;
   const bool fused = pr.h != nullptr;
   const bool active = (fused || fire == nullptr || fire[b] != 0) && n >= kappa + 1;
-  if (fused && !active) probe_in_block(pr, b, s_part, &s_fire);
+  if (fused && !active) probe_in_block<NT>(pr, b, s_part, &s_fire);
   int found = 0;
   if (active) {
     const int lo = kappa - 1;
@@ -166,8 +179,8 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
 #pragma unroll
       for (int u = 0; u < kKgLoads; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            res, (__attribute__((address_space(3))) void*)(stage + kKgPad + u * kKgThreads + wave * kWave),
-            4, u * kKgThreads >= room ? kOutOfRange : u == 0 ? max(i0, 0) * 4 : (i0 + u * kKgThreads) * 4,
+            res, (__attribute__((address_space(3))) void*)(stage + kKgPad + u * NT + wave * kWave),
+            4, u * NT >= room ? kOutOfRange : u == 0 ? max(i0, 0) * 4 : (i0 + u * NT) * 4,
             0, 0, kNonTemporal);
     };
     // Test the chunk whose newest end position is top, staged in `stage`; false
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
         }
       }
       int total;
-      int rank = found + block_excl_scan<kKgThreads, true>(__popc(mask), s_wave, total);
+      int rank = found + block_excl_scan<NT, true>(__popc(mask), s_wave, total);
       while (mask) {
         const int i = __ffs(mask) - 1;
         mask &= mask - 1;
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
     issue(st1, top - kKgChunk);
     // fused probe: computed while the first copies are in flight; a closed probe
     // retrieves nothing
-    const bool fired = !fused || probe_in_block(pr, b, s_part, &s_fire);
+    const bool fired = !fused || probe_in_block<NT>(pr, b, s_part, &s_fire);
     for (; fired;) {
       if (!chunk(st0, top)) break;
       top -= kKgChunk;
@@ -235,12 +248,12 @@ __global__ __launch_bounds__(kKgThreads, 8) void kgram_kernel(
   }
   __syncthreads();
   const int M = min(found, W);
-  for (int w = t; w < W; w += kKgThreads) {
+  for (int w = t; w < W; w += NT) {
     const int p = w < M ? s_list[w] : -1;
     match_end[static_cast<size_t>(b) * W + w] = p;
     cand_len[static_cast<size_t>(b) * W + w] = w < M ? min(D, n - 1 - p) : 0;
   }
-  for (int e = t; e < W * D; e += kKgThreads) {
+  for (int e = t; e < W * D; e += NT) {
     const int w = e / D, j = e - w * D;
     int v = -1;
     if (w < M) {
@@ -259,8 +272,12 @@ hipError_t launch_kgram(const int32_t* ids, const int32_t* cu_len, int B, int ka
                         const uint8_t* fire, int32_t* match_end, int32_t* n_match, int32_t* cand,
                         int32_t* cand_len, uint8_t* copy_gate, hipStream_t s, const KgProbe* probe) {
   const KgProbe pr = probe != nullptr ? *probe : KgProbe{};
-  hipLaunchKernelGGL(kgram_kernel, dim3(B), dim3(kKgThreads), 0, s, ids, cu_len, kappa, W, D, fire,
-                     match_end, n_match, cand, cand_len, copy_gate, pr);
+  if (B < kKgNarrowFrom)
+    hipLaunchKernelGGL(kgram_kernel<kKgWide>, dim3(B), dim3(kKgWide), 0, s, ids, cu_len, kappa, W, D, fire,
+                       match_end, n_match, cand, cand_len, copy_gate, pr);
+  else
+    hipLaunchKernelGGL(kgram_kernel<kKgNarrow>, dim3(B), dim3(kKgNarrow), 0, s, ids, cu_len, kappa, W, D,
+                       fire, match_end, n_match, cand, cand_len, copy_gate, pr);
   return hipGetLastError();
 }
 

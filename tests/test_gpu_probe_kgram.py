@@ -63,6 +63,7 @@ def _fused_vs_oracle(wl, d, W=None, D=None, kappa=None):
     ("llama8b_b1", {}),
     ("llama8b_b32", {"anchor": "natural"}),
     ("qwen3_8b_b8", {}),
+    ("small_bf16", {"B": 600, "n": (50, 5000), "anchor": "natural"}),  # 256-lane workgroups
 ])
 def test_fused_probe_kgram(name, over):
     wl = generate(name, with_tensors=False, **over)

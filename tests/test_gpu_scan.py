@@ -51,6 +51,25 @@ def test_scan_planted_long_contexts(kappa, W, D):
     print(f"[ok] M={ko['n_match'].tolist()}", flush=True)
 
 
+# Many contexts (512 and more run on 256-lane workgroups, whose chunks are 2048
+# end positions): random lengths plus lengths around multiples of 2048, matches
+# planted at or across those multiples.
+MANY = ([int(x) for x in np.random.default_rng(4301).integers(5, 12000, 560)]
+        + [2048, 2049, 2050, 4096, 4096 + 3, 6144 - 1, 2048 * 5 + 1, 2047, 66, 67, 68, 4100])
+
+
+@pytest.mark.parametrize("kappa,W,D", [(5, 10, 20), (1, 10, 20), (3, 64, 64), (64, 5, 20)])
+def test_scan_planted_many_contexts(kappa, W, D):
+    print(f"[case] scan planted, many contexts, kappa={kappa} W={W} D={D} B={len(MANY)}", flush=True)
+    ids, cu = scan_ids_planted(MANY, kappa=kappa, seed=4400 + kappa, boundary=2048)
+    g = cdv.kgram_retrieve(up(ids), up(cu), kappa, W, D)
+    torch.cuda.synchronize()
+    ko = oracle.kgram_retrieve(ids, cu, kappa, W, D)
+    _compare(g, ko, f"many kappa={kappa}")
+    print(f"[ok] contexts with a match {int((ko['n_match'] > 0).sum())}, "
+          f"with W {int((ko['n_match'] >= W).sum())}", flush=True)
+
+
 def test_scan_small_vocabulary_many_matches():
     # vocabulary of 3: every chunk holds many matches, W of them are kept
     rng = np.random.default_rng(4200)

@@ -596,12 +596,13 @@ def scan_ids_device(total, n=SCAN_N, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, d
     return ids, cu
 
 
-def scan_ids_planted(ns, kappa=KAPPA, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, max_occ=14):
+def scan_ids_planted(ns, kappa=KAPPA, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, max_occ=14,
+                     boundary=8192):
     """Host contexts for scan parity: one context of Zipf ids per length in `ns`,
     in which the anchor's kappa-gram is copied to 0..max_occ earlier end
     positions, spread over the whole context, some placed right at or across
-    multiples of 8192 (powers of two are natural chunk boundaries for a scan).
-    Returns (ids int32 [sum(ns)], cu_len int32 [len(ns) + 1])."""
+    multiples of `boundary` (powers of two are natural chunk boundaries for a
+    scan).  Returns (ids int32 [sum(ns)], cu_len int32 [len(ns) + 1])."""
     cdf = _zipf_cdf(V, zipf)
     out = []
     for b, n in enumerate(ns):
@@ -612,7 +613,8 @@ def scan_ids_planted(ns, kappa=KAPPA, V=SCAN_V, zipf=SCAN_ZIPF, seed=SCAN_SEED, 
         ends = set()
         for _ in range(occ):
             if rng.random() < 0.3:   # near a power-of-two boundary
-                p = int(rng.integers(1, max(2, n // 8192 + 1))) * 8192 + int(rng.integers(-kappa, kappa + 1))
+                p = (int(rng.integers(1, max(2, n // boundary + 1))) * boundary
+                     + int(rng.integers(-kappa, kappa + 1)))
             else:
                 p = int(rng.integers(kappa - 1, n - 1))
             if kappa - 1 <= p <= n - 2 - kappa:   # keep the suffix itself intact
