@@ -15,7 +15,8 @@
 // from its eight ids (two 16-byte LDS reads), so lane order equals recency
 // order.  Matches are compacted in that order by a workgroup prefix sum over
 // per-lane counts, and the scan stops as soon as W matches are known.  The
-// candidate gather then copies L_w = min(D, n-1-p_w) ids after each match.
+// candidate gather then copies L_w = min(D, n-1-p_w) ids after each match, from
+// LDS where the chunk the scan ended in (or the kappa-gram suffix) holds them.
 #include "common.h"
 #include "kernels.h"
 #include "switchsd.h"
@@ -145,6 +146,9 @@ __global__ __launch_bounds__(NT, 8) void kgram_kernel(
   const bool active = (fused || fire == nullptr || fire[b] != 0) && n >= kappa + 1;
   if (fused && !active) probe_in_block<NT>(pr, b, s_part, &s_fire);
   int found = 0;
+  // the chunk the scan ended in: its stage still holds positions g_abase .. g_top
+  const int* g_stage = st0;
+  int g_abase = 0, g_top = -1;
   if (active) {
     const int lo = kappa - 1;
     // the LDS destination of a buffer-to-LDS load (M0) must be wave-uniform
@@ -226,7 +230,12 @@ __global__ __launch_bounds__(NT, 8) void kgram_kernel(
       }
       found += total;
       const int nt = top - kKgChunk;
-      if (nt < lo || found >= W) return false;
+      if (nt < lo || found >= W) {
+        g_stage = stage;
+        g_abase = abase;
+        g_top = top;
+        return false;
+      }
       issue(stage, nt - kKgChunk);
       return true;
     };
@@ -253,12 +262,20 @@ __global__ __launch_bounds__(NT, 8) void kgram_kernel(
     match_end[static_cast<size_t>(b) * W + w] = p;
     cand_len[static_cast<size_t>(b) * W + w] = w < M ? min(D, n - 1 - p) : 0;
   }
+  // Candidate gather: id q = p+1+j from the last chunk's stage when it holds q,
+  // from the suffix for the newest kappa positions, else from memory (matches of
+  // earlier, newer chunks whose stage has been reloaded).
   for (int e = t; e < W * D; e += NT) {
     const int w = e / D, j = e - w * D;
     int v = -1;
     if (w < M) {
       const int p = s_list[w];
-      if (j < min(D, n - 1 - p)) v = ids[base + p + 1 + j];
+      if (j < min(D, n - 1 - p)) {
+        const int q = p + 1 + j;
+        if (q >= g_abase && q <= g_top) v = lds_ld(g_stage + kKgPad + q - g_abase);
+        else if (q >= n - kappa) v = s_suffix[q - (n - kappa)];
+        else v = ids[base + q];
+      }
     }
     cand[static_cast<size_t>(b) * W * D + e] = v;
   }
