@@ -3,16 +3,17 @@
 //
 // Every query row of a sequence sees the whole prefix; row (w, j) additionally
 // sees candidate keys (w, 0..j).  The pass is split accordingly:
-//   1. prefix sweep: a dense, unmasked attention of all real rows against the
-//      prefix K/V, split over key ranges (flash-decoding style partials m, l, o
-//      in the exp2 domain).  bf16 runs on 32x32x16 MFMA with the g query heads
-//      of one KV head packed into the M dimension (g*R rows share one K/V
-//      stream); fp32 runs on the vector ALU.
-//   2. merge: per (row, head) the split partials are combined and the row's own
-//      candidate triangle (at most D keys) is folded in exactly, then the
-//      normalised output is written.  Rows that are not real are written as 0.
-// No mask is ever materialised: the candidate triangle lives only in the
-// merge's loop bound j.
+//   1. prefix sweep: attention of all real rows against key ranges ("slots",
+//      flash-decoding style partials m, l, o in the exp2 domain).  bf16 runs on
+//      32x32x16 MFMA with the g query heads of one KV head packed together (g*R
+//      rows share one K/V stream); the prefix is split into ranges, and one more
+//      slot holds the W*D candidate keys, where each row's visible range
+//      (w*D .. w*D + j) is applied to the scores in registers.  fp32 runs the
+//      prefix ranges on the vector ALU.
+//   2. merge: per (row, head) the partials are combined and the normalised
+//      output is written (fp32: the row's own candidate triangle, at most D keys,
+//      is folded in exactly here).  Rows that are not real are written as 0.
+// No mask is ever materialised in memory.
 #include "common.h"
 #include "kernels.h"
 
