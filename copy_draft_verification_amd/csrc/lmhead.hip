@@ -302,20 +302,69 @@ __device__ __forceinline__ void argmax_epilogue(
     int l32, int h, const int32_t* __restrict__ row_list, float* __restrict__ logits_out,
     float (&red_v)[kLmWaves][kLmMC], int (&red_i)[kLmWaves][kLmMC], unsigned long long* __restrict__ keys,
     int grow) {
+  // Debug output, on its own path: inside the scan below, a store per value behind
+  // its own test made the epilogue a chain of about 1400 branches, 16 us per
+  // workgroup even with logits_out null.
+  if (logits_out != nullptr) {
+#pragma unroll
+    for (int t = 0; t < kLmNT; ++t) {
+      const int row = row0 + t * 32 + l32;
+      if (row >= rows) continue;
+      float* lr = logits_out + static_cast<size_t>(row_list[row]) * V;
+#pragma unroll
+      for (int a = 0; a < kLmVA; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (v < V) lr[v] = acc[a][t][r];
+        }
+    }
+  }
+  // Per row tile, this lane's 32 values: their maximum by a tree of fmaxf (which
+  // never returns a NaN against a number, so NaN never wins), then the first
+  // position holding it by a tree of mins over positions (positions rise with the
+  // token index, so the first is the lowest); values past V take no part.  A linear
+  // scan with `better` was a dependent chain through every value (with && and ||,
+  // a few branches per value: 16 us per workgroup; branch-free, still 6.6 us at one
+  // wave per SIMD).
+  constexpr int kN = kLmVA * 16;
+  const bool full = vbase + kLmVA * 32 <= V;  // every value of the tile is a token
+  // token index of position p = 16 a + r of this lane
+  auto tok = [&](int p) { return vbase + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * h + (p & 3); };
 #pragma unroll
   for (int t = 0; t < kLmNT; ++t) {
-    const int row = row0 + t * 32 + l32;
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    float xs[kN];
 #pragma unroll
     for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float x = acc[a][t][r];
-        if (v < V && better(x, v, bv, bi)) { bv = x; bi = v; }
-        if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row_list[row]) * V + v] = x;
-      }
+      for (int r = 0; r < 16; ++r) xs[a * 16 + r] = acc[a][t][r];
+    if (!full) {
+#pragma unroll
+      for (int p = 0; p < kN; ++p) xs[p] = tok(p) < V ? xs[p] : -INFINITY;
+    }
+    float mt[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) mt[i] = xs[i];
+#pragma unroll
+    for (int w = kN / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
+    const float mx = mt[0];
+    int it[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) it[i] = xs[i] == mx ? i : kN;
+#pragma unroll
+    for (int w = kN / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) it[i] = min(it[i], it[i + w]);
+    // A position past V holds -inf: it can equal mx only when every value is -inf
+    // or NaN, and then it must not be reported.  Every value NaN: mx is NaN and no
+    // position matches.  Either way the lane offers (-inf, none), which any value
+    // of another lane beats.
+    const int pbest = it[0];
+    const bool found = (pbest < kN) & (full | (tok(pbest) < V));
+    float bv = found ? mx : -INFINITY;
+    int bi = found ? tok(pbest) : INT_MAX;
     const float ov = __shfl_xor(bv, 32, kWave);
     const int oi = __shfl_xor(bi, 32, kWave);
     if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
