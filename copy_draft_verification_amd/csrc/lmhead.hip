@@ -207,6 +207,9 @@ __device__ __forceinline__ void sample_epilogue(
     exclv[t] = excl;
   }
   const float inv_t2 = sa.inv_t * kLog2e;
+  const bool full = vbase + kLmVA * 32 <= V;  // every value of the tile is a token
+  // token index of position p = 16 a + r of this lane
+  auto tok = [&](int p) { return vbase + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * h + (p & 3); };
   // one call per row tile with a compile-time tile index, so that the
   // accumulators stay in registers (a loop this large is not unrolled)
   auto tile = [&](auto Tc) {
@@ -214,17 +217,30 @@ __device__ __forceinline__ void sample_epilogue(
     const int grow = growv[t], nc = ncv[t];
     const uint32_t excl = exclv[t];
     const int32_t* ch = sa.children + static_cast<size_t>(grow < 0 ? 0 : grow) * sa.W;
-    // log-sum-exp in the base-2 domain (t * log2 e), converted at the end
-    float m = -INFINITY;
+    // Scans over the lane's 32 values in four interleaved chains (short dependent
+    // chains without holding a second copy of the values, which would not fit beside
+    // the accumulators): the maximum of t2 = log2(e) t, the sum of 2^(t2 - max), and
+    // the best t + Gumbel noise over the tokens that are not children, first
+    // position on ties.  Values past V take no part (-inf); children take no part
+    // in the residual draw.
+    constexpr int kN = kLmVA * 16;
+    float v32[kN];
 #pragma unroll
-    for (int a = 0; a < kLmVA; ++a)
+    for (int p = 0; p < kN; ++p)
+      v32[p] = (full | (tok(p) < V)) ? acc[p >> 4][t][p & 15] * inv_t2 : -INFINITY;
+    auto max4 = [&]() {
+      float c[4] = {v32[0], v32[1], v32[2], v32[3]};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = vbase + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (v < V) m = fmaxf(m, acc[a][t][r] * inv_t2);
-      }
-    float s = 0.f, by = -INFINITY;
-    int bx = INT_MAX;
+      for (int p = 4; p < kN; ++p) c[p & 3] = fmaxf(c[p & 3], v32[p]);
+      return fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+    };
+    float m = max4();
+    // a lane without a valid value keeps m = -inf and s = 0
+    const float mref = m == -INFINITY ? 0.f : m;
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kN; ++p) sc[p & 3] += __builtin_amdgcn_exp2f(v32[p] - mref);
+    float s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
 #pragma unroll
     for (int a = 0; a < kLmVA; ++a)
 #pragma unroll
@@ -234,21 +250,36 @@ __device__ __forceinline__ void sample_epilogue(
                                        sa.k0, sa.k1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q + i, x = x0 + i;
-          if (x < V) {
-            const float tv = acc[a][t][r] * sa.inv_t;
-            s += __builtin_amdgcn_exp2f(acc[a][t][r] * inv_t2 - m);
-            if ((excl >> (a * 16 + r)) & 1u) {
-              if (grow >= 0)
-                for (int k = 0; k < nc; ++k)
-                  if (ch[k] == x) sa.child_logit[static_cast<size_t>(grow) * sa.W + k] = tv;
-            } else {
-              const float y = tv + gumbel_of(i == 0 ? wd.x : i == 1 ? wd.y : i == 2 ? wd.z : wd.w);
-              if (better(y, x, by, bx)) { by = y; bx = x; }
-            }
-          }
+          const int p = a * 16 + 4 * q + i;
+          const bool draw = (full | (x0 + i < V)) & (((excl >> p) & 1u) == 0u);
+          const float g = gumbel_of(i == 0 ? wd.x : i == 1 ? wd.y : i == 2 ? wd.z : wd.w);
+          v32[p] = draw ? acc[a][t][4 * q + i] * sa.inv_t + g : -INFINITY;
         }
       }
+    const float ymax = max4();
+    // first position holding ymax: per chain the lowest matching position, then the least
+    int pc[4] = {kN, kN, kN, kN};
+#pragma unroll
+    for (int p = kN - 1; p >= 0; --p) pc[p & 3] = v32[p] == ymax ? p : pc[p & 3];
+    const int pb = min(min(pc[0], pc[1]), min(pc[2], pc[3]));
+    // -inf marks both "no draw" and a drawn -inf: report only a drawn position
+    bool found = pb < kN;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+      if (i == pb) found = found & (full | (tok(i) < V)) & (((excl >> i) & 1u) == 0u);
+    float by = found ? ymax : -INFINITY;
+    int bx = found ? tok(pb) : INT_MAX;
+    // the children's t values go to their slots (rare: few lanes hold a child)
+    if (excl != 0u && grow >= 0) {
+#pragma unroll
+      for (int p = 0; p < kN; ++p)
+        if ((excl >> p) & 1u) {
+          const int x = tok(p);
+          const float tv = acc[p >> 4][t][p & 15] * sa.inv_t;
+          for (int k = 0; k < nc; ++k)
+            if (ch[k] == x) sa.child_logit[static_cast<size_t>(grow) * sa.W + k] = tv;
+        }
+    }
     {
       const float om = __shfl_xor(m, 32, kWave), os = __shfl_xor(s, 32, kWave);
       const float oy = __shfl_xor(by, 32, kWave);
