@@ -32,6 +32,7 @@ ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, 
   if (W > SSD_MAX_W || D > SSD_MAX_D || Hq % Hkv != 0 || !valid_dtype(dt)) return SSD_ERR_INVALID_ARG;
   const long long R = 1 + static_cast<long long>(W) * D;
   if (static_cast<long long>(B) * R * Hq * d > (1ll << 40)) return SSD_ERR_INVALID_ARG;
+  if (static_cast<long long>(B) * R * Hq >= (1ll << 31)) return SSD_ERR_UNSUPPORTED;
   if (dt == SSD_BF16) {
     if (d != 128 || (static_cast<long long>(Hq) * d) % 256 != 0) return SSD_ERR_UNSUPPORTED;
     if (!fits_byte_offsets(B, max_n, R, Hkv, d, static_cast<long long>(Hq) * d))
@@ -137,6 +138,14 @@ size_t ssd_pack_gate_up_bytes(int32_t inter, int32_t K) {
 namespace {
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// The verification kernels read q, K, V and the LM-head weights and write the
+// attention output in 16-byte pieces.
+bool verify_aligned(const void* q, const void* k_pre, const void* v_pre, const void* k_cand,
+                    const void* v_cand, const void* lm_head, const void* attn_out) {
+  return aligned16(q) && aligned16(k_pre) && aligned16(v_pre) && aligned16(k_cand) &&
+         aligned16(v_cand) && aligned16(lm_head) && aligned16(attn_out);
+}
+
 ssd_status_t pack(const void* w, const void* w2, int32_t rows, int32_t K, void* packed,
                   size_t packed_bytes, hipStream_t stream) {
   if (!w || !packed || rows < 1 || K < 1) return SSD_ERR_INVALID_ARG;
@@ -183,6 +192,7 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
       !lm_head || !attn_out || !argmax_out)
     return SSD_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return SSD_ERR_INVALID_ARG;
+  if (!verify_aligned(q, k_pre, v_pre, k_cand, v_cand, lm_head, attn_out)) return SSD_ERR_INVALID_ARG;
   const ssd_status_t st = check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype);
   if (st != SSD_OK) return st;
   const bool bf16 = dtype == SSD_BF16;
@@ -193,26 +203,17 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
   float* ws_attn = static_cast<float*>(workspace);
   void* ws_lm = static_cast<char*>(workspace) + L.attn_bytes;
   const int R = 1 + W * D;
-  // bf16: the row compaction runs as one more workgroup of the attention launch
+  // the row compaction runs as one more workgroup of the attention launch
   const ssd::LmWsView cv = ssd::lm_ws_view(ws_lm, B * R);
   hipError_t e = ssd::launch_attention(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len, copy_gate,
                                        B, W, D, Hq, Hkv, d, bf16, scale, L.attn, attn_out, ws_attn,
-                                       stream, bf16 ? &cv : nullptr);
+                                       stream, &cv);
   if (e != hipSuccess) return SSD_ERR_HIP;
-  if (!bf16) {
-    e = ssd::launch_compact_rows(ws_lm, B * R, R, W, D, cand_len, copy_gate, stream);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-  }
   e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
                          lm_begin, lm_end, stream);
   if (e != hipSuccess) return SSD_ERR_HIP;
-  // bf16: one launch turns the LM head's per-row keys into argmax_out and accepts
-  if (bf16) return from_hip(ssd::launch_argmax_finish(ws_lm, B, R, argmax_out, acc, stream));
-  e = ssd::launch_argmax_reduce(ws_lm, L.lm, B * R, argmax_out, stream);
-  if (e != hipSuccess || acc == nullptr) return from_hip(e);
-  return from_hip(ssd::launch_accept(acc->cand, acc->cand_len, acc->copy_gate, argmax_out, B, W, D,
-                                     acc->accept_len, acc->best_w, acc->best_len, acc->next_token,
-                                     stream));
+  // one launch turns the LM head's per-row keys into argmax_out and accepts
+  return from_hip(ssd::launch_argmax_finish(ws_lm, B, R, argmax_out, acc, stream));
 }
 
 // The no-allocation variant's scratch: one array per GPU (each device that loads
@@ -339,6 +340,7 @@ ssd_status_t ssd_blocktri_verify_sample(
     return SSD_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return SSD_ERR_INVALID_ARG;
   if (!(std::isfinite(temperature) && temperature > 0.f)) return SSD_ERR_INVALID_ARG;
+  if (!verify_aligned(q, k_pre, v_pre, k_cand, v_cand, lm_head, attn_out)) return SSD_ERR_INVALID_ARG;
   const ssd_status_t st = check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype);
   if (st != SSD_OK) return st;
   if (dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;

@@ -520,46 +520,83 @@ __global__ __launch_bounds__(kAttThreads, 1) void attn_prefix_bf16_kernel(
 // bf16 merge: one wave per (sequence, row, query head).  Combines the prefix slots
 // that hold keys of this sequence and the candidate slot (a row without visible
 // candidate keys left m = -inf there, which weighs 0), normalises and writes bf16.
-// Rows that are not real are written as 0.
+// Rows that are not real are written as 0.  The kernel is a chain of dependent
+// loads, so every load it needs is issued up front, from slot indices clamped into
+// the workspace, and the first round uses them without a branch (a branch would let
+// the compiler sink the loads behind it): lane s reads slot s's (m, l), and the
+// outputs of the first kMergeBatch slots come with them; further slots take more
+// rounds.  Requires B*R*Hq < 2^31 and nsplit + 1 <= 64.
+constexpr int kMergeBatch = 8;
 __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(
     const int32_t* __restrict__ cu_len, const int32_t* __restrict__ cand_len,
     const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int W, int D, int nsplit,
     int chunk, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o, uint16_t* __restrict__ out) {
-  const size_t item = static_cast<size_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, r, hq)
+  const uint32_t item = blockIdx.x * 4u + threadIdx.x / kWave;  // (b, r, hq)
   const int lane = threadIdx.x & (kWave - 1);
-  if (item >= static_cast<size_t>(B) * R * Hq) return;
+  const uint32_t per_slot = static_cast<uint32_t>(B) * R * Hq;
+  if (item >= per_slot) return;
   const int r = static_cast<int>((item / Hq) % R);
-  const int b = static_cast<int>(item / (static_cast<size_t>(Hq) * R));
-  uint16_t* op = out + item * kAttD;  // out[b][r][hq*d + ...]
-  if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0)) {
-    *reinterpret_cast<uint32_t*>(op + 2 * lane) = 0u;
-    return;
-  }
+  const int b = static_cast<int>(item / (static_cast<uint32_t>(Hq) * R));
+  const int nslot = nsplit + 1;  // the prefix slots, then the candidate slot
+  const int w = r > 0 ? (r - 1) / D : 0, j = r > 0 ? (r - 1) - w * D : 0;
+  const int gate = copy_gate[b];
+  const int lw = cand_len[static_cast<size_t>(b) * W + w];
   const int n_b = cu_len[b + 1] - cu_len[b];
-  const int nsp = min(nsplit, (n_b + chunk - 1) / chunk);
-  const size_t per_slot = static_cast<size_t>(B) * R * Hq;
-  const size_t row_item = item;  // == (b*R + r)*Hq + hq
-  float M = ws_m[static_cast<size_t>(nsplit) * per_slot + row_item];
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, ws_m[s * per_slot + row_item]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  auto add = [&](size_t po) {
-    const float f = __builtin_amdgcn_exp2f(ws_m[po] - M);
-    L += f * ws_l[po];
-    const float2 v = *reinterpret_cast<const float2*>(ws_o + po * kAttD + 2 * lane);
-    o0 += f * v.x;
-    o1 += f * v.y;
+  const size_t pl = static_cast<size_t>(lane < nslot ? lane : nslot - 1) * per_slot + item;
+  const float m_l = ws_m[pl], l_l = ws_l[pl];
+  float2 ov[kMergeBatch];
+  auto load_o = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const size_t s = static_cast<size_t>(min(s0 + u, nslot - 1));
+      ov[u] = *reinterpret_cast<const float2*>(ws_o + (s * per_slot + item) * kAttD + 2 * lane);
+    }
   };
-  for (int s = 0; s < nsp; ++s) add(s * per_slot + row_item);
-  add(static_cast<size_t>(nsplit) * per_slot + row_item);
+  load_o(0);
+  // every load above is issued before anything waits for one of them
+  __builtin_amdgcn_sched_barrier(0);
+  // bitwise, so that no branch separates the loads from their use
+  const bool real = (gate != 0) & ((r == 0) | (j < min(max(lw, 0), D)));
+  const int nsp = min(nsplit, (n_b + chunk - 1) / chunk);
+  auto used = [&](int s) { return s < nslot && (s < nsp || s == nsplit); };
+  const bool valid = used(lane);
+  const float M = wave_max(valid ? m_l : -INFINITY);
+  const float f = valid ? __builtin_amdgcn_exp2f(m_l - M) : 0.f;
+  const float L = wave_sum(valid ? f * l_l : 0.f);
+  float o0 = 0.f, o1 = 0.f;
+  auto fold = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u;
+      const float fs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(s, kWave - 1)));
+      o0 += used(s) ? fs * ov[u].x : 0.f;
+      o1 += used(s) ? fs * ov[u].y : 0.f;
+    }
+  };
+  fold(0);
+  for (int s0 = kMergeBatch; s0 < nslot; s0 += kMergeBatch) {
+    load_o(s0);
+    fold(s0);
+  }
   const float inv = 1.f / L;
   const uint32_t packed = static_cast<uint32_t>(f32_to_bf16(o0 * inv)) |
                           (static_cast<uint32_t>(f32_to_bf16(o1 * inv)) << 16);
-  *reinterpret_cast<uint32_t*>(op + 2 * lane) = packed;
+  *reinterpret_cast<uint32_t*>(out + static_cast<size_t>(item) * kAttD + 2 * lane) = real ? packed : 0u;
 }
 
 // ----------------------------------------------------------------- fp32 VALU
-// One wavefront per (row, head); lanes hold d/64 output elements each.
+// A workgroup of four wavefronts takes four consecutive rows of one query head,
+// so all four read the same keys: the whole workgroup stages each block of 64 keys
+// of K and V in LDS with coalesced 16-byte loads, issuing the next block's loads
+// before the current one is used.  Scores: lane = key, a d-long dot product per
+// lane against the wave's q (read from LDS as a broadcast), so the running max and
+// sum take one wave reduction per 64 keys rather than one per key.  P.V: lane =
+// output element, the block's 64 probabilities taken from the score lanes with
+// readlane (keys past the range have p = 0 and V = 0).
+constexpr int kF32Rows = 4;   // rows (wavefronts) per workgroup
+constexpr int kF32Keys = 64;  // keys per LDS block
+
 template <int DPL>
 __global__ __launch_bounds__(256) void attn_prefix_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pre, const float* __restrict__ v_pre,
@@ -568,39 +605,87 @@ __global__ __launch_bounds__(256) void attn_prefix_f32_kernel(
     int chunk, float scale_log2, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o) {
   constexpr int d = DPL * kWave;
+  constexpr int d4 = d / 4;                        // 16-byte chunks per key row
+  constexpr int kKs = d4 + 1;                      // padded K row, in chunks
+  constexpr int kLd = kF32Keys * d4 / 256;         // chunks per thread per operand
+  __shared__ float4 sK[kF32Keys * kKs];
+  __shared__ float sV[kF32Keys * d];
+  __shared__ float4 sQ[kF32Rows][d4];
   const int b = blockIdx.y, split = blockIdx.z;
-  const int rh = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (rh >= R * Hq || copy_gate[b] == 0) return;
-  const int r = rh / Hq, hq = rh - r * Hq;
-  if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, true)) return;
+  const int rtiles = (R + kF32Rows - 1) / kF32Rows;
+  const int hq = blockIdx.x / rtiles;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int r = (blockIdx.x - hq * rtiles) * kF32Rows + wave;
+  if (copy_gate[b] == 0) return;
   const int base = cu_len[b];
   const int n_b = cu_len[b + 1] - base;
   const int k0 = split * chunk;
   if (k0 >= n_b) return;
   const int k1 = split == nsplit - 1 ? n_b : min(k0 + chunk, n_b);
+  const bool real = r < R && real_row(r, D, cand_len + static_cast<size_t>(b) * W, true);
+  if (!__syncthreads_or(real)) return;
   const int kv = hq / (Hq / Hkv);
-  float qv[DPL], o[DPL];
-  const float* qp = q + ((static_cast<size_t>(b) * R + r) * Hq + hq) * d;
+  if (real && lane < d4)
+    sQ[wave][lane] = reinterpret_cast<const float4*>(
+        q + ((static_cast<size_t>(b) * R + r) * Hq + hq) * d)[lane];
+  // this thread's chunks of a block: chunk f = tid + 256u is key f / d4, column f % d4
+  float4 rk[kLd], rv[kLd];
+  auto load = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    qv[e] = qp[lane + kWave * e];
-    o[e] = 0.f;
+    for (int u = 0; u < kLd; ++u) {
+      const int f = threadIdx.x + 256 * u, t = f / d4, c = f - (f / d4) * d4;
+      const bool ok = t0 + t < k1;
+      const size_t o = ((static_cast<size_t>(base) + (ok ? t0 + t : k0)) * Hkv + kv) * d4 + c;
+      const float4 kx = reinterpret_cast<const float4*>(k_pre)[o];
+      const float4 vx = reinterpret_cast<const float4*>(v_pre)[o];
+      // component selects (a select of whole float4 values goes through memory)
+      rk[u] = make_float4(ok ? kx.x : 0.f, ok ? kx.y : 0.f, ok ? kx.z : 0.f, ok ? kx.w : 0.f);
+      rv[u] = make_float4(ok ? vx.x : 0.f, ok ? vx.y : 0.f, ok ? vx.z : 0.f, ok ? vx.w : 0.f);
+    }
+  };
+  load(k0);
+  float m = -INFINITY, l = 0.f, o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int t0 = k0; t0 < k1; t0 += kF32Keys) {
+    __syncthreads();  // the previous block has been read by every wave
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int f = threadIdx.x + 256 * u, t = f / d4, c = f - (f / d4) * d4;
+      sK[t * kKs + c] = rk[u];
+      reinterpret_cast<float4*>(sV)[f] = rv[u];
+    }
+    __syncthreads();
+    if (t0 + kF32Keys < k1) load(t0 + kF32Keys);
+    if (real) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int c = 0; c < d4; ++c) {
+        const float4 kk = sK[lane * kKs + c], qq = sQ[wave][c];
+        acc.x += kk.x * qq.x;
+        acc.y += kk.y * qq.y;
+        acc.z += kk.z * qq.z;
+        acc.w += kk.w * qq.w;
+      }
+      const float s = t0 + lane < k1 ? ((acc.x + acc.y) + (acc.z + acc.w)) * scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m, wave_max(s));
+      const float a = exp2f(m - m_new), p = exp2f(s - m_new);
+      l = l * a + wave_sum(p);
+      float pa[DPL][4];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) pa[e][0] = pa[e][1] = pa[e][2] = pa[e][3] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kF32Keys; ++t) {
+        const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) pa[e][t & 3] += pt * sV[t * d + lane + kWave * e];
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + ((pa[e][0] + pa[e][1]) + (pa[e][2] + pa[e][3]));
+      m = m_new;
+    }
   }
-  float m = -INFINITY, l = 0.f;
-  for (int t = k0; t < k1; ++t) {
-    const size_t kvo = ((static_cast<size_t>(base) + t) * Hkv + kv) * d;
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) part += qv[e] * k_pre[kvo + lane + kWave * e];
-    const float s = wave_sum(part) * scale_log2;
-    const float m_new = fmaxf(m, s);
-    const float a = exp2f(m - m_new), p = exp2f(s - m_new);
-    l = l * a + p;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + p * v_pre[kvo + lane + kWave * e];
-    m = m_new;
-  }
+  if (!real) return;
   const size_t po = ((static_cast<size_t>(split) * B + b) * R + r) * Hq + hq;
   if (lane == 0) {
     ws_m[po] = m;
@@ -611,65 +696,126 @@ __global__ __launch_bounds__(256) void attn_prefix_f32_kernel(
 }
 
 // ----------------------------------------------------------------- merge + triangle
-template <typename T, int DPL>
+// fp32 merge: one wave per (sequence, row, query head), laid out as the bf16 merge
+// (lane s holds split s's (m, l); every load issued up front and the first round
+// used without a branch), then the row's own candidate triangle is folded in
+// exactly: keys (w, 0..j), j < D <= 64, lane jj scoring key (w, jj), so one wave max
+// and one wave sum fold it in; lane = output element then accumulates the values.
+// The anchor row (j = -1) sees no candidate key and passes through unchanged.
+template <int DPL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cand, const T* __restrict__ v_cand,
+    const float* __restrict__ q, const float* __restrict__ k_cand, const float* __restrict__ v_cand,
     const int32_t* __restrict__ cu_len, const int32_t* __restrict__ cand_len,
     const uint8_t* __restrict__ copy_gate, int B, int R, int Hq, int Hkv, int W, int D, int nsplit,
     int chunk, float scale_log2, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-    const float* __restrict__ ws_o, T* __restrict__ out) {
-  constexpr int d = DPL * kWave;
-  const size_t item = static_cast<size_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, r, hq)
-  const int lane = threadIdx.x & (kWave - 1);
-  if (item >= static_cast<size_t>(B) * R * Hq) return;
-  const int hq = static_cast<int>(item % Hq);
-  const int r = static_cast<int>((item / Hq) % R);
-  const int b = static_cast<int>(item / (static_cast<size_t>(Hq) * R));
-  T* op = out + item * d;  // out[b][r][hq*d + ...] == out + ((b*R + r)*Hq + hq)*d
-  if (!real_row(r, D, cand_len + static_cast<size_t>(b) * W, copy_gate[b] != 0)) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_f32(op, lane + kWave * e, 0.f);
+    const float* __restrict__ ws_o, float* __restrict__ out, LmWsView compact) {
+  constexpr int d = DPL * kWave, d4 = d / 4;
+  if (compact.row_list != nullptr && blockIdx.x == gridDim.x - 1) {
+    // one more workgroup: the LM head's compact row list (and zeroed argmax keys)
+    __shared__ int s_cwave[256 / kWave];
+    compact_rows_body<256>(B * R, R, W, D, cand_len, copy_gate, compact.row_list, compact.inv,
+                           compact.n_rows, s_cwave, compact.keys);
     return;
   }
+  const uint32_t item = blockIdx.x * 4u + threadIdx.x / kWave;  // (b, r, hq)
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t per_slot = static_cast<uint32_t>(B) * R * Hq;
+  if (item >= per_slot) return;
+  const int hq = static_cast<int>(item % Hq);
+  const int r = static_cast<int>((item / Hq) % R);
+  const int b = static_cast<int>(item / (static_cast<uint32_t>(Hq) * R));
+  const int kv = hq / (Hq / Hkv);
+  const int w = r > 0 ? (r - 1) / D : 0, j = r > 0 ? (r - 1) - w * D : -1;
+  const int jc = j < 0 ? 0 : j;
+  const size_t row0 = (static_cast<size_t>(b) * W * D + static_cast<size_t>(w) * D) * Hkv + kv;
+  const float4* kr = reinterpret_cast<const float4*>(k_cand) +
+                     (row0 + static_cast<size_t>(lane <= jc ? lane : 0) * Hkv) * d4;
+  const float4* qr = reinterpret_cast<const float4*>(q) + static_cast<size_t>(item) * d4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int c = 0; c < d4; ++c) {
+    const float4 kk = kr[c], qq = qr[c];
+    acc.x += kk.x * qq.x;
+    acc.y += kk.y * qq.y;
+    acc.z += kk.z * qq.z;
+    acc.w += kk.w * qq.w;
+  }
+  float vv[kMergeBatch][DPL];
+  auto load_v = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float* vr = v_cand + (row0 + static_cast<size_t>(min(j0 + u, jc)) * Hkv) * d;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) vv[u][e] = vr[lane + kWave * e];
+    }
+  };
+  load_v(0);
+  const int gate = copy_gate[b];
+  const int lw = cand_len[static_cast<size_t>(b) * W + w];
   const int n_b = cu_len[b + 1] - cu_len[b];
+  const size_t pl = static_cast<size_t>(lane < nsplit ? lane : nsplit - 1) * per_slot + item;
+  const float m_l = ws_m[pl], l_l = ws_l[pl];
+  float ov[kMergeBatch][DPL];
+  auto load_o = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float* src = ws_o + (static_cast<size_t>(min(s0 + u, nsplit - 1)) * per_slot + item) * d;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[u][e] = src[lane + kWave * e];
+    }
+  };
+  load_o(0);
+  // every load above is issued before anything waits for one of them
+  __builtin_amdgcn_sched_barrier(0);
+  // bitwise, so that no branch separates the loads from their use
+  const bool real = (gate != 0) & ((r == 0) | (j < min(max(lw, 0), D)));
+  // prefix splits
   const int nsp = min(nsplit, (n_b + chunk - 1) / chunk);
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s)
-    M = fmaxf(M, ws_m[((static_cast<size_t>(s) * B + b) * R + r) * Hq + hq]);
-  float L = 0.f, o[DPL];
+  const bool valid = lane < nsp;
+  const float M = wave_max(valid ? m_l : -INFINITY);
+  const float f = valid ? __builtin_amdgcn_exp2f(m_l - M) : 0.f;
+  float L = wave_sum(valid ? f * l_l : 0.f), o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const size_t po = ((static_cast<size_t>(s) * B + b) * R + r) * Hq + hq;
-    const float f = __builtin_amdgcn_exp2f(ws_m[po] - M);
-    L += f * ws_l[po];
+  auto fold_o = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] += f * ws_o[po * d + lane + kWave * e];
-  }
-  if (r > 0) {
-    // own-candidate triangle: keys (w, 0..j)
-    const int w = (r - 1) / D, j = (r - 1) - w * D;
-    const int kv = hq / (Hq / Hkv);
-    float qv[DPL];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u;
+      const float fs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(s, kWave - 1)));
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qv[e] = load_f32(q, item * d + lane + kWave * e);
-    for (int jj = 0; jj <= j; ++jj) {
-      const size_t kvo = ((static_cast<size_t>(b) * W * D + w * D + jj) * Hkv + kv) * d;
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) part += qv[e] * load_f32(k_cand, kvo + lane + kWave * e);
-      const float sc = wave_sum(part) * scale_log2;
-      const float m_new = fmaxf(M, sc);
-      const float a = exp2f(M - m_new), p = exp2f(sc - m_new);
-      L = L * a + p;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + p * load_f32(v_cand, kvo + lane + kWave * e);
-      M = m_new;
+      for (int e = 0; e < DPL; ++e) o[e] += s < nsp ? fs * ov[u][e] : 0.f;
     }
+  };
+  fold_o(0);
+  for (int s0 = kMergeBatch; s0 < nsp; s0 += kMergeBatch) {
+    load_o(s0);
+    fold_o(s0);
+  }
+  // own-candidate triangle
+  const float sc = lane <= j ? ((acc.x + acc.y) + (acc.z + acc.w)) * scale_log2 : -INFINITY;
+  const float m_new = fmaxf(M, wave_max(sc));
+  const float a = exp2f(M - m_new), p = exp2f(sc - m_new);
+  L = L * a + wave_sum(p);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] *= a;
+  auto fold_v = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int jj = j0 + u;
+      const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), min(jj, kWave - 1)));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] += jj <= j ? pt * vv[u][e] : 0.f;
+    }
+  };
+  fold_v(0);
+  for (int j0 = kMergeBatch; j0 <= j; j0 += kMergeBatch) {
+    load_v(j0);
+    fold_v(j0);
   }
   const float inv = 1.f / L;
+  float* op = out + static_cast<size_t>(item) * d;  // out[b][r][hq*d + ...]
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) store_f32(op, lane + kWave * e, o[e] * inv);
+  for (int e = 0; e < DPL; ++e) op[lane + kWave * e] = real ? o[e] * inv : 0.f;
 }
 
 // ----------------------------------------------------------------- host side
@@ -710,13 +856,14 @@ AttnPlan attn_plan(int B, int max_n, int R, int Hq, int Hkv, bool bf16) {
     p.nslots = ns + 1;  // one more slot for the candidate keys
     return p;
   }
-  p.qtiles = (R * Hq + 3) / 4;
+  p.qtiles = Hq * ((R + kF32Rows - 1) / kF32Rows);  // workgroups of 4 rows of one head
   const int units = B * p.qtiles;
-  const int min_keys = 256, target = 1024;
+  const int min_keys = 128, target = 1024;
   int ns = (target + units - 1) / units;
   int cap = max_n / min_keys;
   if (cap < 1) cap = 1;
   if (ns > cap) ns = cap;
+  if (ns > kWave) ns = kWave;  // the merge holds one split per lane
   if (ns < 1) ns = 1;
   int ch = (max_n + ns - 1) / ns;
   ch = (ch + kKB - 1) / kKB * kKB;
@@ -747,7 +894,7 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                             int D, int Hq, int Hkv, int d, bool bf16, float scale,
                             const AttnPlan& plan, void* attn_out, float* ws, hipStream_t s,
                             const LmWsView* compact) {
-  if (compact != nullptr && !bf16) return hipErrorInvalidValue;
+  if (plan.nslots > kWave) return hipErrorInvalidValue;  // the merges hold a slot per lane
   const int R = 1 + W * D;
   const size_t rows = static_cast<size_t>(plan.nslots) * B * R * Hq;
   float* ws_m = ws;
@@ -756,10 +903,10 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
   const float scale_log2 = scale * kLog2e;
   const size_t items = static_cast<size_t>(B) * R * Hq;
   const dim3 mgrid(static_cast<unsigned>((items + 3) / 4));
+  const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr, nullptr};
   if (bf16) {
     const int per_xcd = (B * Hkv + kXcds - 1) / kXcds * plan.nslots;
     const int items_x = per_xcd * plan.qtiles;
-    const LmWsView cv = compact != nullptr ? *compact : LmWsView{nullptr, nullptr, nullptr, nullptr};
     int* work = nullptr;
     int grid = kXcds * items_x;
     if (plan.persist) {
@@ -778,26 +925,27 @@ hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                        static_cast<uint16_t*>(attn_out));
   } else {
     const dim3 pgrid(plan.qtiles, B, plan.nsplit);
+    const dim3 fgrid(mgrid.x + (compact != nullptr ? 1 : 0));
     if (d == 64) {
       hipLaunchKernelGGL(attn_prefix_f32_kernel<1>, pgrid, dim3(256), 0, s,
                          static_cast<const float*>(q), static_cast<const float*>(k_pre),
                          static_cast<const float*>(v_pre), cu_len, copy_gate, cand_len, B, R, Hq,
                          Hkv, W, D, plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o);
-      hipLaunchKernelGGL((attn_merge_kernel<float, 1>), mgrid, dim3(256), 0, s,
+      hipLaunchKernelGGL(attn_merge_kernel<1>, fgrid, dim3(256), 0, s,
                          static_cast<const float*>(q), static_cast<const float*>(k_cand),
                          static_cast<const float*>(v_cand), cu_len, cand_len, copy_gate, B, R,
                          Hq, Hkv, W, D, plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o,
-                         static_cast<float*>(attn_out));
+                         static_cast<float*>(attn_out), cv);
     } else {
       hipLaunchKernelGGL(attn_prefix_f32_kernel<2>, pgrid, dim3(256), 0, s,
                          static_cast<const float*>(q), static_cast<const float*>(k_pre),
                          static_cast<const float*>(v_pre), cu_len, copy_gate, cand_len, B, R, Hq,
                          Hkv, W, D, plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o);
-      hipLaunchKernelGGL((attn_merge_kernel<float, 2>), mgrid, dim3(256), 0, s,
+      hipLaunchKernelGGL(attn_merge_kernel<2>, fgrid, dim3(256), 0, s,
                          static_cast<const float*>(q), static_cast<const float*>(k_cand),
                          static_cast<const float*>(v_cand), cu_len, cand_len, copy_gate, B, R,
                          Hq, Hkv, W, D, plan.nsplit, plan.chunk, scale_log2, ws_m, ws_l, ws_o,
-                         static_cast<float*>(attn_out));
+                         static_cast<float*>(attn_out), cv);
     }
   }
   return hipGetLastError();

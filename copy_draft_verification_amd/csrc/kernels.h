@@ -50,9 +50,9 @@ struct LmWsView {
   unsigned long long* keys;  // [rows] greedy argmax keys by global row, zeroed with the compaction
 };
 
-// With `compact` (bf16 only), one more workgroup of the prefix launch writes the
-// compact list of the B*(1+W*D) rows, as launch_compact_rows would, beside the
-// attention instead of after it.
+// With `compact`, one more workgroup of one of the attention launches (bf16: the
+// prefix sweep, fp32: the merge) writes the compact list of the B*(1+W*D) rows,
+// as launch_compact_rows would, beside the attention instead of after it.
 hipError_t launch_attention(const void* q, const void* k_pre, const void* v_pre,
                             const int32_t* cu_len, const void* k_cand, const void* v_cand,
                             const int32_t* cand_len, const uint8_t* copy_gate, int B, int W,
@@ -118,14 +118,13 @@ struct AcceptArgs {
   int32_t* next_token = nullptr;
 };
 
-// sample != nullptr: sampling partials.  Otherwise greedy: the fp32 path writes
-// (value, index) partials for launch_argmax_reduce; the bf16 path folds each row's
-// best (value, lowest index) into a 64-bit key per row (launch_argmax_finish).
+// sample != nullptr: sampling partials.  Otherwise greedy: each row's best (value,
+// lowest index) is folded into a 64-bit key per row (launch_argmax_finish).
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
                          const SampleArgs* sample = nullptr);
-// bf16 greedy: argmax_out [B][R] from the keys of launch_lmhead (-1 for rows that are
+// Greedy: argmax_out [B][R] from the keys of launch_lmhead (-1 for rows that are
 // not real), then, with `accept`, the accept of every sequence; one launch.
 hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, const AcceptArgs* accept,
                                 hipStream_t s);
@@ -135,8 +134,6 @@ hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, con
 hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
                                const uint8_t* copy_gate, hipStream_t s);
 
-hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,
-                                hipStream_t s);
 
 // Verification at T > 0: the candidate trie (before the LM head), the reduction of
 // the sampling partials into lse / residual draw per row, and the acceptance walk.

@@ -693,68 +693,98 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
 }
 
 
-// fp32: thread per vocabulary column, 32 rows per workgroup, O staged in LDS.
+// fp32: thread per vocabulary column, 32 rows per workgroup.  Per 64-wide slice of
+// the contraction, each thread loads its column's 64 weights as sixteen 16-byte
+// loads in flight together and the workgroup loads the slice of its 32 rows of O;
+// both go to LDS, the weights transposed so that a thread's piece c sits beside its
+// neighbours'.  The contraction loop reads one weight piece per step and the rows as
+// broadcasts; it is kept rolled (the code runs once per workgroup, and a fully
+// unrolled body costs more in instruction fetches than it saves).  The logits then
+// pass through LDS so that each wave scans eight rows with lanes on consecutive
+// columns; the argmax folds into the per-row keys as in the bf16 kernel (workgroup
+// best, then a device-wide 64-bit atomic max).
 constexpr int kLmF32Rows = 32;
 constexpr int kLmF32VT = 256;  // vocabulary per workgroup (one column per thread)
+constexpr int kLmF32KC = 64;   // contraction slice
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     const float* __restrict__ O, const float* __restrict__ Wt, int K, int V,
     const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
-    float* __restrict__ logits_out, int2* __restrict__ part, int vtiles) {
-  __shared__ float o_lds[kLmF32Rows][64];
-  __shared__ float red_v[4][kLmF32Rows];
-  __shared__ int red_i[4][kLmF32Rows];
+    float* __restrict__ logits_out, unsigned long long* __restrict__ keys) {
+  constexpr int kC = kLmF32KC / 4;                        // 16-byte pieces per slice row
+  constexpr int kStage = kLmF32Rows * kC / 256;           // O pieces per thread and slice (2)
+  static_assert(kC * kLmF32VT * 16 >= kLmF32Rows * kLmF32VT * 4, "logits fit the weight stage");
+  __shared__ float4 s_w[kC][kLmF32VT];                    // weights; later the tile's logits
+  __shared__ float4 o_lds[kLmF32Rows][kC];
   const int mc = blockIdx.x, vt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int row0 = mc * kLmF32Rows;
   const int rows = *n_rows;  // compact rows; O row of compact row i is row_list[i]
   if (row0 >= rows) return;
   const int v = vt * kLmF32VT + tid;
-  const float* wr = Wt + static_cast<size_t>(v < V ? v : V - 1) * K;
+  const float4* wr = reinterpret_cast<const float4*>(Wt + static_cast<size_t>(v < V ? v : V - 1) * K);
+  // staged O rows: compact rows past the end repeat the last one (their sums are
+  // never used)
+  const float4* orow[kStage];
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int e = tid + 256 * u, row = row0 + e / kC;
+    orow[u] = reinterpret_cast<const float4*>(O + static_cast<size_t>(row_list[row < rows ? row : rows - 1]) * K) + e % kC;
+  }
   float acc[kLmF32Rows];
 #pragma unroll
   for (int i = 0; i < kLmF32Rows; ++i) acc[i] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    const int kc = min(64, K - k0);
-    __syncthreads();
-    for (int e = tid; e < kLmF32Rows * 64; e += 256) {
-      const int rr = e / 64, kk = e % 64;
-      const int row = row0 + rr;
-      o_lds[rr][kk] = (row < rows && kk < kc) ? O[static_cast<size_t>(row_list[row]) * K + k0 + kk] : 0.f;
+  for (int k0 = 0; k0 < K; k0 += kLmF32KC) {
+    if (k0 > 0) __syncthreads();  // the previous slice has been read
+    float4 w4[kC], ox[kStage];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) w4[c] = wr[k0 / 4 + c];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) ox[u] = orow[u][k0 / 4];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) s_w[c][tid] = w4[c];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int e = tid + 256 * u;
+      o_lds[e / kC][e % kC] = ox[u];
     }
     __syncthreads();
-    for (int kk = 0; kk < kc; ++kk) {
-      const float wv = wr[k0 + kk];
+#pragma unroll 1
+    for (int c = 0; c < kC; ++c) {
+      const float4 w = s_w[c][tid];
 #pragma unroll
-      for (int i = 0; i < kLmF32Rows; ++i) acc[i] += o_lds[i][kk] * wv;
+      for (int i = 0; i < kLmF32Rows; ++i) {
+        const float4 o = o_lds[i][c];
+        acc[i] += o.x * w.x + o.y * w.y + o.z * w.z + o.w * w.w;
+      }
     }
   }
+  __syncthreads();
+  float* s_l = reinterpret_cast<float*>(&s_w[0][0]);  // [row][column]
 #pragma unroll
-  for (int i = 0; i < kLmF32Rows; ++i) {
-    const int row = row0 + i;
-    if (logits_out && v < V && row < rows) logits_out[static_cast<size_t>(row_list[row]) * V + v] = acc[i];
-    float bv = v < V ? acc[i] : -INFINITY;
-    int bi = v < V ? v : INT_MAX;
+  for (int i = 0; i < kLmF32Rows; ++i) s_l[i * kLmF32VT + tid] = acc[i];
+  __syncthreads();
+  for (int i = wave; i < kLmF32Rows && row0 + i < rows; i += 4) {
+    const int grow = row_list[row0 + i];
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < kLmF32VT / kWave; ++u) {
+      const int col = lane + kWave * u, vc = vt * kLmF32VT + col;
+      const float x = s_l[i * kLmF32VT + col];
+      if (logits_out && vc < V) logits_out[static_cast<size_t>(grow) * V + vc] = x;
+      // NaN logits and columns past V take no part; columns rise with u, so only a
+      // larger value replaces the best
+      if (vc < V && x > bv) { bv = x; bi = vc; }
+      if (vc < V && bi == INT_MAX && x == -INFINITY) bi = vc;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, kWave);
       const int oi = __shfl_xor(bi, o, kWave);
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
-    if (lane == 0) {
-      red_v[wave][i] = bv;
-      red_i[wave][i] = bi;
-    }
-  }
-  __syncthreads();
-  if (tid < kLmF32Rows) {
-    const int row = row0 + tid;
-    if (row < rows) {
-      float bv = red_v[0][tid];
-      int bi = red_i[0][tid];
-      for (int w = 1; w < 4; ++w)
-        if (better(red_v[w][tid], red_i[w][tid], bv, bi)) { bv = red_v[w][tid]; bi = red_i[w][tid]; }
-      part[static_cast<size_t>(row) * vtiles + vt] = make_int2(__float_as_int(bv), bi);
-    }
+    if (lane == 0)
+      __hip_atomic_fetch_max(keys + grow, argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -801,46 +831,6 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(
   __shared__ int s_wave[kCompactThreads / kWave];
   compact_rows_body<kCompactThreads>(rows, R, W, D, cand_len, copy_gate, row_list, inv, n_rows, s_wave,
                                      keys);
-}
-
-// One wave per row: the row's tile partials are contiguous ([row][vtile]), each
-// lane scans every 64th of them, then a wave-wide (value desc, index asc) reduction.
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(
-    const int2* __restrict__ part, int vtiles, int rows, const int32_t* __restrict__ inv,
-    int32_t* __restrict__ argmax_out) {
-  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (row >= rows) return;
-  const int ci = inv[row];  // compact index, -1 for rows that are not real
-  if (ci < 0) {
-    if (lane == 0) argmax_out[row] = -1;
-    return;
-  }
-  float bv = -INFINITY;
-  int bi = INT_MAX;
-  const int2* pr = part + static_cast<size_t>(ci) * vtiles;
-  // eight partials in flight per lane (512 per wave per round)
-  for (int t0 = 0; t0 < vtiles; t0 += 8 * kWave) {
-    int2 p[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = t0 + u * kWave + lane;
-      p[u] = t < vtiles ? pr[t] : make_int2(__float_as_int(-INFINITY), INT_MAX);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float v = __int_as_float(p[u].x);
-      if (better(v, p[u].y, bv, bi)) { bv = v; bi = p[u].y; }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, kWave);
-    const int oi = __shfl_xor(bi, o, kWave);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  // no value (every logit NaN): -1, as the bf16 path reports it
-  if (lane == 0) argmax_out[row] = bi == INT_MAX ? -1 : bi;
 }
 
 // One wave per sequence: the argmax of each of its R rows from the row's key (the
@@ -1034,7 +1024,7 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
                        static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), hid,
-                       V, w.row_list, w.n_rows, logits_out, w.part, plan.vtiles);
+                       V, w.row_list, w.n_rows, logits_out, w.keys);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   return e;
@@ -1055,14 +1045,6 @@ hipError_t launch_pack_weight(const void* w, const void* w2, int N, int K, void*
   hipLaunchKernelGGL(pack_weight_kernel, dim3(blocks), dim3(256), 0, s,
                      static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(w2), N, K,
                      static_cast<uint16_t*>(packed), n_chunks);
-  return hipGetLastError();
-}
-
-hipError_t launch_argmax_reduce(void* ws, const LmPlan& plan, int rows, int32_t* argmax_out,
-                                hipStream_t s) {
-  const LmWs w = lm_ws(ws, rows);
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, w.part,
-                     plan.vtiles, rows, w.inv, argmax_out);
   return hipGetLastError();
 }
 

@@ -212,10 +212,12 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  *   its contents on entry do not matter.
  * lm_begin, lm_end: optional events (may be NULL) recorded on `stream`
  *   immediately before and after the LM-head contraction kernel, for timing.
+ * q, k_pre, v_pre, k_cand, v_cand, lm_head and attn_out must be 16-byte aligned.
  * Errors: INVALID_ARG (nulls, sizes < 1, Hq % Hkv != 0, scale not finite > 0,
- *   W/D above limits), UNSUPPORTED (bf16 with d != 128 or Hq*d % 256 != 0, or
+ *   W/D above limits, misaligned pointers), UNSUPPORTED (bf16 with d != 128 or Hq*d % 256 != 0, or
  *   beyond the bf16 kernels' 32-bit byte offsets: (max_n + 64)*Hkv*d*2 or
- *   B*R*Hq*d*2 not below 0x7ffffff0; fp32 with d not in {64, 128}), WORKSPACE.
+ *   B*R*Hq*d*2 not below 0x7ffffff0; fp32 with d not in {64, 128}; B*R*Hq not
+ *   below 2^31), WORKSPACE.
  */
 ssd_status_t ssd_blocktri_verify(const void* q, const void* k_pre, const void* v_pre,
                                  const int32_t* cu_len, int32_t max_n, const void* k_cand,

@@ -49,7 +49,8 @@ def test_small_bf16_chain(variant):
         assert st["margin_excluded"] <= 0.1 * st["argmax_rows"]
 
 
-@pytest.mark.parametrize("variant", [{}, {"lm_std": 1.0}, {"q_scale": 4.0, "Hq": 4, "Hkv": 2, "hid": 256}])
+@pytest.mark.parametrize("variant", [{}, {"lm_std": 1.0}, {"q_scale": 4.0, "Hq": 4, "Hkv": 2, "hid": 256},
+                                     {"d": 128, "hid": 256, "lm_std": 1.0}])  # d = 128: two elements per lane
 def test_small_fp32_chain(variant):
     _chain(generate("small_f32", **variant))
 

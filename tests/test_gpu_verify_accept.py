@@ -12,6 +12,9 @@ Bars:
 * exact ties: two vocabulary rows with identical weights give identical logits;
   where they hold a row's maximum, the argmax is the lower of the two indices,
   whether they sit in one workgroup's tile or in two.
+* NaN logits never win: with the weights of the most frequent winners set to NaN,
+  the argmax is the oracle's over the remaining columns; with every weight NaN,
+  every row reports -1 and nothing is accepted.
 Every test prints its case before touching the GPU."""
 import numpy as np
 import pytest
@@ -19,7 +22,7 @@ import torch
 
 import copy_draft_verification_amd as cdv
 import oracle
-from parity_lib import DEV, Dev, check_verify, host
+from parity_lib import ARGMAX_MARGIN, DEV, Dev, check_verify, host, widen_out
 from workloads import f32_to_bf16_bits, generate
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +148,66 @@ def test_argmax_exact_ties_take_the_lower_index(pairs):
             assert am[b, r] == int(np.argmax(row))
     print(f"[ok] rows won by a duplicated pair: {hits}", flush=True)
     assert hits > 0
+
+
+def _nan_rows(lm, rows):
+    if lm.dtype == np.uint16:
+        lm[rows] = np.uint16(0x7FC0)       # bf16 quiet NaN
+    else:
+        lm[rows] = np.float32(np.nan)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_f32", "small_bf16"])
+def test_nan_logits_never_win(name):
+    wl = generate(name, lm_std=1.0)
+    s = wl.spec
+    print(f"[case] NaN vocabulary rows, {name}", flush=True)
+    # the winners without NaN, from a first pass
+    d = Dev(wl)
+    g = _retrieve(wl, d)
+    _, m0 = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    torch.cuda.synchronize()
+    won = host(m0)[host(m0) >= 0]
+    top, counts = np.unique(won, return_counts=True)
+    hit = top[np.argsort(-counts)][:4].tolist()
+    _nan_rows(wl.lm_head, hit + [s.V - 1])
+    d = Dev(wl)
+    attn, m, acc = cdv.blocktri_verify_accept(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc,
+                                              g["cand"], g["cand_len"], g["copy_gate"], d.lm,
+                                              s.W, s.D, wl.scale)
+    torch.cuda.synchronize()
+    am = host(m)
+    O = widen_out(attn).reshape(s.B, wl.R, s.Hq * s.d)
+    real = am >= 0
+    assert real.sum() == (host(m0) >= 0).sum()
+    L = oracle.lm_logits(O[real], wl.lm_head)
+    assert np.all(np.isnan(L[:, hit]))
+    L[np.isnan(L)] = -np.inf
+    pred, _, margin = oracle.argmax_with_margin(L)
+    ok = margin >= ARGMAX_MARGIN
+    assert np.array_equal(am[real][ok], pred[ok])
+    assert not np.isin(am[real], hit).any()
+    o = oracle.accept_longest(host(g["cand"]), host(g["cand_len"]), host(g["copy_gate"]).astype(bool),
+                              am, s.W, s.D)
+    for k in ("accept_len", "best_w", "best_len", "next_token"):
+        assert np.array_equal(host(acc[k]), o[k]), k
+    print(f"[ok] NaN rows {hit}; rows checked {int(ok.sum())} of {int(real.sum())}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16"])
+def test_all_nan_logits_give_minus_one(name):
+    wl = generate(name)
+    s = wl.spec
+    print(f"[case] every vocabulary row NaN, {name}", flush=True)
+    _nan_rows(wl.lm_head, slice(None))
+    d = Dev(wl)
+    g = _retrieve(wl, d)
+    _, m, acc = cdv.blocktri_verify_accept(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand"],
+                                           g["cand_len"], g["copy_gate"], d.lm, s.W, s.D, wl.scale)
+    torch.cuda.synchronize()
+    assert np.all(host(m) == -1)
+    o = oracle.accept_longest(host(g["cand"]), host(g["cand_len"]), host(g["copy_gate"]).astype(bool),
+                              host(m), s.W, s.D)
+    for k in ("accept_len", "best_w", "best_len", "next_token"):
+        assert np.array_equal(host(acc[k]), o[k]), k
