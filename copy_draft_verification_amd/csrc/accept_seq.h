@@ -18,39 +18,65 @@ namespace ssd {
 // the accepted prefix is an LDS read rather than another global load.
 constexpr int kAcGroup = 16;
 
-// Sequence b, by the calling wavefront (lane = its lane).  am: the argmax of
-// sequence b's 1 + W*D rows (global memory or LDS); s_pred: this wave's
-// SSD_MAX_W x 64 ints of LDS.
-__device__ __forceinline__ void accept_seq(
-    int b, int lane, const int32_t* __restrict__ cand, const int32_t* __restrict__ cand_len,
-    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ am, int W, int D,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ best_w, int32_t* __restrict__ best_len,
-    int32_t* __restrict__ next_token, int (*s_pred)[kWave]) {
-  // the gate, every candidate length (lane w) and the first group's tokens and
-  // predictions are all requested before any of them is used (the arrays are
-  // fixed-size, so the reads are in bounds whatever the gate says)
-  const int gate = copy_gate[b];
+// What the accept reads before it needs the argmax: the gate, the candidate
+// lengths (lane w) and the first group's candidate tokens.  Issued on its own, it
+// lets a caller overlap these loads with the loads of the argmax itself.
+struct AcceptPre {
+  int gate, len_lane;
+  int c[kAcGroup];
+};
+
+// Candidate token j (= lane) of candidates w0 .. w0+15 of sequence b, -1 past W or D.
+// Unconditional loads from clamped (in-bounds) indices, then selects: predicated
+// loads would become branches, each ending in a wait for every load before it.
+__device__ __forceinline__ void accept_load_cand(const int32_t* __restrict__ cand, int b, int lane,
+                                                 int W, int D, int w0, int (&c)[kAcGroup]) {
+  const int32_t* cb = cand + static_cast<size_t>(b) * W * D;
+#pragma unroll
+  for (int u = 0; u < kAcGroup; ++u) {
+    const int w = w0 + u;
+    const bool cv = w < W && lane < D;
+    const int cx = cb[cv ? w * D + lane : 0];
+    c[u] = cv ? cx : -1;
+  }
+}
+
+__device__ __forceinline__ AcceptPre accept_prefetch(int b, int lane, const int32_t* __restrict__ cand,
+                                                     const int32_t* __restrict__ cand_len,
+                                                     const uint8_t* __restrict__ copy_gate, int W, int D) {
+  // the arrays are fixed-size, so the reads are in bounds whatever the gate says
+  AcceptPre pre;
+  pre.gate = copy_gate[b];
   const int len_raw = cand_len[static_cast<size_t>(b) * W + (lane < W ? lane : 0)];
-  const int len_lane = lane < W ? len_raw : 0;
+  pre.len_lane = lane < W ? len_raw : 0;
+  accept_load_cand(cand, b, lane, W, D, 0, pre.c);
+  return pre;
+}
+
+// Sequence b, by the calling wavefront (lane = its lane), from its prefetched
+// inputs.  am: the argmax of sequence b's 1 + W*D rows (global memory or LDS);
+// s_pred: this wave's SSD_MAX_W x 64 ints of LDS.
+__device__ __forceinline__ void accept_run(
+    const AcceptPre& pre, int b, int lane, const int32_t* __restrict__ cand,
+    const int32_t* __restrict__ am, int W, int D, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ best_w, int32_t* __restrict__ best_len, int32_t* __restrict__ next_token,
+    int (*s_pred)[kWave]) {
   int c[kAcGroup], pv[kAcGroup];
-  // Unconditional loads from clamped (in-bounds) indices, then selects: predicated
-  // loads would become branches, each ending in a wait for every load before it.
-  auto load_group = [&](int w0) {
-    const int32_t* cb = cand + static_cast<size_t>(b) * W * D;
+#pragma unroll
+  for (int u = 0; u < kAcGroup; ++u) c[u] = pre.c[u];
+  // pred(w, lane-1): the anchor's argmax for lane 0, else row (w, lane-1)
+  auto load_pred = [&](int w0) {
 #pragma unroll
     for (int u = 0; u < kAcGroup; ++u) {
       const int w = w0 + u;
-      const bool cv = w < W && lane < D, pvv = w < W && lane <= D;
-      // pred(w, lane-1): the anchor's argmax for lane 0, else row (w, lane-1)
+      const bool pvv = w < W && lane <= D;
       const int pi = (pvv && lane > 0) ? 1 + w * D + lane - 1 : 0;
-      const int cx = cb[cv ? w * D + lane : 0];
       const int px = am[pi];
-      c[u] = cv ? cx : -1;
       pv[u] = pvv ? px : -1;
     }
   };
-  load_group(0);
-  if (gate == 0) {
+  load_pred(0);
+  if (pre.gate == 0) {
     for (int w = lane; w < W; w += kWave) accept_len[static_cast<size_t>(b) * W + w] = 0;
     if (lane == 0) {
       best_w[b] = -1;
@@ -61,12 +87,15 @@ __device__ __forceinline__ void accept_seq(
   }
   int my_a = 0;
   for (int w0 = 0; w0 < W; w0 += kAcGroup) {
-    if (w0 > 0) load_group(w0);
+    if (w0 > 0) {
+      accept_load_cand(cand, b, lane, W, D, w0, c);
+      load_pred(w0);
+    }
 #pragma unroll
     for (int u = 0; u < kAcGroup; ++u) {
       const int w = w0 + u;
       if (w >= W) break;
-      int L = __shfl(len_lane, w, kWave);
+      int L = __shfl(pre.len_lane, w, kWave);
       L = L < 0 ? 0 : (L > D ? D : L);
       const bool ok = lane < L && c[u] == pv[u];
       const unsigned long long m = __ballot(ok);
@@ -90,6 +119,15 @@ __device__ __forceinline__ void accept_seq(
     // pred(bi, bv-1) sits in lane bv of row bi (lanes 0..min(D, 63) were filled)
     next_token[b] = bv < kWave ? s_pred[bi][bv] : am[1 + bi * D + bv - 1];
   }
+}
+
+__device__ __forceinline__ void accept_seq(
+    int b, int lane, const int32_t* __restrict__ cand, const int32_t* __restrict__ cand_len,
+    const uint8_t* __restrict__ copy_gate, const int32_t* __restrict__ am, int W, int D,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ best_w, int32_t* __restrict__ best_len,
+    int32_t* __restrict__ next_token, int (*s_pred)[kWave]) {
+  const AcceptPre pre = accept_prefetch(b, lane, cand, cand_len, copy_gate, W, D);
+  accept_run(pre, b, lane, cand, am, W, D, accept_len, best_w, best_len, next_token, s_pred);
 }
 
 }  // namespace ssd

@@ -35,13 +35,15 @@ namespace ssd {
 // assignment does not change the contraction.
 //
 // Memory pipeline (one iteration = 64 k):
-//  * weights: straight from HBM into registers (the A operand), three iterations
-//    ahead, in four register slots;
-//  * rows: copied from global memory into LDS by buffer-to-LDS loads, also three
-//    iterations ahead, into four LDS stages.
-// Both streams run the same distance ahead because a wave's loads complete in
-// issue order: a short-latency row load issued after a weight load cannot be
-// consumed before that weight load has landed.
+//  * weights: straight from HBM into registers (the A operand), in four register
+//    slots;
+//  * rows: copied from global memory into LDS by buffer-to-LDS loads, into four
+//    LDS stages.
+// With several row chunks both streams run three iterations ahead, the same
+// distance, because a wave's loads complete in issue order: a short-latency row
+// load issued after a weight load cannot be consumed before that weight load has
+// landed.  With one row chunk (kPairSync below) they are issued two iterations at
+// a time, the weights one step before the rows.
 constexpr int kLmWaves = 4;
 constexpr int kLmVA = 2;                          // A tiles (32 vocabulary) per wave
 constexpr int kLmVT = kLmWaves * kLmVA * 32;      // vocabulary per workgroup (256)
@@ -563,24 +565,31 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   constexpr bool kInterleave = kEpi == kEpiArgmax || kEpi == kEpiPair || kEpi == kEpiPartialHalf;
   constexpr int kIssueAt = kEpi == kEpiPartialHalf ? 10 : kLmIssueAt;
   // kPairSync: one barrier per two iterations.  At the start of an even iteration
-  // each wave waits for all of its loads (iterations it and it+1), one barrier
-  // makes every wave's rows of both visible and frees the stages of it-2 and it-1,
-  // and the loads of it+2 and it+3 go out from inside iteration it's MFMAs, two
-  // after each MFMA pair; odd iterations have neither wait nor barrier.  The loads
-  // then run two iterations ahead instead of three.  In the greedy launch with one
-  // row chunk (batch 1) that is 8% faster (244 against 266 us at 201 rows, same
-  // box); with several chunks (batch 32: 6.27 against 5.78 ms) it is 8% slower, so
-  // those keep a barrier per iteration.
+  // each wave waits for all of its loads (iterations it and it+1), and one barrier
+  // makes every wave's rows of both visible and frees the stages of it-2 and it-1;
+  // odd iterations have neither wait nor barrier.  The loads of it+2 and it+3 go
+  // out from inside the MFMA streams of it and it+1, the weights of both in the
+  // even iteration (they come from HBM and need the longer lead) and the rows of
+  // both, into the stages the barrier freed, in the odd one; each set is spread
+  // evenly over the step's 28 MFMA pairs.  In the greedy launch with one row chunk
+  // (batch 1) the barrier per two iterations is 8% faster than one per iteration
+  // (244 against 266 us at 201 rows, same box); with several chunks (batch 32:
+  // 6.27 against 5.78 ms) it is 8% slower, so those keep a barrier per iteration.
+  // Issuing all four sets in the even iteration, two loads after each MFMA pair
+  // from pair 2, was 7-8% slower at batch 1 (205 against 189 us, same box): the
+  // vector memory path took the burst at the cost of the MFMA issue.
   constexpr bool kPairSync = kEpi == kEpiArgmax && kOnce;
-  constexpr int kPairIssueAt = 2;
   // compute: iteration `it` on `w` and `stage`; issue_next() issues kNL loads,
-  // placed among the MFMAs from pair kAt on (kNL = 0: issue_next is not called).
+  // placed among the MFMAs from pair kAt on (kNL = 0: issue_next is not called):
+  // with kSpread evenly over the remaining pairs, else kPer after each pair.
   auto compute = [&](auto NL_c, const uint4 (&w)[kVA][4], const uint16_t* stage, auto&& issue_next) {
     constexpr int kNL = decltype(NL_c)::value;
+    constexpr bool kSpread = kPairSync;
     constexpr int kPer = kNL > kLoadsPerIter ? 2 : 1;               // loads per MFMA pair
-    constexpr int kAt = kNL > kLoadsPerIter ? kPairIssueAt : kIssueAt;
+    constexpr int kAt = kSpread ? 0 : kIssueAt;
     constexpr int NB = 4 * kLmNT;
-    static_assert(kAt + (kNL + kPer - 1) / kPer <= NB, "the loads fit between the MFMA pairs");
+    static_assert(kSpread ? kNL <= NB : kAt + (kNL + kPer - 1) / kPer <= NB,
+                  "the loads fit between the MFMA pairs");
     const uint16_t* ob = stage + l32 * kLmKS;
     const int sw = (l32 >> 1) & 7;
     auto frag = [&](int j) {
@@ -606,7 +615,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     for (int i = 0; i < NB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, kVA, 0);      // MFMAs
       if (i + kLmBAhead < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kNL > 0 && i >= kAt && (i - kAt) * kPer < kNL) {        // global loads
+      if constexpr (kSpread) {                                    // global loads
+        const int cnt = i >= kAt ? ((i + 1 - kAt) * kNL) / (NB - kAt) - ((i - kAt) * kNL) / (NB - kAt) : 0;
+        if (cnt == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      } else if (kNL > 0 && i >= kAt && (i - kAt) * kPer < kNL) {
         if (kPer == 2 && kNL - (i - kAt) * kPer >= 2)
           __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         else
@@ -627,15 +639,18 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       if constexpr (U % 2 == 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
-        // iterations it+2, it+3 go into the stages and slots of it-2, it-1
-        compute(IntC<2 * kLoadsPerIter>{}, aw[U], stages[U], [&]() {
-          load_o(stages[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
+        // the weights of iterations it+2, it+3 into the register slots of it-2, it-1
+        compute(IntC<2 * kVA * 4>{}, aw[U], stages[U], [&]() {
           load_a(aw[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
-          load_o(stages[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
           load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
         });
       } else {
-        compute(IntC<0>{}, aw[U], stages[U], [] {});
+        // (it is odd here) the rows of it+1, it+2 into the stages of it-3, it-2, which
+        // every wave left before the last barrier
+        compute(IntC<2 * kLmBlocksPerWave>{}, aw[U], stages[U], [&]() {
+          load_o(stages[(U + 1) % kLmSlots], it + 1 < nit ? it + 1 : kPastEnd);
+          load_o(stages[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
+        });
       }
       return;
     }
@@ -708,40 +723,61 @@ constexpr int kLmF32VT = 256;  // vocabulary per workgroup (one column per threa
 constexpr int kLmF32KC = 64;   // contraction slice
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     const float* __restrict__ O, const float* __restrict__ Wt, int K, int V,
-    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows, int cap,
     float* __restrict__ logits_out, unsigned long long* __restrict__ keys) {
   constexpr int kC = kLmF32KC / 4;                        // 16-byte pieces per slice row
   constexpr int kStage = kLmF32Rows * kC / 256;           // O pieces per thread and slice (2)
   static_assert(kC * kLmF32VT * 16 >= kLmF32Rows * kLmF32VT * 4, "logits fit the weight stage");
   __shared__ float4 s_w[kC][kLmF32VT];                    // weights; later the tile's logits
   __shared__ float4 o_lds[kLmF32Rows][kC];
+  __shared__ int s_grow[kLmF32Rows];                      // the chunk's attention rows
   const int mc = blockIdx.x, vt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int row0 = mc * kLmF32Rows;
-  const int rows = *n_rows;  // compact rows; O row of compact row i is row_list[i]
-  if (row0 >= rows) return;
   const int v = vt * kLmF32VT + tid;
   const float4* wr = reinterpret_cast<const float4*>(Wt + static_cast<size_t>(v < V ? v : V - 1) * K);
-  // staged O rows: compact rows past the end repeat the last one (their sums are
-  // never used)
+  // The first slice's weights and the staged rows' list entries are requested
+  // with the row count, not after it: entries past the count (stale, or never
+  // written) are clamped into [0, cap) and their sums are never used.
+  int grow[kStage], rows;
+  {
+    float4 w4[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) w4[c] = wr[c];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) grow[u] = row_list[min(row0 + (tid + 256 * u) / kC, cap - 1)];
+    rows = *n_rows;  // compact rows; O row of compact row i is row_list[i]
+    __builtin_amdgcn_sched_barrier(0);  // all of them in flight before the first wait
+#pragma unroll
+    for (int c = 0; c < kC; ++c) s_w[c][tid] = w4[c];
+    // an empty use, so that the list loads stay ahead of the exit test below
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) asm volatile("" ::"v"(grow[u]));
+  }
+  if (row0 >= rows) return;
   const float4* orow[kStage];
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
-    const int e = tid + 256 * u, row = row0 + e / kC;
-    orow[u] = reinterpret_cast<const float4*>(O + static_cast<size_t>(row_list[row < rows ? row : rows - 1]) * K) + e % kC;
+    const int e = tid + 256 * u;
+    const int g = min(max(grow[u], 0), cap - 1);
+    orow[u] = reinterpret_cast<const float4*>(O + static_cast<size_t>(g) * K) + e % kC;
+    if (e % kC == 0) s_grow[e / kC] = g;  // for the epilogue (read after its barriers)
   }
   float acc[kLmF32Rows];
 #pragma unroll
   for (int i = 0; i < kLmF32Rows; ++i) acc[i] = 0.f;
   for (int k0 = 0; k0 < K; k0 += kLmF32KC) {
-    if (k0 > 0) __syncthreads();  // the previous slice has been read
-    float4 w4[kC], ox[kStage];
+    if (k0 > 0) {
+      __syncthreads();  // the previous slice has been read
+      float4 w4[kC];
 #pragma unroll
-    for (int c = 0; c < kC; ++c) w4[c] = wr[k0 / 4 + c];
+      for (int c = 0; c < kC; ++c) w4[c] = wr[k0 / 4 + c];
+#pragma unroll
+      for (int c = 0; c < kC; ++c) s_w[c][tid] = w4[c];
+    }
+    float4 ox[kStage];
 #pragma unroll
     for (int u = 0; u < kStage; ++u) ox[u] = orow[u][k0 / 4];
-#pragma unroll
-    for (int c = 0; c < kC; ++c) s_w[c][tid] = w4[c];
 #pragma unroll
     for (int u = 0; u < kStage; ++u) {
       const int e = tid + 256 * u;
@@ -764,7 +800,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
   for (int i = 0; i < kLmF32Rows; ++i) s_l[i * kLmF32VT + tid] = acc[i];
   __syncthreads();
   for (int i = wave; i < kLmF32Rows && row0 + i < rows; i += 4) {
-    const int grow = row_list[row0 + i];
+    const int grow = s_grow[i];
     float bv = -INFINITY;
     int bi = INT_MAX;
 #pragma unroll
@@ -844,29 +880,43 @@ __global__ __launch_bounds__(kWave) void argmax_finish_kernel(
   __shared__ int s_am[1 + SSD_MAX_W * SSD_MAX_D];
   __shared__ int s_pred[SSD_MAX_W][kWave];
   const int b = blockIdx.x, lane = threadIdx.x;
-  const unsigned long long* kb = keys + static_cast<size_t>(b) * R;
+  // Only the low halves are read: a key's low half is the complemented index, and
+  // the key 0 (no value) has low half 0, whose complement is the -1 reported then.
+  const uint32_t* kb = reinterpret_cast<const uint32_t*>(keys + static_cast<size_t>(b) * R);
   int32_t* ob = argmax_out + static_cast<size_t>(b) * R;
   constexpr int kU = 8;  // keys in flight per lane
-  for (int r0 = 0; r0 < R; r0 += kU * kWave) {
-    unsigned long long k[kU];
+  uint32_t k[kU];
+  auto load_keys = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = r0 + u * kWave + lane;
-      k[u] = r < R ? kb[r] : 0ull;
+      k[u] = kb[2 * static_cast<size_t>(r < R ? r : R - 1)];
     }
+  };
+  load_keys(0);
+  // the accept's own inputs are requested with the first keys (one wait for both)
+  AcceptPre pre{};
+  if (acc.cand != nullptr) {
+    pre = accept_prefetch(b, lane, acc.cand, acc.cand_len, acc.copy_gate, acc.W, acc.D);
+    asm volatile("" ::"v"(pre.gate), "v"(pre.len_lane));
+#pragma unroll
+    for (int u = 0; u < kAcGroup; ++u) asm volatile("" ::"v"(pre.c[u]));
+  }
+  for (int r0 = 0; r0 < R; r0 += kU * kWave) {
+    if (r0 > 0) load_keys(r0);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = r0 + u * kWave + lane;
       if (r >= R) break;
-      const int v = k[u] == 0ull ? -1 : static_cast<int>(~static_cast<uint32_t>(k[u]));
+      const int v = static_cast<int>(~k[u]);
       ob[r] = v;
       s_am[r] = v;
     }
   }
   if (acc.cand == nullptr) return;
   __syncthreads();
-  accept_seq(b, lane, acc.cand, acc.cand_len, acc.copy_gate, s_am, acc.W, acc.D, acc.accept_len,
-             acc.best_w, acc.best_len, acc.next_token, s_pred);
+  accept_run(pre, b, lane, acc.cand, s_am, acc.W, acc.D, acc.accept_len, acc.best_w, acc.best_len,
+             acc.next_token, s_pred);
 }
 
 // One wave per row: merges the row's per-tile (max, sum-exp, best score, best
@@ -1024,7 +1074,7 @@ hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, in
   else
     hipLaunchKernelGGL(lmhead_f32_kernel, dim3(plan.mchunks, plan.vtiles), dim3(256), 0, s,
                        static_cast<const float*>(attn_out), static_cast<const float*>(lm_head), hid,
-                       V, w.row_list, w.n_rows, logits_out, w.keys);
+                       V, w.row_list, w.n_rows, rows, logits_out, w.keys);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end && hipEventRecord(ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   return e;

@@ -66,7 +66,8 @@ def test_bf16_chain_other_candidate_shapes(W, D):
 def test_bf16_chain_many_key_splits():
     # one sequence whose rows fit one tile of one KV head: the 12000-token context is
     # cut into 23 key splits, 21 of which hold keys; the merge combines 21 prefix
-    # partials and the candidate slot, which comes last
+    # partials and the candidate slot, which comes last (24 slots: the merge's first
+    # round of eight slot outputs and two more rounds)
     st = _chain(generate("small_bf16", B=1, n=(12000, 12000), W=1, D=20, lm_std=1.0, q_scale=4.0))
     assert st["att_rows"] > 0
 
@@ -318,7 +319,7 @@ def test_max_n_only_sizes_the_launch():
     outs = []
     # 32 * max_n gives 22 key splits, most of them past every context: the merge skips
     # the slots past each context (it counts the splits from n_b) and still reads the
-    # candidate slot, the last one
+    # candidate slot, the last one, in its third round of eight slot outputs
     for mn in (wl.max_n, 64, 4 * wl.max_n, 32 * wl.max_n):
         a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, mn, d.kc, d.vc, g["cand_len"],
                                    g["copy_gate"], d.lm, s.W, s.D, wl.scale)
