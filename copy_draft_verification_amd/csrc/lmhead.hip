@@ -42,8 +42,8 @@ namespace ssd {
 // With several row chunks both streams run three iterations ahead, the same
 // distance, because a wave's loads complete in issue order: a short-latency row
 // load issued after a weight load cannot be consumed before that weight load has
-// landed.  With one row chunk (kPairSync below) they are issued two iterations at
-// a time, the weights one step before the rows.
+// landed.  With one row chunk (kPairSync below) the weights run three iterations
+// ahead and the rows two.
 constexpr int kLmWaves = 4;
 constexpr int kLmVA = 2;                          // A tiles (32 vocabulary) per wave
 constexpr int kLmVT = kLmWaves * kLmVA * 32;      // vocabulary per workgroup (256)
@@ -565,19 +565,20 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   constexpr bool kInterleave = kEpi == kEpiArgmax || kEpi == kEpiPair || kEpi == kEpiPartialHalf;
   constexpr int kIssueAt = kEpi == kEpiPartialHalf ? 10 : kLmIssueAt;
   // kPairSync: one barrier per two iterations.  At the start of an even iteration
-  // each wave waits for all of its loads (iterations it and it+1), and one barrier
-  // makes every wave's rows of both visible and frees the stages of it-2 and it-1;
-  // odd iterations have neither wait nor barrier.  The loads of it+2 and it+3 go
-  // out from inside the MFMA streams of it and it+1, the weights of both in the
-  // even iteration (they come from HBM and need the longer lead) and the rows of
-  // both, into the stages the barrier freed, in the odd one; each set is spread
-  // evenly over the step's 28 MFMA pairs.  In the greedy launch with one row chunk
-  // (batch 1) the barrier per two iterations is 8% faster than one per iteration
-  // (244 against 266 us at 201 rows, same box); with several chunks (batch 32:
-  // 6.27 against 5.78 ms) it is 8% slower, so those keep a barrier per iteration.
-  // Issuing all four sets in the even iteration, two loads after each MFMA pair
-  // from pair 2, was 7-8% slower at batch 1 (205 against 189 us, same box): the
-  // vector memory path took the burst at the cost of the MFMA issue.
+  // each wave waits for its rows and weights of iterations it and it+1, and one
+  // barrier makes every wave's rows of both visible and frees the stages of it-2
+  // and it-1; odd iterations have neither wait nor barrier.  Each step issues the
+  // rows of it+2 and the weights of it+3 (a register slot is free as soon as its
+  // own wave is done with it, a stage only after the barrier), spread evenly over
+  // the step's 28 MFMA pairs.  In the greedy launch with one row chunk (batch 1)
+  // the barrier per two iterations is 8% faster than one per iteration (244
+  // against 266 us at 201 rows, same box); with several chunks (batch 32: 6.27
+  // against 5.78 ms) it is 8% slower, so those keep a barrier per iteration.  At
+  // batch 1, same box: all loads of it+2 and it+3 in the even step, two after each
+  // MFMA pair from pair 2, 205 us (the vector memory path took the burst at the
+  // cost of MFMA issue); the weights of both in the even step and the rows of both
+  // in the odd one, each spread, 189 us; this schedule, 185 us (193 against 185 on
+  // another box).
   constexpr bool kPairSync = kEpi == kEpiArgmax && kOnce;
   // compute: iteration `it` on `w` and `stage`; issue_next() issues kNL loads,
   // placed among the MFMAs from pair kAt on (kNL = 0: issue_next is not called):
@@ -636,22 +637,20 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   auto step = [&](auto U_c, int it) {
     constexpr int U = decltype(U_c)::value;
     if constexpr (kPairSync) {
+      // Every step issues the rows of it+2, into the stage of it-2 (every wave left
+      // it before the last barrier), then the weights of it+3, into this wave's
+      // register slot of it-1.  At an even step everything up to the rows of it+1
+      // has landed once only the newest weights (those of it+2, from the odd step
+      // before) are outstanding.
+      auto issue_next = [&]() {
+        load_o(stages[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
+        load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
+      };
       if constexpr (U % 2 == 0) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVA * 4));
         lds_barrier();
-        // the weights of iterations it+2, it+3 into the register slots of it-2, it-1
-        compute(IntC<2 * kVA * 4>{}, aw[U], stages[U], [&]() {
-          load_a(aw[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
-          load_a(aw[(U + 3) % kLmSlots], it + 3 < nit ? it + 3 : kPastEnd);
-        });
-      } else {
-        // (it is odd here) the rows of it+1, it+2 into the stages of it-3, it-2, which
-        // every wave left before the last barrier
-        compute(IntC<2 * kLmBlocksPerWave>{}, aw[U], stages[U], [&]() {
-          load_o(stages[(U + 1) % kLmSlots], it + 1 < nit ? it + 1 : kPastEnd);
-          load_o(stages[(U + 2) % kLmSlots], it + 2 < nit ? it + 2 : kPastEnd);
-        });
       }
+      compute(IntC<kLoadsPerIter>{}, aw[U], stages[U], issue_next);
       return;
     }
     // s_waitcnt as a builtin, so that the compiler's own wait tracking knows it
@@ -683,8 +682,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   if constexpr (!kPairSync) {
     load_o(st2, 2);
     load_a(aw[2], 2);
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    load_a(aw[2], 2);  // the weights run three iterations ahead, the rows two
   }
+  __builtin_amdgcn_sched_barrier(0);
   for (int it0 = 0; it0 < nit; it0 += kLmSlots) {
     step(IntC<0>{}, it0);
     step(IntC<1>{}, it0 + 1);
