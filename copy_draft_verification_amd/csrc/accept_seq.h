@@ -4,8 +4,8 @@
 // For candidate w, lane j tests cand[w][j] == pred(w, j-1); a ballot turns the
 // tests into a bit mask and the run of ones from bit 0 is the accepted length a_w.
 // A wave reduction then picks the largest a_w, lowest w on ties, and the token
-// after it.  Used by the accept kernel and by the last workgroup of the greedy
-// LM-head launch when it accepts as well.
+// after it.  Used by the accept kernel and by the argmax launch that follows the
+// greedy LM head when it accepts as well.
 #pragma once
 #include "common.h"
 #include "switchsd.h"

@@ -1010,7 +1010,7 @@ struct LmWs {
   int32_t* row_list;
   int32_t* inv;
   int2* part;
-  unsigned long long* keys;  // greedy bf16: the start of the partials region
+  unsigned long long* keys;  // greedy (both dtypes): a key per row at the start of the partials region
 };
 LmWs lm_ws(void* ws, int rows) {
   char* p = static_cast<char*>(ws);
@@ -1027,8 +1027,8 @@ LmWs lm_ws(void* ws, int rows) {
 }
 }  // namespace
 
-// The tile partials take 16 bytes per (row, tile): (value, index) at T = 0,
-// (max, sum-exp, best score, best token) when sampling.
+// The partials region: 16 bytes per (row, tile) when sampling (max, sum-exp, best
+// score, best token); a greedy launch uses only its first 8 bytes per row (the keys).
 LmWsView lm_ws_view(void* ws, int rows) {
   const LmWs w = lm_ws(ws, rows);
   return LmWsView{w.n_rows, w.row_list, w.inv, w.keys};

@@ -62,7 +62,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 10
+#define SSD_ABI_VERSION 11
 
 typedef enum {
   SSD_OK = 0,
@@ -276,9 +276,9 @@ ssd_status_t ssd_accept_longest(const int32_t* cand, const int32_t* cand_len,
  * verification alone: exactly ssd_blocktri_verify (no logits output) and then
  * ssd_accept_longest on its argmax_out (paper §3.3 "Parallel Verification with
  * Block-Triangular Attention" and the longest-validated-continuation rule; write-up
- * §3.1), for callers that want the step's fixed launch cost lower.  With bf16 the
- * accept runs in the last workgroup of the LM-head launch; with fp32 it is a launch
- * of its own.  Arguments and outputs are those of the two calls: cand [B][W][D]
+ * §3.1), for callers that want the step's fixed launch cost lower.  The accept
+ * runs in the launch after the LM head that turns its per-row results into
+ * argmax_out (both dtypes).  Arguments and outputs are those of the two calls: cand [B][W][D]
  * int32 (from ssd_kgram_retrieve), accept_len [B][W], best_w, best_len,
  * next_token [B] int32; workspace of ssd_verify_workspace_bytes(...) bytes.
  * Errors: those of ssd_blocktri_verify, and INVALID_ARG for null cand or accept
