@@ -72,6 +72,7 @@ def test_workspace_query(lib):
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x1008)
 
 
 def test_pack_validation(lib):
@@ -162,6 +163,12 @@ def test_verify_validation(lib):
     assert f(*_verify_args(dtype=0, Hq=3, Hkv=1, ws_bytes=16)) == 3
     assert f(*_verify_args(ws_bytes=16)) == 3
     assert f(*_verify_args(ws=None)) == 3
+    # the kernels move q, K, V, the weights and the output in 16-byte pieces
+    for k in ("q", "k_pre", "v_pre", "k_cand", "v_cand", "lm_head", "attn_out"):
+        assert f(*_verify_args(**{k: MISALIGNED})) == 1, k
+        assert f(*_verify_args(dtype=0, d=64, **{k: MISALIGNED})) == 1, k
+    # B*R*Hq must stay below 2^31 (32-bit index math in the merges)
+    assert f(*_verify_args(dtype=0, d=64, B=2 ** 20, W=64, D=64, Hq=1, Hkv=1)) == 2
 
 
 def _verify_accept_args(**over):
@@ -183,6 +190,7 @@ def test_verify_accept_validation(lib):
     assert f(*_verify_accept_args(scale=0.0)) == 1
     assert f(*_verify_accept_args(d=64)) == 2
     assert f(*_verify_accept_args(ws_bytes=16)) == 3
+    assert f(*_verify_accept_args(k_pre=MISALIGNED)) == 1
 
 
 def test_accept_validation(lib):
@@ -294,6 +302,7 @@ def test_verify_sample_validation(lib):
     assert f(*_sample_args(d=64)) == 2
     assert f(*_sample_args()) == 3                                # workspace too small
     assert f(*_sample_args(seed=(1 << 64) - 1)) == 3              # any 64-bit seed is accepted
+    assert f(*_sample_args(v_cand=MISALIGNED)) == 1
 
 
 def test_accept_sample_validation(lib):
