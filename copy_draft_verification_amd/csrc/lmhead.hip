@@ -318,6 +318,21 @@ __device__ __forceinline__ void sample_epilogue(
 // largest value with the lowest index, the order of `better`.  0 stands for no
 // value (every value NaN or past V); no real pair maps to it, since its high half
 // would be a NaN's.
+// Maxima of MFMA results without the canonicalising maximum the compiler puts in
+// front of every fmaxf input (which doubled the epilogue's maximum tree).  In IEEE
+// mode v_max_f32 / v_max3_f32 return the other operand for a quiet NaN, as fmaxf
+// does; the inputs are MFMA results or -inf, never signalling NaNs.
+__device__ __forceinline__ float vmax2_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
   if (i == INT_MAX) return 0ull;
   uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
@@ -353,13 +368,12 @@ __device__ __forceinline__ void argmax_epilogue(
         }
     }
   }
-  // Per row tile, this lane's 32 values: their maximum by a tree of fmaxf (which
+  // Per row tile, this lane's 32 values: their maximum by a tree of v_max3 (which
   // never returns a NaN against a number, so NaN never wins), then the first
-  // position holding it by a tree of mins over positions (positions rise with the
-  // token index, so the first is the lowest); values past V take no part.  A linear
-  // scan with `better` was a dependent chain through every value (with && and ||,
-  // a few branches per value: 16 us per workgroup; branch-free, still 6.6 us at one
-  // wave per SIMD).
+  // position holding it (positions rise with the token index, so the first is the
+  // lowest); values past V take no part.  A linear scan with `better` was a
+  // dependent chain through every value (with && and ||, a few branches per value:
+  // 16 us per workgroup; branch-free, still 6.6 us at one wave per SIMD).
   constexpr int kN = kLmVA * 16;
   const bool full = vbase + kLmVA * 32 <= V;  // every value of the tile is a token
   // token index of position p = 16 a + r of this lane
@@ -375,26 +389,22 @@ __device__ __forceinline__ void argmax_epilogue(
 #pragma unroll
       for (int p = 0; p < kN; ++p) xs[p] = tok(p) < V ? xs[p] : -INFINITY;
     }
-    float mt[kN];
+    static_assert(kN == 32, "the max tree below is written for 32 values");
+    float t1[11];
 #pragma unroll
-    for (int i = 0; i < kN; ++i) mt[i] = xs[i];
+    for (int i = 0; i < 10; ++i) t1[i] = vmax3_raw(xs[3 * i], xs[3 * i + 1], xs[3 * i + 2]);
+    t1[10] = vmax2_raw(xs[30], xs[31]);
+    const float t20 = vmax3_raw(t1[0], t1[1], t1[2]), t21 = vmax3_raw(t1[3], t1[4], t1[5]);
+    const float t22 = vmax3_raw(t1[6], t1[7], t1[8]), t23 = vmax2_raw(t1[9], t1[10]);
+    const float mx = vmax2_raw(vmax3_raw(t20, t21, t22), t23);
+    // the first position holding it, by a descending chain of selects
+    int pbest = kN;
 #pragma unroll
-    for (int w = kN / 2; w >= 1; w /= 2)
-#pragma unroll
-      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
-    const float mx = mt[0];
-    int it[kN];
-#pragma unroll
-    for (int i = 0; i < kN; ++i) it[i] = xs[i] == mx ? i : kN;
-#pragma unroll
-    for (int w = kN / 2; w >= 1; w /= 2)
-#pragma unroll
-      for (int i = 0; i < w; ++i) it[i] = min(it[i], it[i + w]);
+    for (int p = kN - 1; p >= 0; --p) pbest = xs[p] == mx ? p : pbest;
     // A position past V holds -inf: it can equal mx only when every value is -inf
     // or NaN, and then it must not be reported.  Every value NaN: mx is NaN and no
     // position matches.  Either way the lane offers (-inf, none), which any value
     // of another lane beats.
-    const int pbest = it[0];
     const bool found = (pbest < kN) & (full | (tok(pbest) < V));
     float bv = found ? mx : -INFINITY;
     int bi = found ? tok(pbest) : INT_MAX;
