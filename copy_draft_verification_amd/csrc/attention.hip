@@ -123,13 +123,19 @@ struct AttnRows {
 };
 
 // Row maximum of a block of scores (both halves of the row), scaled.
+// The scores are MFMA results or -inf, so the raw maximum instructions serve.
 __device__ __forceinline__ float block_max(const f32x16 (&s)[2], float scale) {
-  float mx = -INFINITY;
+  float t1[11];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  for (int i = 0; i < 10; ++i) {
+    const int a = 3 * i, b = a + 1, c = a + 2;
+    t1[i] = vmax3_raw(s[a >> 4][a & 15], s[b >> 4][b & 15], s[c >> 4][c & 15]);
+  }
+  t1[10] = vmax2_raw(s[1][14], s[1][15]);
+  const float t2 = vmax3_raw(vmax3_raw(t1[0], t1[1], t1[2]), vmax3_raw(t1[3], t1[4], t1[5]),
+                             vmax3_raw(t1[6], t1[7], t1[8]));
+  float mx = vmax3_raw(t2, t1[9], t1[10]);
+  mx = vmax2_raw(mx, __shfl_xor(mx, 32, kWave));
   return mx * scale;   // scale > 0: the max commutes with it
 }
 

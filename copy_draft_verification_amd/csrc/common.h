@@ -164,6 +164,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Maxima of MFMA results without the canonicalising maximum the compiler puts in
+// front of every fmaxf input (which doubles a maximum tree).  In IEEE mode
+// v_max_f32 / v_max3_f32 return the other operand for a quiet NaN, as fmaxf does;
+// callers pass MFMA results or -inf, never signalling NaNs.
+__device__ __forceinline__ float vmax2_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // (value, index) order used by every argmax: larger value wins, equal values
 // go to the lower index.  NaN never wins.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {

@@ -318,21 +318,6 @@ __device__ __forceinline__ void sample_epilogue(
 // largest value with the lowest index, the order of `better`.  0 stands for no
 // value (every value NaN or past V); no real pair maps to it, since its high half
 // would be a NaN's.
-// Maxima of MFMA results without the canonicalising maximum the compiler puts in
-// front of every fmaxf input (which doubled the epilogue's maximum tree).  In IEEE
-// mode v_max_f32 / v_max3_f32 return the other operand for a quiet NaN, as fmaxf
-// does; the inputs are MFMA results or -inf, never signalling NaNs.
-__device__ __forceinline__ float vmax2_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float vmax3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
   if (i == INT_MAX) return 0ull;
   uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
