@@ -13,7 +13,7 @@ import torch  # loaded first so the library binds to the same HIP runtime as tor
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libswitchsd.so")
 
-SSD_F32, SSD_BF16 = 0, 1
+SSD_F32, SSD_BF16, SSD_BF16_ROWS = 0, 1, 2
 _lib = None
 
 _c_p = ctypes.c_void_p
@@ -329,15 +329,21 @@ def _packed(w, name, rows, K, pair=False):
     return w.data
 
 
-def _lm_arg(lm_head, dtype, K):
-    """(tensor, V) of the LM-head argument: packed for bf16, a plain [V, K] fp32 matrix
-    otherwise."""
+def _lm_arg(lm_head, dtype, K, rows_ok=False):
+    """(tensor, V, dtype code) of the LM-head argument: for bf16 a PackedWeight, or, where
+    the call takes it (rows_ok), the plain [V, K] bf16 matrix (SSD_BF16_ROWS); a plain
+    [V, K] fp32 matrix otherwise."""
     if dtype == torch.bfloat16:
-        return _packed(lm_head, "lm_head", None, K), lm_head.rows
+        if rows_ok and isinstance(lm_head, torch.Tensor):
+            _dev(lm_head, "lm_head", (torch.bfloat16,))
+            if lm_head.dim() != 2 or lm_head.shape[1] != K:
+                raise SwitchSDError(f"lm_head must be [V, {K}], got {tuple(lm_head.shape)}")
+            return lm_head, lm_head.shape[0], SSD_BF16_ROWS
+        return _packed(lm_head, "lm_head", None, K), lm_head.rows, SSD_BF16
     _dev(lm_head, "lm_head", (torch.float32,))
-    if lm_head.shape[1] != K:
-        raise SwitchSDError(f"lm_head has K = {lm_head.shape[1]}, the rows have {K}")
-    return lm_head, lm_head.shape[0]
+    if lm_head.dim() != 2 or lm_head.shape[1] != K:
+        raise SwitchSDError(f"lm_head has K = {lm_head.shape[-1]}, the rows have {K}")
+    return lm_head, lm_head.shape[0], SSD_F32
 
 
 def verify_workspace_bytes(B, max_n, W, D, Hq, Hkv, d, V, dtype):
@@ -379,13 +385,14 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
                     events=None, stream=None):
     """One verification pass.  q [B, R, Hq, d]; k_pre/v_pre [N, Hkv, d]; k_cand/v_cand
     [B, W*D, Hkv, d]; cand_len [B, W]; cu_len [B+1]; copy_gate [B]; lm_head [V, Hq*d]
-    (fp32) or a PackedWeight (bf16).  Outputs, when given: attn_out [B, R, Hq*d] of
+    (fp32), or for bf16 a PackedWeight (the fast layout) or the plain [V, Hq*d] matrix.
+    Outputs, when given: attn_out [B, R, Hq*d] of
     q's dtype, argmax_out [B, R] int32, logits_out [B, R, V] float32; workspace uint8
     of at least verify_workspace_bytes.  cu_len[B] <= N is the caller's to keep (it
     lives on the device).  Returns (attn_out, argmax_out)."""
     B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
                                       copy_gate, W, D, (torch.float32, torch.bfloat16))
-    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    lm, V, code = _lm_arg(lm_head, q.dtype, Hq * d, rows_ok=True)
     dev = q.device
     ts = _torch_stream(stream, dev)
     if attn_out is None:
@@ -401,7 +408,7 @@ def blocktri_verify(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand_len, co
     ev0, ev1 = _events(events)
     _check(load().ssd_blocktri_verify(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
-        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q),
+        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, code,
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
         "blocktri_verify")
@@ -416,7 +423,7 @@ def blocktri_verify_noalloc(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand
     float32 or None).  Calls that overlap on one GPU race on the shared scratch."""
     B, R, Hq, Hkv, d = _verify_inputs(q, k_pre, v_pre, cu_len, k_cand, v_cand, cand_len,
                                       copy_gate, W, D, (torch.float32, torch.bfloat16))
-    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    lm, V, code = _lm_arg(lm_head, q.dtype, Hq * d, rows_ok=True)
     dev = q.device
     ts = _torch_stream(stream, dev)
     _out(attn_out, "attn_out", q.dtype, (B, R, Hq * d), dev)
@@ -425,7 +432,7 @@ def blocktri_verify_noalloc(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand
         _out(logits_out, "logits_out", torch.float32, (B, R, V), dev)
     _check(load().ssd_blocktri_verify_noalloc(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
-        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q), float(scale),
+        _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, code, float(scale),
         _ptr(attn_out), _ptr(argmax_out), _ptr(logits_out), _torch_stream_handle(ts)),
         "blocktri_verify_noalloc")
     return attn_out, argmax_out
@@ -442,7 +449,7 @@ def blocktri_verify_accept(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
                                       copy_gate, W, D, (torch.float32, torch.bfloat16))
     _dev(cand, "cand", (torch.int32,))
     _shape(cand, "cand", (B, W, D))
-    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    lm, V, code = _lm_arg(lm_head, q.dtype, Hq * d, rows_ok=True)
     dev = q.device
     _same_device(dev, (cand, "cand"))
     ts = _torch_stream(stream, dev)
@@ -462,7 +469,7 @@ def blocktri_verify_accept(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
     ev0, ev1 = _events(events)
     _check(load().ssd_blocktri_verify_accept(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
-        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, _dt(q),
+        _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V, code,
         float(scale), _ptr(attn_out), _ptr(argmax_out), _ptr(out["accept_len"]), _ptr(out["best_w"]),
         _ptr(out["best_len"]), _ptr(out["next_token"]), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
@@ -489,7 +496,7 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
                                       copy_gate, W, D, (torch.bfloat16,))
     _dev(cand, "cand", (torch.int32,))
     _shape(cand, "cand", (B, W, D))
-    lm, V = _lm_arg(lm_head, q.dtype, Hq * d)
+    lm, V, code = _lm_arg(lm_head, q.dtype, Hq * d)
     dev = q.device
     ts = _torch_stream(stream, dev)
     if attn_out is None:
@@ -508,7 +515,7 @@ def blocktri_verify_sample(q, k_pre, v_pre, cu_len, max_n, k_cand, v_cand, cand,
     _check(load().ssd_blocktri_verify_sample(
         _ptr(q), _ptr(k_pre), _ptr(v_pre), _ptr(cu_len), int(max_n), _ptr(k_cand), _ptr(v_cand),
         _ptr(cand), _ptr(cand_len), _ptr(copy_gate), _ptr(lm), B, W, D, Hq, Hkv, d, V,
-        _dt(q), float(scale), float(temperature), int(seed) & ((1 << 64) - 1), _ptr(attn_out),
+        code, float(scale), float(temperature), int(seed) & ((1 << 64) - 1), _ptr(attn_out),
         _ptr(rows["n_children"]), _ptr(rows["children"]), _ptr(rows["child_w"]),
         _ptr(rows["child_logit"]), _ptr(rows["lse"]), _ptr(rows["resample"]), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ev0, ev1, _torch_stream_handle(ts)),
@@ -715,7 +722,7 @@ def verify_forward(ids, cu_len, max_n, cand, cand_len, copy_gate, embed, layers,
     _dev(copy_gate, "copy_gate", (torch.uint8,))
     for t, n in ((embed, "embed"), (final_norm, "final_norm")):
         _dev(t, n, (torch.bfloat16,))
-    lm, V = _lm_arg(lm_head, torch.bfloat16, Hq * d)
+    lm, V, _ = _lm_arg(lm_head, torch.bfloat16, Hq * d)
     hid = Hq * d
     shapes = {"wqkv": ((Hq + 2 * Hkv) * d, hid, False), "wo": (hid, hid, False),
               "w_gate_up": (inter, hid, True), "w_down": (hid, inter, False)}

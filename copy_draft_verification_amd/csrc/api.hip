@@ -13,6 +13,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool valid_dtype(ssd_dtype_t t) { return t == SSD_F32 || t == SSD_BF16; }
+// the verification calls also take bf16 with a row-major LM head
+bool valid_verify_dtype(ssd_dtype_t t) { return valid_dtype(t) || t == SSD_BF16_ROWS; }
 
 ssd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
@@ -29,11 +31,11 @@ ssd_status_t check_verify_shape(int32_t B, int32_t max_n, int32_t W, int32_t D, 
                                 int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dt) {
   if (B < 1 || max_n < 1 || W < 1 || D < 1 || Hq < 1 || Hkv < 1 || d < 1 || V < 1)
     return SSD_ERR_INVALID_ARG;
-  if (W > SSD_MAX_W || D > SSD_MAX_D || Hq % Hkv != 0 || !valid_dtype(dt)) return SSD_ERR_INVALID_ARG;
+  if (W > SSD_MAX_W || D > SSD_MAX_D || Hq % Hkv != 0 || !valid_verify_dtype(dt)) return SSD_ERR_INVALID_ARG;
   const long long R = 1 + static_cast<long long>(W) * D;
   if (static_cast<long long>(B) * R * Hq * d > (1ll << 40)) return SSD_ERR_INVALID_ARG;
   if (static_cast<long long>(B) * R * Hq >= (1ll << 31)) return SSD_ERR_UNSUPPORTED;
-  if (dt == SSD_BF16) {
+  if (dt != SSD_F32) {
     if (d != 128 || (static_cast<long long>(Hq) * d) % 256 != 0) return SSD_ERR_UNSUPPORTED;
     if (!fits_byte_offsets(B, max_n, R, Hkv, d, static_cast<long long>(Hq) * d))
       return SSD_ERR_UNSUPPORTED;
@@ -170,7 +172,7 @@ ssd_status_t ssd_pack_gate_up(const void* w_gate, const void* w_up, int32_t inte
 size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D, int32_t Hq,
                                   int32_t Hkv, int32_t d, int32_t V, ssd_dtype_t dtype) {
   if (check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype) != SSD_OK) return 0;
-  const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, dtype == SSD_BF16);
+  const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, dtype != SSD_F32);
   return L.attn_bytes + L.lm_bytes;
 }
 
@@ -195,7 +197,7 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
   if (!verify_aligned(q, k_pre, v_pre, k_cand, v_cand, lm_head, attn_out)) return SSD_ERR_INVALID_ARG;
   const ssd_status_t st = check_verify_shape(B, max_n, W, D, Hq, Hkv, d, V, dtype);
   if (st != SSD_OK) return st;
-  const bool bf16 = dtype == SSD_BF16;
+  const bool bf16 = dtype != SSD_F32, rows_layout = dtype == SSD_BF16_ROWS;
   const VerifyLayout L = verify_layout(B, max_n, W, D, Hq, Hkv, d, V, bf16);
   ssd_status_t ws_err = SSD_OK;
   void* workspace = get_ws(L.attn_bytes + L.lm_bytes, &ws_err);
@@ -210,7 +212,7 @@ ssd_status_t verify_impl(const void* q, const void* k_pre, const void* v_pre, co
                                        stream, &cv);
   if (e != hipSuccess) return SSD_ERR_HIP;
   e = ssd::launch_lmhead(attn_out, lm_head, B * R, Hq * d, V, bf16, L.lm, logits_out, ws_lm,
-                         lm_begin, lm_end, stream);
+                         lm_begin, lm_end, stream, nullptr, rows_layout);
   if (e != hipSuccess) return SSD_ERR_HIP;
   // one launch turns the LM head's per-row keys into argmax_out and accepts
   return from_hip(ssd::launch_argmax_finish(ws_lm, B, R, argmax_out, acc, stream));

@@ -120,10 +120,12 @@ struct AcceptArgs {
 
 // sample != nullptr: sampling partials.  Otherwise greedy: each row's best (value,
 // lowest index) is folded into a 64-bit key per row (launch_argmax_finish).
+// rows_layout (bf16 greedy only): lm_head is the plain row-major [V][hid] matrix
+// instead of the packed layout.
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
-                         const SampleArgs* sample = nullptr);
+                         const SampleArgs* sample = nullptr, bool rows_layout = false);
 // Greedy: argmax_out [B][R] from the keys of launch_lmhead (-1 for rows that are
 // not real), then, with `accept`, the accept of every sequence; one launch.
 hipError_t launch_argmax_finish(void* ws, int B, int R, int32_t* argmax_out, const AcceptArgs* accept,

@@ -418,7 +418,10 @@ __device__ __forceinline__ void argmax_epilogue(
 // chunk), so the weight loads carry the nontemporal hint, which streams faster
 // from HBM; with several row chunks the chunks of one tile share it through L2,
 // and the default policy keeps it there.
-template <int kEpi, bool kOnce>
+// kRows: the weights are the plain row-major [N][K] matrix instead of the packed
+// layout (greedy launch only): each A-fragment load then gathers 16 bytes from each
+// of 32 rows, where the packed layout reads 1 KB contiguous.
+template <int kEpi, bool kOnce, bool kRows = false>
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
     const int32_t* __restrict__ row_list, const int32_t* __restrict__ n_rows,
@@ -476,11 +479,19 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // the range return zero (rows past `rows`, prefetches past the K range), so the
   // pipeline needs no guards.
   const int o_bytes = total_rows * K * 2;
+  static_assert(!kRows || (kEpi == kEpiArgmax && kVA == kLmVA), "row-major weights: greedy launch only");
+  // rows of the tile past N (plain layout: past the end of the matrix) read as zero
+  const int tile_rows = kRows ? max(0, min(kLmVT, V - ptile * kLmVT)) : kLmVT;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Wt + static_cast<size_t>(ptile) * kLmVT * K), 0, K * kLmVT * 2, kBufFlags);
+      const_cast<uint16_t*>(Wt + static_cast<size_t>(ptile) * kLmVT * K), 0, K * tile_rows * 2, kBufFlags);
   int aoff[kVA];
 #pragma unroll
-  for (int a = 0; a < kVA; ++a) aoff[a] = wave * kPkWaveBytes + (a + hh) * 4 * kWave * 16 + lane * 16;
+  for (int a = 0; a < kVA; ++a)
+    aoff[a] = kRows ? (wave * 64 + (a + hh) * 32 + (lane & 31)) * K * 2 + (lane >> 5) * 16
+                    : wave * kPkWaveBytes + (a + hh) * 4 * kWave * 16 + lane * 16;
+  // per k-step (16 k) and k-slab (64 k) strides of the A-fragment loads
+  constexpr int kStepBytes = kRows ? 32 : kWave * 16;
+  constexpr int kSlabBytes = kRows ? kLmKS * 2 : kPkSlabBytes;
   const __amdgpu_buffer_rsrc_t ores =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(O), 0, o_bytes, kBufFlags);
   // Row blocks of this wave: block b = wave*7 + j holds stage rows 8b..8b+7; lane i
@@ -523,14 +534,14 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   auto load_a = [&](uint4 (&dst)[kVA][4], int it) {
     const bool past = it == kPastEnd;
     // slab block of iteration it; run (a, s) of this wave, 16 B per lane
-    const int so = past ? 0 : slab(it) * kPkSlabBytes;
+    const int so = past ? 0 : slab(it) * kSlabBytes;
 #pragma unroll
     for (int a = 0; a < kVA; ++a)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         dst[a][s] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wres, past ? kOutOfRange : aoff[a] + s * kWave * 16, so, kOnce ? kNonTemporal : 0));
+                       wres, past ? kOutOfRange : aoff[a] + s * kStepBytes, so, kOnce ? kNonTemporal : 0));
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
@@ -1035,12 +1046,12 @@ size_t lm_workspace_bytes(const LmPlan& p, int rows) {
 
 // Launch the bf16 kernel with epilogue kEpi; the nontemporal weight loads when the
 // launch has one row chunk.
-template <int kEpi, typename... Args>
+template <int kEpi, bool kRows = false, typename... Args>
 static void launch_bf16(const LmPlan& plan, dim3 grid, hipStream_t s, Args... args) {
   if (plan.mchunks == 1)
-    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, true>), grid, dim3(256), 0, s, args...);
+    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, true, kRows>), grid, dim3(256), 0, s, args...);
   else
-    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, false>), grid, dim3(256), 0, s, args...);
+    hipLaunchKernelGGL((lmhead_bf16_kernel<kEpi, false, kRows>), grid, dim3(256), 0, s, args...);
 }
 
 hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const int32_t* cand_len,
@@ -1054,10 +1065,16 @@ hipError_t launch_compact_rows(void* ws, int rows, int R, int W, int D, const in
 hipError_t launch_lmhead(const void* attn_out, const void* lm_head, int rows, int hid, int V,
                          bool bf16, const LmPlan& plan, float* logits_out, void* ws,
                          hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s,
-                         const SampleArgs* sample) {
+                         const SampleArgs* sample, bool rows_layout) {
   const LmWs w = lm_ws(ws, rows);
+  if (rows_layout && (!bf16 || sample != nullptr)) return hipErrorInvalidValue;
   if (ev_begin && hipEventRecord(ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
-  if (bf16 && sample)
+  if (rows_layout)
+    launch_bf16<kEpiArgmax, true>(plan, dim3(plan.blocks), s,
+                       static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
+                       rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.keys),
+                       plan.vtiles, plan.mchunks, plan.sv, plan.sm, SampleArgs{}, GemmArgs{});
+  else if (bf16 && sample)
     launch_bf16<kEpiSample>(plan, dim3(plan.blocks), s,
                        static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(lm_head),
                        rows, hid, V, w.row_list, w.n_rows, logits_out, static_cast<void*>(w.part),

@@ -62,7 +62,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SSD_ABI_VERSION 11
+#define SSD_ABI_VERSION 12
 
 typedef enum {
   SSD_OK = 0,
@@ -72,7 +72,12 @@ typedef enum {
   SSD_ERR_HIP = 4          /* a kernel launch failed */
 } ssd_status_t;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+/* SSD_BF16_ROWS: bf16 like SSD_BF16 (bf16 storage, fp32 accumulation), with the
+ * LM head given as the plain row-major [V][hid] matrix instead of the packed layout
+ * of ssd_pack_weight.  Taken by the T = 0 verification calls only
+ * (ssd_blocktri_verify, _noalloc, _accept); its weight stream is slower than the
+ * packed layout's, each A-fragment load gathering 16 bytes from each of 32 rows. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_BF16_ROWS = 2 } ssd_dtype_t;
 
 /* Limits checked by validation. */
 #define SSD_MAX_W 64      /* candidates per sequence */
@@ -200,12 +205,14 @@ size_t ssd_verify_workspace_bytes(int32_t B, int32_t max_n, int32_t W, int32_t D
  *                                   real (gate closed, w >= M, j >= L_w) are zeros
  * LM head + argmax:
  *   lm_head  fp32: [V][Hq*d]        transposed projection (row v = weights of token v)
- *            bf16: that matrix as written by ssd_pack_weight
+ *            SSD_BF16: that matrix as written by ssd_pack_weight
+ *            SSD_BF16_ROWS: that matrix itself, bf16 row-major
  *   argmax_out [B][R] int32         lowest index among equal maxima (NaN logits
  *                                   never win); -1 on rows that are not real and
  *                                   on rows whose logits are all NaN
  *   logits_out [B][R][V] float or NULL (debug output; written for every row)
- * dtype: SSD_F32 (all float) or SSD_BF16 (all bf16, fp32 accumulation).
+ * dtype: SSD_F32 (all float), SSD_BF16 (all bf16, fp32 accumulation) or SSD_BF16_ROWS
+ *   (as SSD_BF16 with a row-major LM head).
  * max_n: host-side upper bound on the context lengths (every cu_len[b+1] -
  * cu_len[b] <= max_n), used to size the launch; results do not depend on it.
  * workspace: device scratch of at least ssd_verify_workspace_bytes(...) bytes;
@@ -360,7 +367,8 @@ ssd_status_t ssd_commit_accepted(const void* k_cand, const void* v_cand, const i
  *   temperature: finite, > 0, with a finite reciprocal
  * Other arguments, workspace and events as for ssd_blocktri_verify.
  * Errors: as ssd_blocktri_verify; INVALID_ARG for a bad temperature or a null
- *   output; UNSUPPORTED for SSD_F32.
+ *   output; UNSUPPORTED for SSD_F32 and SSD_BF16_ROWS (the sampling epilogue reads
+ *   the packed LM head only).
  */
 ssd_status_t ssd_blocktri_verify_sample(
     const void* q, const void* k_pre, const void* v_pre, const int32_t* cu_len, int32_t max_n,

@@ -69,6 +69,9 @@ def test_workspace_query(lib):
     assert f(1304, 4096, 10, 20, 32, 8, 128, 1000, 1) > 0           # 1304 * 201 * 8 KiB
     assert f(1305, 4096, 10, 20, 32, 8, 128, 1000, 1) == 0
     assert f(1305, 4096, 10, 20, 32, 8, 64, 1000, 0) > 0            # fp32 path: no limit
+    # the row-major bf16 LM head needs the packed one's workspace
+    assert f(1, 4096, 10, 20, 32, 8, 128, 128256, 2) == f(1, 4096, 10, 20, 32, 8, 128, 128256, 1)
+    assert f(1, 4096, 10, 20, 32, 8, 128, 128256, 3) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -169,6 +172,12 @@ def test_verify_validation(lib):
         assert f(*_verify_args(dtype=0, d=64, **{k: MISALIGNED})) == 1, k
     # B*R*Hq must stay below 2^31 (32-bit index math in the merges)
     assert f(*_verify_args(dtype=0, d=64, B=2 ** 20, W=64, D=64, Hq=1, Hkv=1)) == 2
+    # SSD_BF16_ROWS (bf16, row-major LM head) takes bf16's shape rules
+    assert f(*_verify_args(dtype=2, d=64)) == 2
+    assert f(*_verify_args(dtype=2, Hq=3, Hkv=1)) == 2
+    assert f(*_verify_args(dtype=2, ws_bytes=16)) == 3
+    assert f(*_verify_args(dtype=2, lm_head=MISALIGNED)) == 1
+    assert f(*_verify_args(dtype=3)) == 1
 
 
 def _verify_accept_args(**over):
@@ -191,6 +200,8 @@ def test_verify_accept_validation(lib):
     assert f(*_verify_accept_args(d=64)) == 2
     assert f(*_verify_accept_args(ws_bytes=16)) == 3
     assert f(*_verify_accept_args(k_pre=MISALIGNED)) == 1
+    assert f(*_verify_accept_args(dtype=2, ws_bytes=16)) == 3
+    assert f(*_verify_accept_args(dtype=2, d=64)) == 2
 
 
 def test_accept_validation(lib):
@@ -300,6 +311,7 @@ def test_verify_sample_validation(lib):
         assert f(*_sample_args(temperature=t)) == 1, t           # 1e-45: 1/T overflows
     assert f(*_sample_args(dtype=0, d=64, Hq=1, Hkv=1)) == 2      # sampling is bf16 only
     assert f(*_sample_args(d=64)) == 2
+    assert f(*_sample_args(dtype=2)) == 2                         # sampling needs the packed head
     assert f(*_sample_args()) == 3                                # workspace too small
     assert f(*_sample_args(seed=(1 << 64) - 1)) == 3              # any 64-bit seed is accepted
     assert f(*_sample_args(v_cand=MISALIGNED)) == 1

@@ -174,13 +174,50 @@ def test_pack_gate_up_layout_bitwise(inter, K):
     assert np.array_equal(got, _pack_host(_pair_rows_host(gbits, ubits), K))
 
 
-def test_unpacked_bf16_lm_head_is_refused():
+@pytest.mark.parametrize("name,over", [
+    ("small_bf16", {"lm_std": 1.0}),                              # V = 3001: a partial last tile
+    ("small_bf16", {"B": 32, "n": (200, 400), "seed": 2203, "lm_std": 1.0}),  # several row chunks
+    ("llama8b_b1", {"lm_std": 1.0}),
+])
+def test_row_major_bf16_lm_head_matches_packed(name, over):
+    # SSD_BF16_ROWS: the plain [V, hid] matrix gives the packed layout's results bit for
+    # bit (the same MFMA operands reach every lane, only the load addressing differs)
+    wl = generate(name, **over)
+    s = wl.spec
+    print(f"[case] row-major LM head, {name} {over}", flush=True)
+    d = Dev(wl)
+    g = cdv.kgram_retrieve(d.ids, d.cu, s.kappa, s.W, s.D)
+    plain = up(wl.lm_head)
+    assert plain.dtype == torch.bfloat16 and not isinstance(plain, cdv.PackedWeight)
+    logits = s.V <= 10000
+    outs = []
+    for lm in (d.lm, plain):
+        L = torch.empty(s.B, wl.R, s.V, dtype=torch.float32, device=DEV) if logits else None
+        a, m = cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
+                                   g["copy_gate"], lm, s.W, s.D, wl.scale, logits_out=L)
+        a2, m2, acc = cdv.blocktri_verify_accept(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc,
+                                                 g["cand"], g["cand_len"], g["copy_gate"], lm,
+                                                 s.W, s.D, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(m, m2)
+        outs.append((m, L, acc))
+    assert torch.equal(outs[0][0], outs[1][0])
+    if logits:
+        real = host(outs[0][0]) >= 0
+        assert np.array_equal(host(outs[0][1])[real], host(outs[1][1])[real])
+    for k in outs[0][2]:
+        assert torch.equal(outs[0][2][k], outs[1][2][k]), k
+    print(f"[ok] argmax equal on {int((host(outs[0][0]) >= 0).sum())} real rows", flush=True)
+
+
+def test_row_major_bf16_lm_head_is_refused_by_sampling():
     wl = generate("small_bf16")
     d = Dev(wl)
     g = cdv.kgram_retrieve(d.ids, d.cu, wl.spec.kappa, wl.spec.W, wl.spec.D)
     with pytest.raises(cdv.SwitchSDError, match="packed"):
-        cdv.blocktri_verify(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand_len"],
-                            g["copy_gate"], up(wl.lm_head), wl.spec.W, wl.spec.D, wl.scale)
+        cdv.blocktri_verify_sample(d.q, d.kp, d.vp, d.cu, wl.max_n, d.kc, d.vc, g["cand"],
+                                   g["cand_len"], g["copy_gate"], up(wl.lm_head), wl.spec.W,
+                                   wl.spec.D, wl.scale, 1.0, 7)
 
 
 def _nan_tail(t, extra_rows):
