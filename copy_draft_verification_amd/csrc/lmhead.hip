@@ -420,7 +420,9 @@ __device__ __forceinline__ void argmax_epilogue(
 // and the default policy keeps it there.
 // kRows: the weights are the plain row-major [N][K] matrix instead of the packed
 // layout (greedy launch only): each A-fragment load then gathers 16 bytes from each
-// of 32 rows, where the packed layout reads 1 KB contiguous.
+// of 32 rows, where the packed layout reads 1 KB contiguous.  The four k-steps of
+// a slab read the same 128-byte line of each row, so these loads keep the default
+// cache policy, which holds the line in the vector cache from one step to the next.
 template <int kEpi, bool kOnce, bool kRows = false>
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ Wt, int total_rows, int K, int V,
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       for (int s = 0; s < 4; ++s)
         dst[a][s] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wres, past ? kOutOfRange : aoff[a] + s * kStepBytes, so, kOnce ? kNonTemporal : 0));
+                       wres, past ? kOutOfRange : aoff[a] + s * kStepBytes, so, (kOnce && !kRows) ? kNonTemporal : 0));
   };
   auto load_o = [&](uint16_t* stage, int it) {
     const bool past = it == kPastEnd;
