@@ -29,7 +29,6 @@ constexpr int kStage = kKB * kAttD;                              // bf16 per K o
 constexpr int kDmaPerWave = kStage * 2 / 16 / kWave / kAttWaves; // 16-byte copies per wave and stage (2)
 constexpr int kXcds = 8;            // workgroups are dealt round-robin over the 8 XCDs
 constexpr float kFreeRange = 32.f;  // scores may exceed the running max by 2^32 before it moves
-constexpr float kLazyRescale = 8.f; // masked blocks: the running max moves when exceeded by 2^8
 constexpr int kAhead = 2;           // LDS fragment reads in flight ahead of their MFMA
 constexpr int kOutOfRange = 0x7ffffff0;
 constexpr int kPersistCus = 256;    // persistent grid: one workgroup per CU
