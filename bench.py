@@ -751,8 +751,8 @@ def measure(runner, steps, warmup, flush):
       milliseconds of load do not have);
     * step: each step between two events, the last-level cache flushed before each
       step outside its events (the step times, p10 / p50 / p90);
-    * back to back: the steps between two events with nothing between them, the
-      driver's bracket (warm caches)."""
+    * back to back: the steps between two events with nothing between them, as a
+      caller timing a loop of steps sees them (warm caches)."""
     import torch
     st = runner.stream
     for i in range(warmup):
@@ -814,9 +814,9 @@ def step_result(runner, tm):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported in this build "
-              f"(the path shards over sequences with no exchange; see the sharding notes).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: the path would shard "
+              f"over sequences, one process per GPU with no exchange between them, and only the "
+              f"one-GPU figure is measured.", file=sys.stderr)
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy()
