@@ -163,13 +163,50 @@ def blas_threads():
 
 
 def cpu_baseline(wl, budget_s, gpu_stage_ms=None):
-    """Time the oracle (as it stands) on the host for one step of this workload.
+    """Time the oracle (as it stands) on the host for steps of this workload: one
+    step (see _cpu_step), repeated until about half the budget (at most 10 s) is
+    spent, so that a step the oracle finishes in well under a second is still
+    timed over seconds of CPU work; the step of median time is reported.  With the
+    GPU's per-stage medians (ms) the per-stage GPU/oracle speedups are reported
+    too."""
+    goal = min(10.0, budget_s / 2)
+    runs, spent = [], 0.0
+    while True:
+        r = _cpu_step(wl, budget_s)
+        if r is None:
+            return None
+        runs.append(r)
+        spent += r["measured_s"]
+        if spent >= goal or len(runs) >= 50:
+            break
+    runs.sort(key=lambda r: r["value"])
+    res = runs[len(runs) // 2]
+    res["sample"] += f"; the median of {len(runs)} such steps ({spent:.1f}s of oracle time in all)"
+    res["repetitions"] = len(runs)
+    res["measured_total_s"] = round(spent, 2)
+    stages = res["stages"]
+    if gpu_stage_ms:
+        # the GPU runs the probe and the retrieval as one launch, and the argmax and
+        # the accept inside the LM-head launch
+        pairs = {"probe_kgram_retrieve": (("probe", "kgram_retrieve"), ("probe_kgram_retrieve",)),
+                 "attention": (("attention",), ("attention",)),
+                 "lm_head_argmax_accept": (("lm_head_argmax", "accept"), ("lm_head", "after_lm_head"))}
+        sp = {}
+        for k, (cpu, g) in pairs.items():
+            gm = sum(gpu_stage_ms.get(x) or 0.0 for x in g)
+            if gm > 0:
+                sp[k] = round(sum(stages[c]["s"] for c in cpu) / (gm * 1e-3), 1)
+        res["oracle_over_gpu"] = sp
+    return res
+
+
+def _cpu_step(wl, budget_s):
+    """One step of the oracle on the host.
 
     The probe, the kappa-gram retrieval and the acceptance are Python loops: one
     thread, every sequence.  Attention and the LM head are numpy float64 matmuls on
     the BLAS threads, on a seeded sample of real rows sized to the budget, their
-    time scaled to all real rows of the step.  With the GPU's per-stage medians
-    (ms) the per-stage GPU/oracle speedups are reported too."""
+    time scaled to all real rows of the step."""
     import oracle
     from oracle.attention import real_rows
     threads = blas_threads()
@@ -237,18 +274,6 @@ def cpu_baseline(wl, budget_s, gpu_stage_ms=None):
                       f"threads; scaled to all rows: {t_step:.2f}s per step"),
            "cpu_model": model, "nproc": nproc, "blas_threads": int(threads),
            "stages": stages, "measured_s": round(t_probe + t_kg + t_att + t_lm + t_acc, 2)}
-    if gpu_stage_ms:
-        # the GPU runs the probe and the retrieval as one launch, and the argmax and
-        # the accept inside the LM-head launch
-        pairs = {"probe_kgram_retrieve": (("probe", "kgram_retrieve"), ("probe_kgram_retrieve",)),
-                 "attention": (("attention",), ("attention",)),
-                 "lm_head_argmax_accept": (("lm_head_argmax", "accept"), ("lm_head", "after_lm_head"))}
-        sp = {}
-        for k, (cpu, g) in pairs.items():
-            gm = sum(gpu_stage_ms.get(x) or 0.0 for x in g)
-            if gm > 0:
-                sp[k] = round(sum(stages[c]["s"] for c in cpu) / (gm * 1e-3), 1)
-        res["oracle_over_gpu"] = sp
     return res
 
 
